@@ -1,0 +1,163 @@
+"""CPU oracle for the Mamba selective scan -- TEST INFRASTRUCTURE ONLY.
+
+A thin ctypes wrapper around ``oracle.c``: the plain sequential fp64
+recurrence (see that file's header for what is computed and which passage of
+the pages each step follows).  Only the test suite, ``__graft_entry__.smoke()``
+and the bench's ``cpu_baseline`` leg may import this package.  It does not
+import the HIP library, and the HIP library never imports it.
+
+Every function takes numpy arrays of fp32 values (the exact values the GPU
+path consumes, bf16 inputs already widened) and returns fp64 results.
+Channels are independent, so the wrapper splits a channel list over threads;
+each thread runs the unmodified sequential C code on its share.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11"]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        i64, fp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+        lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [fp] * 8 + [fp, i64, dp, dp]
+        lib.oracle_scan.restype = None
+        lib.oracle_state_update.argtypes = [i64, i64, i64, dp] + [fp] * 7 + [dp]
+        lib.oracle_state_update.restype = None
+        lib.oracle_ssd.argtypes = [i64] * 6 + [fp] * 8 + [fp, i64, dp, dp]
+        lib.oracle_ssd.restype = None
+        _lib = lib
+    return _lib
+
+
+def _f32(a):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def _run_channels(fn, channels: np.ndarray, L: int, N: int, threads: int):
+    """Split `channels` over threads; fn(ch_slice, y_slice, h_slice) fills outputs."""
+    n = len(channels)
+    y = np.empty((n, L), dtype=np.float64)
+    h = np.empty((n, N), dtype=np.float64)
+    if n == 0:
+        return y, h
+    threads = max(1, min(threads, n))
+    bounds = np.linspace(0, n, threads + 1).astype(np.int64)
+
+    def work(i):
+        a, b = bounds[i], bounds[i + 1]
+        if b > a:
+            fn(channels[a:b], y[a:b], h[a:b])
+
+    if threads == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, range(threads)))
+    return y, h
+
+
+def scan(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threads=None):
+    """Mamba-1 selective scan.
+
+    Shapes: x, delta, z (B, L, D); Bm, Cm (B, L, N); A (D, N); D_skip (D,);
+    h0 (B, D, N).  With ``channels=None`` returns y (B, L, D) and h_final
+    (B, D, N) in fp64; otherwise ``channels`` lists flat indices b*D + d and
+    the result is y (k, L), h_final (k, N) for those channels.
+    """
+    lib = _load()
+    x, delta, A, Bm, Cm = map(_f32, (x, delta, A, Bm, Cm))
+    D_skip, z, h0 = map(_f32, (D_skip, z, h0))
+    B, L, D = x.shape
+    N = A.shape[1]
+    full = channels is None
+    ch = np.arange(B * D, dtype=np.int64) if full else np.ascontiguousarray(channels, dtype=np.int64)
+    threads = threads or default_threads()
+
+    def fn(c, ys, hs):
+        lib.oracle_scan(B, L, D, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                        _ptr(D_skip), _ptr(z), _ptr(h0), c.ctypes.data, len(c),
+                        ys.ctypes.data, hs.ctypes.data)
+
+    y, h = _run_channels(fn, ch, L, N, threads)
+    if full:
+        return y.reshape(B, D, L).transpose(0, 2, 1).copy(), h.reshape(B, D, N)
+    return y, h
+
+
+def state_update(state, x, delta, A, Bm, Cm, D_skip=None, z=None):
+    """One decode step.  state (S, D, N) fp64 is updated in place; returns y (S, D)."""
+    lib = _load()
+    assert state.dtype == np.float64 and state.flags.c_contiguous
+    x, delta, A, Bm, Cm, D_skip, z = map(_f32, (x, delta, A, Bm, Cm, D_skip, z))
+    S, D = x.shape
+    N = A.shape[1]
+    y = np.empty((S, D), dtype=np.float64)
+    lib.oracle_state_update(S, D, N, state.ctypes.data, _ptr(x), _ptr(delta), _ptr(A),
+                            _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z), y.ctypes.data)
+    return y
+
+
+def ssd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threads=None):
+    """Mamba-2 SSD recurrence.
+
+    Shapes: x, z (B, L, H, P); dt (B, L, H); A, D_skip (H,); Bm, Cm
+    (B, L, G, N); h0 (B, H, P, N).  With ``channels=None`` returns y
+    (B, L, H, P) and h_final (B, H, P, N); otherwise ``channels`` lists flat
+    indices (b*H + h)*P + p and the result is y (k, L), h_final (k, N).
+    """
+    lib = _load()
+    x, dt, A, Bm, Cm, D_skip, z, h0 = map(_f32, (x, dt, A, Bm, Cm, D_skip, z, h0))
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    if H % G != 0:
+        raise ValueError("heads must be a multiple of groups")
+    full = channels is None
+    ch = np.arange(B * H * P, dtype=np.int64) if full else np.ascontiguousarray(channels, dtype=np.int64)
+    threads = threads or default_threads()
+
+    def fn(c, ys, hs):
+        lib.oracle_ssd(B, L, H, P, G, N, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm),
+                       _ptr(D_skip), _ptr(z), _ptr(h0), c.ctypes.data, len(c),
+                       ys.ctypes.data, hs.ctypes.data)
+
+    y, h = _run_channels(fn, ch, L, N, threads)
+    if full:
+        return (y.reshape(B, H, P, L).transpose(0, 3, 1, 2).copy(), h.reshape(B, H, P, N))
+    return y, h

@@ -1,0 +1,170 @@
+/*
+ * CPU oracle for the Mamba selective scan -- TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the plain, slow, sequential definition of what the HIP path
+ * computes, written in fp64.  Only the test suite, the smoke check and the
+ * bench's CPU-baseline leg may load it.  It shares no code, header, table or
+ * helper with the HIP library, and the HIP library never calls it.
+ *
+ * Inputs are fp32 arrays (bf16 inputs arrive already widened to their exact
+ * fp32 values); every operation below is carried out in double precision and
+ * results are returned in double.  Build with -ffp-contract=off so that each
+ * line is evaluated exactly as written (no fused multiply-add contraction),
+ * which makes the step function and the scan bitwise comparable.
+ *
+ * What is computed, and where the pages state it
+ * ----------------------------------------------
+ * - The recurrence h_t = dA_t * h_{t-1} + dBx_t with a caller-given initial
+ *   state h_0 (zero when absent): "Adding Initial Value Support to Selective
+ *   Scan Forward Kernel" (state-spaces/mamba issue 285), the opening question
+ *   (h_t = A*h_{t-1} + Bx with h_0 fixed at 0, asking for an initial value).
+ * - Discretisation dA_t = exp(delta_t * A[d,n]): same page, the later reply
+ *   that gives the scan element as the pair (exp(delta*A), hidden_state) and
+ *   the backward note that uses exp(delta_0 * A); dBx_t = delta_t*B_t[n]*x_t
+ *   is the additive term of that pair.
+ * - The initial state enters as the pair (1, h0), i.e. it is h before step 1,
+ *   not a decay factor: same page, the reply that corrects the (h0, 0) seed to
+ *   (1, h0).  Here that is simply "h starts at h0".
+ * - Output y_t = sum_n C_t[n] h_t[n] + D[d] x_t, gated by silu(z_t) when z is
+ *   given: "ggml : add GPU support for Mamba models" (llama.cpp issue 6758):
+ *   the ssm_d {d_inner} tensor in compilade's ctx_layer diff, and jploski's
+ *   report that ggml_silu(ctx, z) is applied to the z half of xz.  The scan is
+ *   inclusive (y_t uses h_t after token t): the mamba page's InclusiveScan.
+ * - Inputs are not modified and the final state is a separate output: the
+ *   llama.cpp page, compilade's note that ggml_ssm_scan no longer modifies its
+ *   inputs and returns the final state with its output.
+ * - Decode (single-token state update, Megatron's selective_state_update in
+ *   "Clean up SSM ops directory structure - #6444"): the same step with L = 1,
+ *   state updated in place.
+ * - Mamba-2 SSD: the same recurrence per (b, head, p) with a scalar A per head,
+ *   so dA_t = exp(dt_t * A[h]) for every n, and B/C shared by the heads of a
+ *   group (head h uses group h / (H/G)): the SSD kernel family of the Megatron
+ *   page, the head-group naming and repeat_interleave of "Tensor-parallel SSM
+ *   #333", and the groups-divide-heads rule of "Current Implementation of TP in
+ *   MambaMixer2".  The chunked SSD algorithm reaches this recurrence exactly
+ *   (up to rounding order); the chunk length does not enter the definition.
+ *
+ * Layouts: row-major, last index fastest.
+ *   scan:   x, delta, z: (B, L, D); Bm, Cm: (B, L, N); A: (D, N); D_skip: (D);
+ *           h0: (B, D, N)
+ *   step:   state: (S, D, N); x, delta, z: (S, D); Bm, Cm: (S, N)
+ *   SSD:    x, z: (B, L, H, P); dt: (B, L, H); A, D_skip: (H); Bm, Cm:
+ *           (B, L, G, N); h0: (B, H, P, N)
+ * Outputs are written per requested channel so that a test can evaluate a
+ * sample of channels of a full-size problem:
+ *   y_out[k*L + t] and h_out[k*N + n] for the k-th requested channel.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/*
+ * Mamba-1 selective scan for channels c = b*D + d listed in `channels`.
+ * D_skip, z and h0 may be NULL (no skip term, no gate, zero initial state).
+ */
+void oracle_scan(int64_t B, int64_t L, int64_t D, int64_t N,
+                 const float *x, const float *delta, const float *A,
+                 const float *Bm, const float *Cm, const float *D_skip,
+                 const float *z, const float *h0,
+                 const int64_t *channels, int64_t n_channels,
+                 double *y_out, double *h_out)
+{
+    (void)B;
+    for (int64_t k = 0; k < n_channels; ++k) {
+        const int64_t b = channels[k] / D;
+        const int64_t d = channels[k] % D;
+        double *h = h_out + k * N;  /* running state h[n] of this channel */
+        for (int64_t n = 0; n < N; ++n)
+            h[n] = h0 ? (double)h0[(b * D + d) * N + n] : 0.0;
+
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t row = b * L + t;           /* token (b, t) */
+            const double dl = delta[row * D + d];
+            const double u = x[row * D + d];
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double dA = exp(dl * (double)A[d * N + n]);
+                const double dBx = dl * (double)Bm[row * N + n] * u;
+                h[n] = dA * h[n] + dBx;
+                acc += (double)Cm[row * N + n] * h[n];
+            }
+            double v = acc;
+            if (D_skip) v += (double)D_skip[d] * u;
+            if (z) v *= silu((double)z[row * D + d]);
+            y_out[k * L + t] = v;
+        }
+    }
+}
+
+/*
+ * One decode step for S sequences: the scan body with L = 1, state updated in
+ * place (fp64 state so a test can chain steps without fp32 rounding).
+ */
+void oracle_state_update(int64_t S, int64_t D, int64_t N, double *state,
+                         const float *x, const float *delta, const float *A,
+                         const float *Bm, const float *Cm, const float *D_skip,
+                         const float *z, double *y)
+{
+    for (int64_t s = 0; s < S; ++s) {
+        for (int64_t d = 0; d < D; ++d) {
+            double *h = state + (s * D + d) * N;
+            const double dl = delta[s * D + d];
+            const double u = x[s * D + d];
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double dA = exp(dl * (double)A[d * N + n]);
+                const double dBx = dl * (double)Bm[s * N + n] * u;
+                h[n] = dA * h[n] + dBx;
+                acc += (double)Cm[s * N + n] * h[n];
+            }
+            double v = acc;
+            if (D_skip) v += (double)D_skip[d] * u;
+            if (z) v *= silu((double)z[s * D + d]);
+            y[s * D + d] = v;
+        }
+    }
+}
+
+/*
+ * Mamba-2 SSD: the recurrence per channel c = (b*H + h)*P + p with scalar
+ * A[h] and B/C of group g = h / (H/G).  D_skip, z, h0 may be NULL.
+ */
+void oracle_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                const float *x, const float *dt, const float *A,
+                const float *Bm, const float *Cm, const float *D_skip,
+                const float *z, const float *h0,
+                const int64_t *channels, int64_t n_channels,
+                double *y_out, double *h_out)
+{
+    (void)B;
+    const int64_t heads_per_group = H / G;
+    for (int64_t k = 0; k < n_channels; ++k) {
+        const int64_t c = channels[k];
+        const int64_t p = c % P;
+        const int64_t hd = (c / P) % H;
+        const int64_t b = c / (P * H);
+        const int64_t g = hd / heads_per_group;
+        double *h = h_out + k * N;
+        for (int64_t n = 0; n < N; ++n)
+            h[n] = h0 ? (double)h0[((b * H + hd) * P + p) * N + n] : 0.0;
+
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t tok = b * L + t;
+            const double dl = dt[tok * H + hd];
+            const double u = x[(tok * H + hd) * P + p];
+            const double dA = exp(dl * (double)A[hd]);
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double dBx = dl * (double)Bm[(tok * G + g) * N + n] * u;
+                h[n] = dA * h[n] + dBx;
+                acc += (double)Cm[(tok * G + g) * N + n] * h[n];
+            }
+            double v = acc;
+            if (D_skip) v += (double)D_skip[hd] * u;
+            if (z) v *= silu((double)z[(tok * H + hd) * P + p]);
+            y_out[k * L + t] = v;
+        }
+    }
+}
