@@ -1,0 +1,178 @@
+/*
+ * ssm_scan.h -- C ABI of libssmscan.so, the MI355X (gfx950) selective-scan
+ * library.
+ *
+ * Every entry point takes plain pointers and sizes.  Unless stated otherwise
+ * a tensor pointer is a DEVICE pointer to a contiguous row-major array (last
+ * index fastest) owned by the caller; the library never allocates device
+ * memory, never frees caller memory and keeps no state between calls.  Work
+ * is enqueued on `stream` (a hipStream_t; NULL means the default stream) and
+ * the call returns without synchronising.  Arguments are validated on the
+ * host before anything is enqueued; a rejected call has no side effects.
+ * No entry point aborts the process: every failure is a status code.
+ *
+ * Notation follows the pages: B sequences (batch), L tokens, D channels
+ * (d_inner), N states per channel (d_state); for Mamba-2 SSD, H heads of P
+ * channels each and G groups of heads sharing B and C.
+ *
+ * Sources (page title, then the part of it that states the fact):
+ * [mamba#285]  "Adding Initial Value Support to Selective Scan Forward Kernel"
+ *              (state-spaces/mamba issue 285): the recurrence
+ *              h_t = dA*h_{t-1} + Bx, the scan pair (exp(delta*A), state), and
+ *              an initial state h0 of shape (B, D, N) entering as the pair
+ *              (1, h0) -- the opening question and the running-prefix replies.
+ * [ggml#6758]  "ggml : add GPU support for Mamba models" (llama.cpp issue
+ *              6758): the SSM_SCAN op ggml_ssm_scan(s, x, dt, A, B, C) with
+ *              tensors s {d_state, d_inner, n_seqs}, x/dt {d_inner,
+ *              n_seq_tokens, n_seqs}, A {d_state, d_inner}, B/C {d_state,
+ *              n_seq_tokens, n_seqs} (compilade's test patch, fastest
+ *              dimension first); the ssm_d {d_inner} skip term (ctx_layer
+ *              diff); silu(z) applied to the z half (jploski's silu report);
+ *              inputs left unmodified with the final state returned as an
+ *              output (compilade's follow-up); non-contiguous x/z views as a
+ *              source of wrong results (slaren's ggml_cont diff).
+ * [megatron#6444] "Clean up SSM ops directory structure - #6444": the decode
+ *              op selective_state_update and the Mamba-2 state-space-duality
+ *              kernels ssd_bmm, ssd_chunk_state, ssd_state_passing,
+ *              ssd_chunk_scan, ssd_combined.
+ * [fastllm#333] "Tensor-parallel SSM #333": head groups (repeat_interleave of
+ *              groups to heads) for Mamba-2.
+ * [mixer2-tp]  "Current Implementation of TP in MambaMixer2": the number of
+ *              groups divides the number of heads.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtype of x, delta (dt), z, Bm, Cm and y.  A, D_skip, h0, h_final
+ * and the decode state are always fp32; arithmetic is fp32 throughout. */
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_INVALID_ARG = 1, /* negative size, NULL required pointer, aliasing */
+    SSM_ERR_UNSUPPORTED = 2, /* size outside what the kernels are built for   */
+    SSM_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required        */
+    SSM_ERR_HIP = 4          /* a HIP launch failed (see hipGetLastError)      */
+} ssm_status;
+
+/* Kernel-variant selection for ssm_scan_fwd.  Pass NULL for the defaults.
+ * The default choice depends only on (L, D, N) -- never on B or on the
+ * device -- so a sequence gives bitwise the same result whatever batch it
+ * is part of.  */
+typedef struct {
+    int32_t variant;   /* 0 = automatic; 1 = channel-sequential (one lane per
+                          channel, all N states in registers, loop over L);
+                          2 = chunked over L (segment summaries, carry pass,
+                          output pass) */
+    int32_t chunk_len; /* variant 2: tokens per segment (multiple of 8,
+                          >= 8); 0 = automatic */
+    int32_t reserved[6]; /* must be zero */
+} ssm_tuning;
+
+/* Largest N the Mamba-1 kernels (scan and decode) are built for. */
+#define SSM_SCAN_MAX_N 64
+/* Largest N the SSD kernels are built for, and the supported head dim P. */
+#define SSM_SSD_MAX_N 256
+
+/*
+ * ssm_scan_fwd -- Mamba-1 selective scan over a prefill of L tokens.
+ *
+ * For every sequence b, channel d and state n ([mamba#285]):
+ *   dA_t  = exp(delta[b,t,d] * A[d,n])
+ *   dBx_t = delta[b,t,d] * Bm[b,t,n] * x[b,t,d]
+ *   h_t   = dA_t * h_{t-1} + dBx_t,   h_0 = h0[b,d,n] (zeros if h0 == NULL)
+ *   y[b,t,d] = (sum_n Cm[b,t,n] * h_t[n] + D_skip[d] * x[b,t,d])
+ *              * silu(z[b,t,d])       (skip term only if D_skip != NULL,
+ *                                      gate only if z != NULL; [ggml#6758])
+ *   h_final[b,d,n] = h_L[n]
+ * y_t uses the state after token t (inclusive scan).
+ *
+ * x, delta, z, y : (B, L, D), dtype `dt`
+ * Bm, Cm         : (B, L, N), dtype `dt`
+ * A              : (D, N) fp32;   D_skip : (D) fp32 or NULL
+ * h0, h_final    : (B, D, N) fp32; either may be NULL (h_final NULL = not
+ *                  returned).  h_final must not overlap h0 or any input.
+ * y must not overlap any input.  Inputs are never modified.
+ * workspace      : device scratch of at least ssm_scan_fwd_workspace_size()
+ *                  bytes (may be NULL when that size is 0); contents on
+ *                  entry are ignored.
+ * Sizes: B, L, D, N >= 0; N <= SSM_SCAN_MAX_N.  L == 0 writes h_final = h0
+ * (or zeros); B, D or N == 0 is a no-op.
+ * Returns SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED,
+ * SSM_ERR_WORKSPACE or SSM_ERR_HIP.
+ */
+ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                        const void *x, const void *delta, const float *A,
+                        const void *Bm, const void *Cm, const float *D_skip,
+                        const void *z, const float *h0, void *y, float *h_final,
+                        void *workspace, size_t workspace_bytes,
+                        const ssm_tuning *tuning, void *stream);
+
+/* Device workspace ssm_scan_fwd needs for these sizes and tuning (bytes). */
+size_t ssm_scan_fwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N,
+                                   const ssm_tuning *tuning);
+
+/*
+ * ssm_state_update -- one decode step for S independent sequences
+ * (selective_state_update, [megatron#6444]): the ssm_scan_fwd body with
+ * L = 1, the state read and written IN PLACE.
+ *
+ * state          : (S, D, N) fp32, in/out
+ * x, delta, z, y : (S, D), dtype `dt`;  Bm, Cm : (S, N), dtype `dt`
+ * A              : (D, N) fp32;  D_skip : (D) fp32 or NULL;  z may be NULL.
+ * y must not overlap any input or the state.  Sizes as ssm_scan_fwd.
+ */
+ssm_status ssm_state_update(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
+                            float *state, const void *x, const void *delta,
+                            const float *A, const void *Bm, const void *Cm,
+                            const float *D_skip, const void *z, void *y,
+                            void *stream);
+
+/*
+ * ssm_ssd_fwd -- Mamba-2 state-space-duality (SSD) chunked scan
+ * (ssd_combined and the kernels it drives, [megatron#6444]).
+ *
+ * Per sequence b, head h, channel p < P and state n, with group
+ * g = h / (H / G) ([fastllm#333], [mixer2-tp]):
+ *   dA_t  = exp(dt[b,t,h] * A[h])                  (scalar per head)
+ *   h_t[p,n] = dA_t * h_{t-1}[p,n] + dt[b,t,h] * Bm[b,t,g,n] * x[b,t,h,p]
+ *   y[b,t,h,p] = (sum_n Cm[b,t,g,n] h_t[p,n] + D_skip[h] x[b,t,h,p])
+ *                * silu(z[b,t,h,p])
+ * computed chunk by chunk (`chunk` tokens): intra-chunk products on the
+ * matrix cores, chunk states passed sequentially in fp32, seeded by h0.
+ *
+ * x, z, y   : (B, L, H, P) dtype `dt`;  dt_in : (B, L, H) dtype `dt`
+ * Bm, Cm    : (B, L, G, N) dtype `dt`;  A, D_skip : (H) fp32 (D_skip may be NULL)
+ * h0, h_final : (B, H, P, N) fp32 or NULL.  z may be NULL.
+ * Supported: dt == SSM_BF16; P == 64; N a multiple of 32 with
+ * N <= SSM_SSD_MAX_N; chunk in {64, 128, 256}; H % G == 0.  Other sizes
+ * return SSM_ERR_UNSUPPORTED.  Any L >= 0 (a ragged last chunk is handled).
+ */
+ssm_status ssm_ssd_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                       int64_t N, int64_t chunk, ssm_dtype dt, const void *x,
+                       const void *dt_in, const float *A, const void *Bm,
+                       const void *Cm, const float *D_skip, const void *z,
+                       const float *h0, void *y, float *h_final,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+size_t ssm_ssd_fwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P,
+                                  int64_t G, int64_t N, int64_t chunk);
+
+/* Static description of a status code. */
+const char *ssm_status_string(ssm_status s);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int ssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

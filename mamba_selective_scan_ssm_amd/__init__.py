@@ -1,0 +1,213 @@
+"""Python binding of libssmscan.so, the gfx950 selective-scan library.
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity) and their device pointers, sizes and torch's current HIP stream
+are passed to the C ABI declared in include/ssm_scan.h.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library is missing the import of this module still works, but every call
+raises -- build it with ``python -m mamba_selective_scan_ssm_amd.build``.
+
+Non-contiguous inputs are rejected rather than copied: strided x/z views of
+a packed in-projection were a source of wrong results in the llama.cpp Mamba
+GPU port ("ggml : add GPU support for Mamba models", the ggml_cont fixes).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip error"}
+
+
+class SSMError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: status {code} ({STATUS.get(code, '?')})")
+        self.code = code
+
+
+class Tuning(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libssmscan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: the HIP library has not been built")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        L.ssm_scan_fwd.argtypes = [i64, i64, i64, i64, ctypes.c_int] + [vp] * 10 + [vp, sz, vp, vp]
+        L.ssm_scan_fwd.restype = ctypes.c_int
+        L.ssm_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i64, vp]
+        L.ssm_scan_fwd_workspace_size.restype = sz
+        L.ssm_state_update.argtypes = [i64, i64, i64, ctypes.c_int] + [vp] * 9 + [vp]
+        L.ssm_state_update.restype = ctypes.c_int
+        L.ssm_ssd_fwd.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 10 + [vp, sz, vp]
+        L.ssm_ssd_fwd.restype = ctypes.c_int
+        L.ssm_ssd_fwd_workspace_size.argtypes = [i64] * 7
+        L.ssm_ssd_fwd_workspace_size.restype = sz
+        L.ssm_status_string.argtypes = [ctypes.c_int]
+        L.ssm_status_string.restype = ctypes.c_char_p
+        L.ssm_version.argtypes = []
+        L.ssm_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: expected float32 or bfloat16")
+
+
+def _check(name, t, shape, dtype, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _call(fn_name, *args):
+    rc = getattr(lib(), fn_name)(*args)
+    if rc != 0:
+        raise SSMError(fn_name, rc)
+
+
+def scan_fwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, y=None, h_final=None,
+             return_final=True, variant=0, chunk_len=0, workspace=None):
+    """Mamba-1 selective scan (ssm_scan_fwd).
+
+    x, delta, z: (B, L, D); Bm, Cm: (B, L, N), all float32 or all bfloat16;
+    A: (D, N) float32; D_skip: (D,) float32; h0: (B, D, N) float32.
+    Returns (y, h_final); y has the input dtype, h_final is float32.
+    """
+    if x.dim() != 3 or Bm.dim() != 3:
+        raise ValueError("x must be (B, L, D) and Bm (B, L, N)")
+    B, L, D = x.shape
+    N = Bm.shape[2]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _check("x", x, (B, L, D), dt, dev)
+    _check("delta", delta, (B, L, D), dt, dev)
+    _check("z", z, (B, L, D), dt, dev)
+    _check("Bm", Bm, (B, L, N), dt, dev)
+    _check("Cm", Cm, (B, L, N), dt, dev)
+    _check("A", A, (D, N), torch.float32, dev)
+    _check("D_skip", D_skip, (D,), torch.float32, dev)
+    _check("h0", h0, (B, D, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, L, D), dtype=dt, device=dev)
+    _check("y", y, (B, L, D), dt, dev)
+    if h_final is None and return_final:
+        h_final = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+    _check("h_final", h_final, (B, D, N), torch.float32, dev)
+    tun = Tuning(variant, chunk_len)
+    ws_bytes = lib().ssm_scan_fwd_workspace_size(B, L, D, N, ctypes.byref(tun))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("ssm_scan_fwd", B, L, D, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+          _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), ws_len,
+          ctypes.byref(tun), _stream(dev))
+    return y, h_final
+
+
+def scan_fwd_workspace_size(B, L, D, N, variant=0, chunk_len=0) -> int:
+    return int(lib().ssm_scan_fwd_workspace_size(B, L, D, N, ctypes.byref(Tuning(variant, chunk_len))))
+
+
+def state_update(state, x, delta, A, Bm, Cm, D_skip=None, z=None, *, y=None):
+    """One decode step (ssm_state_update); `state` (S, D, N) float32 is updated in place.
+
+    x, delta, z: (S, D); Bm, Cm: (S, N) float32 or bfloat16.  Returns y (S, D).
+    """
+    S, D, N = state.shape
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _check("state", state, (S, D, N), torch.float32, dev)
+    for nm, t in (("x", x), ("delta", delta), ("z", z)):
+        _check(nm, t, (S, D), dt, dev)
+    _check("Bm", Bm, (S, N), dt, dev)
+    _check("Cm", Cm, (S, N), dt, dev)
+    _check("A", A, (D, N), torch.float32, dev)
+    _check("D_skip", D_skip, (D,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((S, D), dtype=dt, device=dev)
+    _check("y", y, (S, D), dt, dev)
+    _call("ssm_state_update", S, D, N, code, _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
+          _ptr(Cm), _ptr(D_skip), _ptr(z), _ptr(y), _stream(dev))
+    return y
+
+
+def ssd_fwd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, *, chunk=256, y=None, h_final=None,
+            return_final=True, workspace=None):
+    """Mamba-2 SSD chunked scan (ssm_ssd_fwd).
+
+    x, z: (B, L, H, P); dt: (B, L, H); Bm, Cm: (B, L, G, N) bfloat16;
+    A, D_skip: (H,) float32; h0: (B, H, P, N) float32.  Returns (y, h_final).
+    """
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    dev, typ = x.device, x.dtype
+    code = _dtype_code(x)
+    _check("x", x, (B, L, H, P), typ, dev)
+    _check("dt", dt, (B, L, H), typ, dev)
+    _check("z", z, (B, L, H, P), typ, dev)
+    _check("Bm", Bm, (B, L, G, N), typ, dev)
+    _check("Cm", Cm, (B, L, G, N), typ, dev)
+    _check("A", A, (H,), torch.float32, dev)
+    _check("D_skip", D_skip, (H,), torch.float32, dev)
+    _check("h0", h0, (B, H, P, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, L, H, P), dtype=typ, device=dev)
+    _check("y", y, (B, L, H, P), typ, dev)
+    if h_final is None and return_final:
+        h_final = torch.empty((B, H, P, N), dtype=torch.float32, device=dev)
+    _check("h_final", h_final, (B, H, P, N), torch.float32, dev)
+    ws_bytes = lib().ssm_ssd_fwd_workspace_size(B, L, H, P, G, N, chunk)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("ssm_ssd_fwd", B, L, H, P, G, N, chunk, code, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm),
+          _ptr(Cm), _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace),
+          ws_len, _stream(dev))
+    return y, h_final
+
+
+def ssd_fwd_workspace_size(B, L, H, P, G, N, chunk) -> int:
+    return int(lib().ssm_ssd_fwd_workspace_size(B, L, H, P, G, N, chunk))
+
+
+def version() -> int:
+    return int(lib().ssm_version())

@@ -1,0 +1,216 @@
+// C ABI of libssmscan.so: host-side validation, variant choice and dispatch.
+// Validation is pure host code and runs before any HIP call, so a rejected
+// call enqueues nothing and has no side effects.
+#include "../../include/ssm_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.h"
+
+namespace {
+
+using ssm::DType;
+
+constexpr int64_t kMaxGridYZ = 65535;
+
+bool valid_dtype(ssm_dtype dt) { return dt == SSM_F32 || dt == SSM_BF16; }
+int64_t esize(ssm_dtype dt) { return dt == SSM_BF16 ? 2 : 4; }
+
+struct Range {
+  const void *p;
+  int64_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+template <size_t K>
+bool overlaps_any(Range out, const Range (&ins)[K]) {
+  for (size_t i = 0; i < K; ++i)
+    if (overlap(out, ins[i])) return true;
+  return false;
+}
+
+bool tuning_ok(const ssm_tuning *t) {
+  if (!t) return true;
+  for (int i = 0; i < 6; ++i)
+    if (t->reserved[i] != 0) return false;
+  if (t->variant < 0 || t->variant > 2) return false;
+  if (t->chunk_len < 0 || (t->chunk_len != 0 && (t->chunk_len < 8 || t->chunk_len % 8 != 0)))
+    return false;
+  return true;
+}
+
+// Variant choice: a function of (L, D, N) only, so a sequence's result does
+// not depend on the batch it is in.  Sequential when one sequence already
+// brings enough 64-channel waves or L is short; otherwise chunked with
+// segments sized so one sequence yields ~2048 waves.
+struct Plan {
+  int variant;  // 1 sequential, 2 chunked
+  int64_t seg_len;
+};
+
+Plan plan_scan(int64_t L, int64_t D, const ssm_tuning *t) {
+  const int64_t wps = (D + 63) / 64;  // waves per sequence and segment
+  int variant = t ? t->variant : 0;
+  int64_t seg = t ? t->chunk_len : 0;
+  if (variant == 0) variant = (L <= 256 || wps >= 64) ? 1 : 2;
+  if (variant == 2 && seg == 0) {
+    int64_t nseg = 2048 / (wps > 0 ? wps : 1);
+    if (nseg < 1) nseg = 1;
+    seg = (L + nseg - 1) / nseg;
+    seg = (seg + 7) / 8 * 8;
+    if (seg < 64) seg = 64;
+  }
+  if (variant == 2 && seg <= 0) seg = 64;
+  return Plan{variant, seg};
+}
+
+ssm_status hip_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ssm_status_string(ssm_status s) {
+  switch (s) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_INVALID_ARG: return "invalid argument";
+    case SSM_ERR_UNSUPPORTED: return "unsupported size or dtype";
+    case SSM_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSM_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int ssm_version(void) { return 100; }  // 0.1.0
+
+size_t ssm_scan_fwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N,
+                                   const ssm_tuning *tuning) {
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0 || !tuning_ok(tuning)) return 0;
+  const Plan p = plan_scan(L, D, tuning);
+  if (p.variant != 2) return 0;
+  return static_cast<size_t>(ssm::scan_chunked_ws_floats(B, L, D, N, p.seg_len)) * sizeof(float);
+}
+
+ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt, const void *x,
+                        const void *delta, const float *A, const void *Bm, const void *Cm,
+                        const float *D_skip, const void *z, const float *h0, void *y,
+                        float *h_final, void *workspace, size_t workspace_bytes,
+                        const ssm_tuning *tuning, void *stream) {
+  if (B < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_INVALID_ARG;
+  if (!valid_dtype(dt) || !tuning_ok(tuning)) return SSM_ERR_INVALID_ARG;
+  if (N > SSM_SCAN_MAX_N) return SSM_ERR_UNSUPPORTED;
+  if (B == 0 || D == 0) return SSM_OK;
+  if (B > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  const int64_t es = esize(dt);
+  const int64_t nBLD = B * L * D, nBLN = B * L * N, nBDN = B * D * N;
+  if (L > 0 && (!x || !delta || !y)) return SSM_ERR_INVALID_ARG;
+  if (L > 0 && N > 0 && (!Bm || !Cm)) return SSM_ERR_INVALID_ARG;
+  if (N > 0 && !A) return SSM_ERR_INVALID_ARG;
+  const Range ins[] = {{x, nBLD * es},   {delta, nBLD * es}, {A, D * N * 4}, {Bm, nBLN * es},
+                       {Cm, nBLN * es},  {D_skip, D * 4},    {z, nBLD * es}, {h0, nBDN * 4}};
+  if (overlaps_any(Range{y, nBLD * es}, ins)) return SSM_ERR_INVALID_ARG;
+  if (overlaps_any(Range{h_final, nBDN * 4}, ins)) return SSM_ERR_INVALID_ARG;
+  if (overlap(Range{y, nBLD * es}, Range{h_final, nBDN * 4})) return SSM_ERR_INVALID_ARG;
+
+  ssm::ScanArgs a{};
+  a.B = B; a.L = L; a.D = D; a.N = N;
+  a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
+  a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
+  a.D_skip = D_skip; a.z = z; a.h0 = h0; a.y = y; a.h_final = h_final;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const Plan p = plan_scan(L, D, tuning);
+  if (p.variant == 2 && L > 0 && N > 0) {
+    const int64_t nseg = (L + p.seg_len - 1) / p.seg_len;
+    if (nseg > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+    const size_t need = static_cast<size_t>(ssm::scan_chunked_ws_floats(B, L, D, N, p.seg_len)) * 4;
+    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+    if (overlaps_any(Range{workspace, static_cast<int64_t>(need)}, ins)) return SSM_ERR_INVALID_ARG;
+    return hip_status(ssm::launch_scan_chunked(a, p.seg_len, static_cast<float *>(workspace), s));
+  }
+  return hip_status(ssm::launch_scan_sequential(a, s));
+}
+
+ssm_status ssm_state_update(int64_t S, int64_t D, int64_t N, ssm_dtype dt, float *state,
+                            const void *x, const void *delta, const float *A, const void *Bm,
+                            const void *Cm, const float *D_skip, const void *z, void *y,
+                            void *stream) {
+  if (S < 0 || D < 0 || N < 0 || !valid_dtype(dt)) return SSM_ERR_INVALID_ARG;
+  if (N > SSM_SCAN_MAX_N) return SSM_ERR_UNSUPPORTED;
+  if (S == 0 || D == 0) return SSM_OK;
+  if (S > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  if (!x || !delta || !y) return SSM_ERR_INVALID_ARG;
+  if (N > 0 && (!state || !A || !Bm || !Cm)) return SSM_ERR_INVALID_ARG;
+  const int64_t es = esize(dt);
+  const Range ins[] = {{x, S * D * es},  {delta, S * D * es}, {A, D * N * 4}, {Bm, S * N * es},
+                       {Cm, S * N * es}, {D_skip, D * 4},     {z, S * D * es}};
+  const Range st{state, S * D * N * 4};
+  if (overlaps_any(Range{y, S * D * es}, ins) || overlap(Range{y, S * D * es}, st))
+    return SSM_ERR_INVALID_ARG;
+  if (overlaps_any(st, ins)) return SSM_ERR_INVALID_ARG;
+
+  ssm::StepArgs a{};
+  a.S = S; a.D = D; a.N = N;
+  a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
+  a.state = state; a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
+  a.D_skip = D_skip; a.z = z; a.y = y;
+  // The vectorised step needs 16-byte aligned state and A rows.
+  const bool aligned = (reinterpret_cast<uintptr_t>(state) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(A) % 16 == 0);
+  a.vec_ok = aligned;
+  return hip_status(ssm::launch_state_update(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t ssm_ssd_fwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                  int64_t N, int64_t chunk) {
+  if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk <= 0) return 0;
+  return static_cast<size_t>(ssm::ssd_ws_bytes(B, L, H, P, G, N, chunk));
+}
+
+ssm_status ssm_ssd_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                       int64_t chunk, ssm_dtype dt, const void *x, const void *dt_in,
+                       const float *A, const void *Bm, const void *Cm, const float *D_skip,
+                       const void *z, const float *h0, void *y, float *h_final, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  if (B < 0 || L < 0 || H < 0 || P < 0 || G < 0 || N < 0 || chunk < 0 || !valid_dtype(dt))
+    return SSM_ERR_INVALID_ARG;
+  if (dt != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (P != 64 || N % 32 != 0 || N > SSM_SSD_MAX_N || N == 0) return SSM_ERR_UNSUPPORTED;
+  if (chunk != 64 && chunk != 128 && chunk != 256) return SSM_ERR_UNSUPPORTED;
+  if (G <= 0 || H % G != 0) return SSM_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return SSM_OK;
+  const int64_t nc = (L + chunk - 1) / chunk;
+  if (B > kMaxGridYZ || H > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  if (L > 0 && (!x || !dt_in || !Bm || !Cm || !y)) return SSM_ERR_INVALID_ARG;
+  if (!A) return SSM_ERR_INVALID_ARG;
+  const int64_t es = 2;
+  const int64_t nX = B * L * H * P, nB = B * L * G * N, nS = B * H * P * N;
+  const Range ins[] = {{x, nX * es},  {dt_in, B * L * H * es}, {A, H * 4},  {Bm, nB * es},
+                       {Cm, nB * es}, {D_skip, H * 4},         {z, nX * es}, {h0, nS * 4}};
+  if (overlaps_any(Range{y, nX * es}, ins)) return SSM_ERR_INVALID_ARG;
+  if (overlaps_any(Range{h_final, nS * 4}, ins)) return SSM_ERR_INVALID_ARG;
+  if (overlap(Range{y, nX * es}, Range{h_final, nS * 4})) return SSM_ERR_INVALID_ARG;
+  const int64_t need = ssm::ssd_ws_bytes(B, L, H, P, G, N, chunk);
+  if (need > 0 && (!workspace || static_cast<int64_t>(workspace_bytes) < need))
+    return SSM_ERR_WORKSPACE;
+  if (need > 0 && (overlaps_any(Range{workspace, need}, ins) ||
+                   overlap(Range{workspace, need}, Range{y, nX * es}) ||
+                   overlap(Range{workspace, need}, Range{h_final, nS * 4})))
+    return SSM_ERR_INVALID_ARG;
+  (void)nc;
+
+  ssm::SSDArgs a{};
+  a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N; a.chunk = chunk;
+  a.x = x; a.dt = dt_in; a.A = A; a.Bm = Bm; a.Cm = Cm; a.D_skip = D_skip; a.z = z;
+  a.h0 = h0; a.y = y; a.h_final = h_final;
+  return hip_status(ssm::launch_ssd(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal launcher interface between the C ABI (capi.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+struct ScanArgs {
+  int64_t B, L, D, N;
+  DType dt;
+  const void *x, *delta;
+  const float *A;
+  const void *Bm, *Cm;
+  const float *D_skip;
+  const void *z;
+  const float *h0;
+  void *y;
+  float *h_final;
+};
+
+// Channel-sequential scan: one lane per (b, d), all N states in registers,
+// loop over the L tokens.  h0 and h_final may alias (same lane reads then
+// writes its own row), which the decode fallback relies on.
+hipError_t launch_scan_sequential(const ScanArgs &a, hipStream_t s);
+
+// Chunked scan: segment summaries, carry pass over segments, output pass.
+// ws must hold scan_chunked_ws_floats(a, seg_len) floats.
+int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg_len);
+hipError_t launch_scan_chunked(const ScanArgs &a, int64_t seg_len, float *ws, hipStream_t s);
+
+struct StepArgs {
+  int64_t S, D, N;
+  DType dt;
+  float *state;
+  const void *x, *delta;
+  const float *A;
+  const void *Bm, *Cm;
+  const float *D_skip;
+  const void *z;
+  void *y;
+  bool vec_ok;  // state and A rows 16-byte aligned: vectorised lanes allowed
+};
+
+hipError_t launch_state_update(const StepArgs &a, hipStream_t s);
+
+struct SSDArgs {
+  int64_t B, L, H, P, G, N, chunk;
+  const void *x, *dt;
+  const float *A;
+  const void *Bm, *Cm;
+  const float *D_skip;
+  const void *z;
+  const float *h0;
+  void *y;
+  float *h_final;
+};
+
+int64_t ssd_ws_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t chunk);
+hipError_t launch_ssd(const SSDArgs &a, void *ws, hipStream_t s);
+
+}  // namespace ssm

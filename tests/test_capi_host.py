@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host before any HIP call
+(a rejected call never reaches the device, so fake pointers are safe here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_selective_scan_ssm_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssm.LIB_PATH):
+        pytest.skip("libssmscan.so not built")
+    return ssm.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("ssm_scan_fwd", "ssm_scan_fwd_workspace_size", "ssm_state_update", "ssm_ssd_fwd",
+              "ssm_ssd_fwd_workspace_size", "ssm_status_string", "ssm_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert ssm.version() >= 100
+    for code in range(5):
+        assert lib.ssm_status_string(code)
+
+
+# fake, distinct, 256-byte-aligned "device" addresses: never dereferenced
+P = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(16)]
+
+
+def scan(lib, B=2, L=8, D=64, N=16, dt=F32, ptrs=None, ws=None, ws_len=0, tun=None, **over):
+    p = dict(x=P[0], delta=P[1], A=P[2], Bm=P[3], Cm=P[4], D_skip=P[5], z=P[6], h0=P[7], y=P[8],
+             h_final=P[9])
+    p.update(over)
+    return lib.ssm_scan_fwd(B, L, D, N, dt, p["x"], p["delta"], p["A"], p["Bm"], p["Cm"],
+                            p["D_skip"], p["z"], p["h0"], p["y"], p["h_final"], ws, ws_len,
+                            ctypes.byref(tun) if tun is not None else None, None)
+
+
+def test_scan_rejects_negative_sizes(lib):
+    for kw in (dict(B=-1), dict(L=-1), dict(D=-5), dict(N=-2)):
+        assert scan(lib, **kw) == INVALID
+
+
+def test_scan_rejects_large_n_and_bad_dtype(lib):
+    assert scan(lib, N=65) == UNSUPPORTED
+    assert scan(lib, dt=7) == INVALID
+
+
+def test_scan_rejects_null_required(lib):
+    for name in ("x", "delta", "A", "Bm", "Cm", "y"):
+        assert scan(lib, **{name: None}) == INVALID, name
+
+
+def test_scan_rejects_aliasing(lib):
+    assert scan(lib, y=P[0]) == INVALID                        # y on x
+    assert scan(lib, h_final=P[7]) == INVALID                  # h_final on h0
+    assert scan(lib, y=ctypes.c_void_p(P[1].value + 64)) == INVALID  # y inside delta
+
+
+def test_scan_empty_batch_is_noop(lib):
+    assert scan(lib, B=0) == OK
+    assert scan(lib, D=0) == OK
+
+
+def test_scan_tuning_validation(lib):
+    t = ssm.Tuning(3, 0)
+    assert scan(lib, tun=t) == INVALID
+    t = ssm.Tuning(2, 12)
+    assert scan(lib, tun=t) == INVALID
+    t = ssm.Tuning(0, 0)
+    t.reserved[2] = 1
+    assert scan(lib, tun=t) == INVALID
+
+
+def test_scan_chunked_needs_workspace(lib):
+    t = ssm.Tuning(2, 64)
+    need = lib.ssm_scan_fwd_workspace_size(2, 1024, 64, 16, ctypes.byref(t))
+    assert need == 2 * 2 * 16 * 64 * 16 * 4
+    assert scan(lib, L=1024, tun=t) == WORKSPACE
+    assert scan(lib, L=1024, tun=t, ws=P[12], ws_len=need - 4) == WORKSPACE
+    # workspace overlapping an input is rejected too
+    assert scan(lib, L=1024, tun=t, ws=P[0], ws_len=need) == INVALID
+
+
+def test_sequential_needs_no_workspace(lib):
+    t = ssm.Tuning(1, 0)
+    assert lib.ssm_scan_fwd_workspace_size(8, 4096, 5120, 16, ctypes.byref(t)) == 0
+
+
+def step(lib, S=4, D=64, N=16, dt=BF16, **over):
+    p = dict(state=P[0], x=P[1], delta=P[2], A=P[3], Bm=P[4], Cm=P[5], D_skip=P[6], z=P[7], y=P[8])
+    p.update(over)
+    return lib.ssm_state_update(S, D, N, dt, p["state"], p["x"], p["delta"], p["A"], p["Bm"], p["Cm"],
+                                p["D_skip"], p["z"], p["y"], None)
+
+
+def test_state_update_validation(lib):
+    assert step(lib, S=-1) == INVALID
+    assert step(lib, N=80) == UNSUPPORTED
+    assert step(lib, state=None) == INVALID
+    assert step(lib, y=P[0]) == INVALID   # y on the state
+    assert step(lib, y=P[1]) == INVALID   # y on x
+    assert step(lib, S=0) == OK
+
+
+def ssd(lib, B=1, L=512, H=8, P_=64, G=2, N=128, chunk=256, dt=BF16, ws=None, ws_len=0, **over):
+    p = dict(x=P[0], dtv=P[1], A=P[2], Bm=P[3], Cm=P[4], D_skip=P[5], z=P[6], h0=P[7], y=P[8],
+             h_final=P[9])
+    p.update(over)
+    return lib.ssm_ssd_fwd(B, L, H, P_, G, N, chunk, dt, p["x"], p["dtv"], p["A"], p["Bm"], p["Cm"],
+                           p["D_skip"], p["z"], p["h0"], p["y"], p["h_final"], ws, ws_len, None)
+
+
+def test_ssd_validation(lib):
+    assert ssd(lib, B=-1) == INVALID
+    assert ssd(lib, dt=F32) == UNSUPPORTED
+    assert ssd(lib, P_=48) == UNSUPPORTED
+    assert ssd(lib, N=100) == UNSUPPORTED
+    assert ssd(lib, chunk=100) == UNSUPPORTED
+    assert ssd(lib, H=8, G=3) == UNSUPPORTED
+    assert ssd(lib, y=P[0]) == INVALID
+    assert ssd(lib, B=0) == OK

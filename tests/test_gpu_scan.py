@@ -1,0 +1,239 @@
+"""GPU parity of ssm_scan_fwd against the CPU oracle (same seeded inputs).
+
+Each case prints its name, seed and shape before touching the GPU.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import ssm_inputs as gen
+from tests.helpers import assert_close, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [(1, 0), (2, 8), (2, 64)]  # (variant, chunk_len)
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def run_gpu(inp, gate=True, h0=True, variant=0, chunk_len=0, d_skip=True):
+    x = to_dev(inp.x)
+    y, hf = __import__("mamba_selective_scan_ssm_amd").scan_fwd(
+        x, to_dev(inp.delta), to_dev(inp.A), to_dev(inp.Bm), to_dev(inp.Cm),
+        to_dev(inp.D_skip) if d_skip else None, to_dev(inp.z) if gate else None,
+        to_dev(inp.h0) if h0 else None, variant=variant, chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    return to_np(y), to_np(hf)
+
+
+def run_oracle(oracle_mod, inp, gate=True, h0=True, channels=None, d_skip=True):
+    return oracle_mod.scan(inp.x.f32, inp.delta.f32, inp.A, inp.Bm.f32, inp.Cm.f32,
+                           inp.D_skip if d_skip else None, inp.z.f32 if gate else None,
+                           inp.h0 if h0 else None, channels=channels)
+
+
+@pytest.mark.parametrize("variant,chunk", VARIANTS)
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("h0", [False, True])
+def test_tiny_fp32(oracle_mod, variant, chunk, gate, h0):
+    inp = gen.make_workload("tiny_fp32")
+    _say("tiny_fp32", variant, chunk, gate, h0)
+    y, hf = run_gpu(inp, gate, h0, variant, chunk)
+    ry, rh = run_oracle(oracle_mod, inp, gate, h0)
+    assert_close(y, ry, "f32", "y")
+    assert_close(hf, rh, "f32", "h_final")
+
+
+@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 0), (2, 128)])
+@pytest.mark.parametrize("h0", [False, True])
+def test_mamba130m_fp32(oracle_mod, variant, chunk, h0):
+    inp = gen.make_workload("mamba130m_fp32")
+    _say("mamba130m_fp32", variant, chunk, h0)
+    y, hf = run_gpu(inp, True, h0, variant, chunk)
+    ry, rh = run_oracle(oracle_mod, inp, True, h0)
+    assert_close(y, ry, "f32", "y")
+    assert_close(hf, rh, "f32", "h_final")
+
+
+@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 0)])
+def test_mamba130m_split_sequence(oracle_mod, variant, chunk):
+    """Two calls of L/2 with h_final fed back as h0 equal one oracle scan of L."""
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_workload("mamba130m_fp32")
+    _say("mamba130m split", variant, chunk)
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds, h0 = to_dev(inp.A), to_dev(inp.D_skip), to_dev(inp.h0)
+    half = inp.L // 2
+    parts = []
+    h = h0
+    for sl in (slice(0, half), slice(half, inp.L)):
+        y, h = ssm.scan_fwd(t["x"][:, sl].contiguous(), t["delta"][:, sl].contiguous(), A,
+                            t["Bm"][:, sl].contiguous(), t["Cm"][:, sl].contiguous(), Ds,
+                            t["z"][:, sl].contiguous(), h, variant=variant, chunk_len=chunk)
+        parts.append(y)
+    torch.cuda.synchronize()
+    y = to_np(torch.cat(parts, 1))
+    ry, rh = run_oracle(oracle_mod, inp)
+    assert_close(y, ry, "f32", "y")
+    assert_close(to_np(h), rh, "f32", "h_final")
+
+
+def _sample_channels(B, D, k, seed):
+    rng = np.random.default_rng(seed)
+    ch = set(rng.integers(0, B * D, size=k).tolist())
+    for b in (0, B - 1):                # the edges of channel tiles and of D
+        for d in (0, 63, 64, D - 1):
+            ch.add(b * D + d)
+    return np.array(sorted(ch), dtype=np.int64)
+
+
+def test_mamba2p8b_prefill_bf16_sampled(oracle_mod):
+    """Full-size 2.8B-shaped prefill in the bench's launch configuration,
+    checked on sampled channels (each channel's whole sequence and state)."""
+    inp = gen.make_workload("mamba2p8b_prefill_bf16")
+    _say("mamba2p8b_prefill_bf16 full size, sampled channels")
+    y, hf = run_gpu(inp)
+    B, L, D, N = inp.B, inp.L, inp.D, inp.N
+    ch = _sample_channels(B, D, 96, 5)
+    ry, rh = run_oracle(oracle_mod, inp, channels=ch)
+    b, d = ch // D, ch % D
+    assert_close(y[b, :, d], ry, "bf16", "y")
+    assert_close(hf[b, d], rh, "bf16", "h_final")
+    # and the same channels as fp32-relative statistics, for the record
+    assert np.isfinite(y).all()
+
+
+SHAPES = [
+    # (B, L, D, N, dtype) -- llama.cpp's test-backend-ops SSM_SCAN shape first
+    (2, 7, 1536, 16, "f32"),
+    (8, 1024, 256, 16, "f32"),      # "more tokens and more sequences" (1024 tokens, 8 seqs)
+    (3, 37, 1500, 16, "bf16"),      # D not a multiple of 64, odd L
+    (2, 300, 100, 4, "f32"),
+    (2, 300, 100, 5, "f32"),        # N off the exact buckets
+    (1, 19, 70, 1, "bf16"),
+    (1, 50, 64, 64, "f32"),
+    (2, 1, 130, 16, "bf16"),        # single token
+    (2, 513, 96, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,L,D,N,dtype", SHAPES)
+@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 16)])
+def test_shapes(oracle_mod, B, L, D, N, dtype, variant, chunk):
+    inp = gen.make_scan(B, L, D, N, dtype=dtype, seed=100 + L + D + N)
+    _say("shape", B, L, D, N, dtype, variant, chunk)
+    y, hf = run_gpu(inp, variant=variant, chunk_len=chunk)
+    ry, rh = run_oracle(oracle_mod, inp)
+    assert_close(y, ry, dtype, "y")
+    assert_close(hf, rh, dtype, "h_final")
+
+
+def test_no_skip_no_gate_no_h0(oracle_mod):
+    inp = gen.make_scan(2, 40, 80, 16, dtype="f32", seed=21)
+    _say("no D, no z, no h0")
+    y, hf = run_gpu(inp, gate=False, h0=False, d_skip=False)
+    ry, rh = run_oracle(oracle_mod, inp, gate=False, h0=False, d_skip=False)
+    assert_close(y, ry, "f32", "y")
+    assert_close(hf, rh, "f32", "h_final")
+
+
+def test_empty_sequence_returns_h0(oracle_mod):
+    inp = gen.make_scan(2, 0, 70, 16, dtype="f32", seed=22)
+    _say("L=0")
+    y, hf = run_gpu(inp)
+    assert y.shape == (2, 0, 70)
+    np.testing.assert_array_equal(hf, inp.h0.astype(np.float64))
+    y, hf = run_gpu(inp, h0=False)
+    np.testing.assert_array_equal(hf, 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_batch_invariance_bitwise(dtype):
+    """A sequence gives bitwise the same y and h_final alone or in a batch."""
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(3, 300, 1536, 16, dtype=dtype, seed=23)
+    _say("batch invariance", dtype)
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds, h0 = to_dev(inp.A), to_dev(inp.D_skip), to_dev(inp.h0)
+    y, hf = ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0)
+    for b in range(3):
+        sl = slice(b, b + 1)
+        yb, hb = ssm.scan_fwd(t["x"][sl], t["delta"][sl], A, t["Bm"][sl], t["Cm"][sl], Ds,
+                              t["z"][sl], h0[sl])
+        assert torch.equal(yb, y[sl]) and torch.equal(hb, hf[sl])
+
+
+def test_repeat_determinism():
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(2, 777, 640, 16, dtype="bf16", seed=24)
+    _say("determinism")
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds, h0 = to_dev(inp.A), to_dev(inp.D_skip), to_dev(inp.h0)
+    for variant in (1, 2):
+        outs = [ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0,
+                             variant=variant) for _ in range(3)]
+        for y, hf in outs[1:]:
+            assert torch.equal(y, outs[0][0]) and torch.equal(hf, outs[0][1])
+
+
+def test_chunk_length_invariance(oracle_mod):
+    """Different segmentations agree with each other within the tolerance."""
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(1, 1000, 192, 16, dtype="f32", seed=25)
+    _say("chunk invariance")
+    ry, rh = run_oracle(oracle_mod, inp)
+    for ch in (8, 24, 200, 1000):
+        y, hf = run_gpu(inp, variant=2, chunk_len=ch)
+        assert_close(y, ry, "f32", f"y chunk {ch}")
+        assert_close(hf, rh, "f32", f"h chunk {ch}")
+
+
+def test_guard_bands_untouched():
+    """Outputs are written exactly in place: NaN guards around y and h_final stay NaN."""
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(2, 45, 100, 16, dtype="bf16", seed=26)
+    _say("guard bands")
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds, h0 = to_dev(inp.A), to_dev(inp.D_skip), to_dev(inp.h0)
+    G = 4096
+    for variant in (1, 2):
+        ybuf = torch.full((G + 2 * 45 * 100 + G,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        hbuf = torch.full((G + 2 * 100 * 16 + G,), float("nan"), dtype=torch.float32, device="cuda")
+        y = ybuf[G:G + 2 * 45 * 100].view(2, 45, 100)
+        hf = hbuf[G:G + 2 * 100 * 16].view(2, 100, 16)
+        ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, y=y, h_final=hf,
+                     variant=variant, chunk_len=16)
+        torch.cuda.synchronize()
+        assert torch.isnan(ybuf[:G]).all() and torch.isnan(ybuf[-G:]).all()
+        assert torch.isnan(hbuf[:G]).all() and torch.isnan(hbuf[-G:]).all()
+        assert torch.isfinite(y.float()).all() and torch.isfinite(hf).all()
+
+
+def test_nan_stays_in_its_channel():
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(2, 64, 128, 16, dtype="f32", seed=27)
+    _say("nan confinement")
+    x = inp.x.f32.copy()
+    x[1, 10, 77] = np.nan
+    y, hf = ssm.scan_fwd(to_dev(x), to_dev(inp.delta), to_dev(inp.A), to_dev(inp.Bm),
+                         to_dev(inp.Cm), to_dev(inp.D_skip), to_dev(inp.z), to_dev(inp.h0))
+    bad = ~torch.isfinite(y).cpu().numpy()
+    assert bad[1, 10:, 77].all()
+    bad[1, 10:, 77] = False
+    assert not bad.any()
+    hb = ~torch.isfinite(hf).cpu().numpy()
+    assert hb[1, 77].all()
+    hb[1, 77] = False
+    assert not hb.any()
+
+
+def test_rejects_non_contiguous():
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(1, 16, 64, 16, dtype="f32", seed=28)
+    xz = torch.randn(1, 16, 128, device="cuda")
+    with pytest.raises(ValueError):
+        ssm.scan_fwd(xz[..., :64], to_dev(inp.delta), to_dev(inp.A), to_dev(inp.Bm),
+                     to_dev(inp.Cm))
