@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of the selective-scan hot path on one MI355X.
+
+A step is one ssm_scan_fwd call over the Mamba-2.8B-shaped prefill workload
+(B=8, L=4096, D=5120, N=16; x/delta/z/B/C bf16, A/D fp32, fp32 state, random
+h0, silu(z) gate on) with all inputs resident in HBM.  The headline value is
+selective-scan elements per second, B*L*D*N / step time, in Gelem/s.
+
+The JSON line also carries
+* roofline: the scan kernel against the ceiling that binds it (measured live
+  with HIP events on the launch stream), plus its algorithmic HBM bandwidth
+  against the 8 TB/s peak;
+* cpu_baseline: the fp64 CPU oracle (untuned, threads over channels) timed
+  on a bounded sample of the same workload;
+* rows: the other hot-path entry points measured the same way -- the decode
+  step (S=256, D=5120, N=16, 128 steps) and the Mamba-2 SSD chunked scan
+  (B=2, L=8192, H=80, P=64, N=128, G=8, chunk 256).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# fp32 VALU lane rate from 157.3 TFLOP/s (FMA = 2 flops) and the
+# transcendental unit at a quarter of it (8 lanes/clk/SIMD * 1024 SIMDs * 2.4 GHz)
+VALU_LANE_OPS = 157.3e12 / 2
+TRANS_LANE_OPS = VALU_LANE_OPS / 4
+# per scan element: dA = exp2(delta*A2) -> 1 mul + 1 exp; u*B -> 1 mul;
+# h = dA*h + u*B -> 1 fma; y += C*h -> 1 fma.  6 flops + 1 transcendental.
+SCAN_VALU_PER_ELEM, SCAN_TRANS_PER_ELEM, SCAN_FLOPS_PER_ELEM = 4, 1, 6
+SCAN_ELEM_PEAK = 1.0 / (SCAN_VALU_PER_ELEM / VALU_LANE_OPS + SCAN_TRANS_PER_ELEM / TRANS_LANE_OPS)
+
+
+def csrc_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "mamba_selective_scan_ssm_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, launch_bytes_alg: float):
+    """HBM bytes per launch from committed rocprofv3 --pmc runs, if they were
+    taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            t = json.load(f)
+        e = t.get(kernel)
+        if not e or e.get("csrc_hash") != csrc_hash():
+            return None
+        return float(e["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def scan_alg_bytes(B, L, D, N, es, gate=True, h0=True, hf=True):
+    """Algorithmic HBM bytes of one scan: every input read once, outputs written once."""
+    b = B * L * D * es * (3 if gate else 2)      # x, delta, (z)
+    b += B * L * D * es                          # y
+    b += 2 * B * L * N * es                      # Bm, Cm
+    b += D * N * 4 + D * 4                       # A, D_skip
+    b += B * D * N * 4 * ((1 if h0 else 0) + (1 if hf else 0))
+    return float(b)
+
+
+def time_calls(fn, steps, warmup, torch):
+    """Mean time of `fn` (ms) with HIP events on the current stream, bracketed by syncs."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [a.elapsed_time(b) for a, b in ev]
+    return float(np.mean(per)), float(np.min(per)), wall
+
+
+def upload(t, torch):
+    if isinstance(t, np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).cuda()
+    if t.bf16 is not None:
+        return torch.from_numpy(t.bf16.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(t.f32)).cuda()
+
+
+def cpu_baseline(inp, n_seq: int):
+    import oracle
+    threads = min(16, oracle.default_threads())
+    D = inp.D
+    ch = np.arange(n_seq * D, dtype=np.int64)          # every channel of the first n_seq sequences
+    t0 = time.perf_counter()
+    oracle.scan(inp.x.f32, inp.delta.f32, inp.A, inp.Bm.f32, inp.Cm.f32, inp.D_skip, inp.z.f32,
+                inp.h0, channels=ch, threads=threads)
+    dt = time.perf_counter() - t0
+    elems = n_seq * inp.L * D * inp.N
+    return {"value": elems / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} of {inp.B} sequences (all {D} channels, L={inp.L}, N={inp.N}), "
+                      f"fp64 sequential recurrence, {dt:.2f} s wall"}
+
+
+def bench_decode(torch, ssm, gen, steps_meas=128):
+    dec = gen.make_workload("decode_256x5120_bf16")
+    S, D, N = dec.S, dec.D, dec.N
+    state = upload(dec.state0, torch)
+    xs, ds, zs, bs, cs = (upload(getattr(dec, k), torch) for k in ("x", "delta", "z", "Bm", "Cm"))
+    A, Ds = upload(dec.A, torch), upload(dec.D_skip, torch)
+    y = torch.empty((S, D), dtype=torch.bfloat16, device="cuda")
+    it = [0]
+
+    def one():
+        t = it[0] % dec.steps
+        it[0] += 1
+        ssm.state_update(state, xs[t], ds[t], A, bs[t], cs[t], Ds, zs[t], y=y)
+
+    mean_ms, min_ms, wall_ms = time_calls(one, steps_meas, 8, torch)
+    alg = S * D * N * 4 * 2 + S * D * 2 * 4 + 2 * S * N * 2 + D * N * 4 + D * 4
+    return {"workload": "decode_256x5120_bf16 (S=256, D=5120, N=16, bf16, fp32 state)",
+            "kernel_ms_per_step": mean_ms, "wall_ms_per_step": wall_ms,
+            "Gelem_per_s": S * D * N / (mean_ms * 1e-3) / 1e9,
+            "alg_bytes_per_step": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
+            "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_ssd(torch, ssm, gen, steps=10):
+    w = gen.make_workload("ssd_mamba2_bf16")
+    t = {k: upload(getattr(w, k), torch) for k in ("x", "dt", "Bm", "Cm")}
+    A, Ds, h0 = upload(w.A, torch), upload(w.D_skip, torch), upload(w.h0, torch)
+    ws_n = ssm.ssd_fwd_workspace_size(w.B, w.L, w.H, w.P, w.G, w.N, w.chunk)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.B, w.L, w.H, w.P), dtype=torch.bfloat16, device="cuda")
+    hf = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device="cuda")
+
+    def one():
+        ssm.ssd_fwd(t["x"], t["dt"], A, t["Bm"], t["Cm"], Ds, None, h0, chunk=w.chunk, y=y,
+                    h_final=hf, workspace=ws)
+
+    try:
+        one()
+    except Exception as e:  # not built for this configuration
+        return {"workload": "ssd_mamba2_bf16", "error": str(e)}
+    mean_ms, min_ms, wall_ms = time_calls(one, steps, 3, torch)
+    B, L, H, P, G, N = w.B, w.L, w.H, w.P, w.G, w.N
+    alg = (B * L * H * P * 2 * 2 + B * L * H * 2 + 2 * B * L * G * N * 2 + H * 8
+           + 2 * B * H * P * N * 4)
+    flops = 2.0 * B * L * (w.chunk * G * N + w.chunk * H * P + 2 * H * P * N)  # dense chunked GEMMs
+    return {"workload": "ssd_mamba2_bf16 (B=2, L=8192, H=80, P=64, N=128, G=8, chunk=256)",
+            "ms": mean_ms, "Gelem_per_s": B * L * H * P * N / (mean_ms * 1e-3) / 1e9,
+            "alg_bytes": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
+            "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "dense_gemm_TFLOPs": flops / (mean_ms * 1e-3) / 1e12,
+            "mfma_frac_bf16": flops / (mean_ms * 1e-3) / 2.5e15, "workspace_bytes": ws_n}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true", help="skip the decode and SSD rows")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seqs", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(channels and sequences are independent; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mamba_selective_scan_ssm_amd as ssm
+    import ssm_inputs as gen
+
+    name = "mamba2p8b_prefill_bf16"
+    inp = gen.make_workload(name)
+    B, L, D, N = inp.B, inp.L, inp.D, inp.N
+    t = {k: upload(getattr(inp, k), torch) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds, h0 = upload(inp.A, torch), upload(inp.D_skip, torch), upload(inp.h0, torch)
+    y = torch.empty((B, L, D), dtype=torch.bfloat16, device="cuda")
+    hf = torch.empty((B, D, N), dtype=torch.float32, device="cuda")
+    ws_n = ssm.scan_fwd_workspace_size(B, L, D, N)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, y=y, h_final=hf,
+                     workspace=ws)
+
+    mean_ms, min_ms, wall_ms = time_calls(step, args.steps, args.warmup, torch)
+    elems = B * L * D * N
+    value = elems / (wall_ms * 1e-3) / 1e9
+    alg = scan_alg_bytes(B, L, D, N, 2)
+    kern_s = mean_ms * 1e-3
+    hbm_gbs = alg / kern_s / 1e9
+    elem_rate = elems / kern_s
+    traffic = load_traffic("scan_fwd", alg)
+    roofline = {
+        "bound": "alu",
+        "achieved": elem_rate * SCAN_FLOPS_PER_ELEM / 1e12,
+        "peak": SCAN_ELEM_PEAK * SCAN_FLOPS_PER_ELEM / 1e12,
+        "unit": "TFLOP/s",
+        "frac": elem_rate / SCAN_ELEM_PEAK,
+        "traffic": traffic,
+        "kernel_ms": mean_ms,
+        "kernel_ms_min": min_ms,
+        "hbm": {"achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": hbm_gbs / HBM_PEAK_GBS, "alg_bytes_per_launch": alg},
+        "note": "per element 4 fp32 VALU ops + 1 v_exp_f32; ALU ceiling "
+                f"{SCAN_ELEM_PEAK / 1e12:.2f} Telem/s is below the HBM ceiling "
+                f"{HBM_PEAK_GBS * 1e9 / (alg / elems) / 1e12:.2f} Telem/s",
+    }
+    out = {
+        "metric": "selective-scan Gelem/s (B*L*D*N) + achieved HBM GB/s vs peak on 1 MI355X",
+        "value": value, "unit": "Gelem/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "mamba-2.8B-shaped prefill selective scan", "B": B, "L": L, "D": D,
+                   "N": N, "inputs": "x/delta/z/B/C bf16, A/D fp32, fp32 state, random h0, gate on",
+                   "parallelism": "single GPU"},
+        "hbm_GBs": hbm_gbs, "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
+        "roofline": roofline,
+    }
+    if not args.no_rows:
+        out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

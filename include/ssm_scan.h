@@ -67,13 +67,17 @@ typedef enum {
  * device -- so a sequence gives bitwise the same result whatever batch it
  * is part of.  */
 typedef struct {
-    int32_t variant;   /* 0 = automatic; 1 = channel-sequential (one lane per
-                          channel, all N states in registers, loop over L);
-                          2 = chunked over L (segment summaries, carry pass,
-                          output pass) */
+    int32_t variant;   /* 0 = automatic; 1 = channel-sequential (a workgroup
+                          per 64-channel tile whose waves split the N states,
+                          one pass over the L tokens); 2 = chunked over L
+                          (segment summaries, carry pass, output pass) */
     int32_t chunk_len; /* variant 2: tokens per segment (multiple of 8,
                           >= 8); 0 = automatic */
-    int32_t reserved[6]; /* must be zero */
+    int32_t states_per_lane; /* 0 = automatic; else 2, 4, 8 or 16: each lane
+                          keeps this many of a channel's N states and
+                          ceil(N / states_per_lane) waves (1, 2, 4 or 8)
+                          share a channel tile */
+    int32_t reserved[5]; /* must be zero */
 } ssm_tuning;
 
 /* Largest N the Mamba-1 kernels (scan and decode) are built for. */
@@ -101,10 +105,12 @@ typedef struct {
  *                  returned).  h_final must not overlap h0 or any input.
  * y must not overlap any input.  Inputs are never modified.
  * workspace      : device scratch of at least ssm_scan_fwd_workspace_size()
- *                  bytes (may be NULL when that size is 0); contents on
- *                  entry are ignored.
+ *                  bytes (may be NULL when that size is 0): B/C repacked to
+ *                  fp32 per token and wave, plus the segment summaries of the
+ *                  chunked schedule.  Contents on entry are ignored; it must
+ *                  not overlap any argument.
  * Sizes: B, L, D, N >= 0; N <= SSM_SCAN_MAX_N.  L == 0 writes h_final = h0
- * (or zeros); B, D or N == 0 is a no-op.
+ * (or zeros); B or D == 0 is a no-op; N == 0 leaves y = D_skip x silu(z).
  * Returns SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED,
  * SSM_ERR_WORKSPACE or SSM_ERR_HIP.
  */

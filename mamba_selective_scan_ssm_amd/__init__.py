@@ -34,7 +34,7 @@ class SSMError(RuntimeError):
 
 class Tuning(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("states_per_lane", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 _lib = None
@@ -105,7 +105,7 @@ def _call(fn_name, *args):
 
 
 def scan_fwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, y=None, h_final=None,
-             return_final=True, variant=0, chunk_len=0, workspace=None):
+             return_final=True, variant=0, chunk_len=0, states_per_lane=0, workspace=None):
     """Mamba-1 selective scan (ssm_scan_fwd).
 
     x, delta, z: (B, L, D); Bm, Cm: (B, L, N), all float32 or all bfloat16;
@@ -132,7 +132,7 @@ def scan_fwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, y=None, h_fin
     if h_final is None and return_final:
         h_final = torch.empty((B, D, N), dtype=torch.float32, device=dev)
     _check("h_final", h_final, (B, D, N), torch.float32, dev)
-    tun = Tuning(variant, chunk_len)
+    tun = Tuning(variant, chunk_len, states_per_lane)
     ws_bytes = lib().ssm_scan_fwd_workspace_size(B, L, D, N, ctypes.byref(tun))
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -143,8 +143,9 @@ def scan_fwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, y=None, h_fin
     return y, h_final
 
 
-def scan_fwd_workspace_size(B, L, D, N, variant=0, chunk_len=0) -> int:
-    return int(lib().ssm_scan_fwd_workspace_size(B, L, D, N, ctypes.byref(Tuning(variant, chunk_len))))
+def scan_fwd_workspace_size(B, L, D, N, variant=0, chunk_len=0, states_per_lane=0) -> int:
+    t = Tuning(variant, chunk_len, states_per_lane)
+    return int(lib().ssm_scan_fwd_workspace_size(B, L, D, N, ctypes.byref(t)))
 
 
 def state_update(state, x, delta, A, Bm, Cm, D_skip=None, z=None, *, y=None):

@@ -38,13 +38,17 @@ bool overlaps_any(Range out, const Range (&ins)[K]) {
 
 bool tuning_ok(const ssm_tuning *t) {
   if (!t) return true;
-  for (int i = 0; i < 6; ++i)
+  for (int i = 0; i < 5; ++i)
     if (t->reserved[i] != 0) return false;
   if (t->variant < 0 || t->variant > 2) return false;
   if (t->chunk_len < 0 || (t->chunk_len != 0 && (t->chunk_len < 8 || t->chunk_len % 8 != 0)))
     return false;
+  const int s = t->states_per_lane;
+  if (s != 0 && s != 2 && s != 4 && s != 8 && s != 16) return false;
   return true;
 }
+
+int spl_of(const ssm_tuning *t) { return t ? t->states_per_lane : 0; }
 
 // Variant choice: a function of (L, D, N) only, so a sequence's result does
 // not depend on the batch it is in.  Sequential when one sequence already
@@ -56,12 +60,12 @@ struct Plan {
 };
 
 Plan plan_scan(int64_t L, int64_t D, const ssm_tuning *t) {
-  const int64_t wps = (D + 63) / 64;  // waves per sequence and segment
+  const int64_t wps = (D + 63) / 64;  // channel tiles per sequence
   int variant = t ? t->variant : 0;
   int64_t seg = t ? t->chunk_len : 0;
   if (variant == 0) variant = (L <= 256 || wps >= 64) ? 1 : 2;
   if (variant == 2 && seg == 0) {
-    int64_t nseg = 2048 / (wps > 0 ? wps : 1);
+    int64_t nseg = 512 / (wps > 0 ? wps : 1);  // ~512 tiles x segments per sequence
     if (nseg < 1) nseg = 1;
     seg = (L + nseg - 1) / nseg;
     seg = (seg + 7) / 8 * 8;
@@ -90,12 +94,23 @@ const char *ssm_status_string(ssm_status s) {
 
 int ssm_version(void) { return 100; }  // 0.1.0
 
+// Workspace: the fp32 B/C pack, then (chunked only) the segment summaries.
+int64_t scan_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, const ssm_tuning *t,
+                       int64_t *pack_floats) {
+  *pack_floats = 0;
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
+  const Plan p = plan_scan(L, D, t);
+  int64_t pk = ssm::scan_pack_floats(B, L, N, spl_of(t));
+  pk = (pk + 63) / 64 * 64;  // keep the summaries 256-byte aligned
+  *pack_floats = pk;
+  return pk + (p.variant == 2 ? ssm::scan_chunked_ws_floats(B, L, D, N, p.seg_len) : 0);
+}
+
 size_t ssm_scan_fwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N,
                                    const ssm_tuning *tuning) {
-  if (B <= 0 || L <= 0 || D <= 0 || N <= 0 || !tuning_ok(tuning)) return 0;
-  const Plan p = plan_scan(L, D, tuning);
-  if (p.variant != 2) return 0;
-  return static_cast<size_t>(ssm::scan_chunked_ws_floats(B, L, D, N, p.seg_len)) * sizeof(float);
+  if (!tuning_ok(tuning) || N > SSM_SCAN_MAX_N) return 0;
+  int64_t pk;
+  return static_cast<size_t>(scan_ws_floats(B, L, D, N, tuning, &pk)) * sizeof(float);
 }
 
 ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt, const void *x,
@@ -127,15 +142,20 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const Plan p = plan_scan(L, D, tuning);
-  if (p.variant == 2 && L > 0 && N > 0) {
-    const int64_t nseg = (L + p.seg_len - 1) / p.seg_len;
-    if (nseg > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
-    const size_t need = static_cast<size_t>(ssm::scan_chunked_ws_floats(B, L, D, N, p.seg_len)) * 4;
-    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
-    if (overlaps_any(Range{workspace, static_cast<int64_t>(need)}, ins)) return SSM_ERR_INVALID_ARG;
-    return hip_status(ssm::launch_scan_chunked(a, p.seg_len, static_cast<float *>(workspace), s));
-  }
-  return hip_status(ssm::launch_scan_sequential(a, s));
+  if (L == 0 || N == 0) return hip_status(ssm::launch_scan_lane(a, s));  // no B/C to pack
+  if (p.variant == 2 && (L + p.seg_len - 1) / p.seg_len > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  int64_t pack = 0;
+  const int64_t need_f = scan_ws_floats(B, L, D, N, tuning, &pack);
+  const size_t need = static_cast<size_t>(need_f) * sizeof(float);
+  if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+  const Range wsr{workspace, static_cast<int64_t>(need)};
+  if (overlaps_any(wsr, ins) || overlap(wsr, Range{y, nBLD * es}) ||
+      overlap(wsr, Range{h_final, nBDN * 4}))
+    return SSM_ERR_INVALID_ARG;
+  float *ws = static_cast<float *>(workspace);
+  if (p.variant == 2)
+    return hip_status(ssm::launch_scan_chunked(a, spl_of(tuning), p.seg_len, ws, ws + pack, s));
+  return hip_status(ssm::launch_scan_sequential(a, spl_of(tuning), ws, s));
 }
 
 ssm_status ssm_state_update(int64_t S, int64_t D, int64_t N, ssm_dtype dt, float *state,

@@ -8,22 +8,42 @@
 // with the final state written to its own buffer.
 //
 // Layout in HBM: x, delta, z, y (B, L, D); Bm, Cm (B, L, N); A (D, N);
-// h0, h_final (B, D, N).  A wave owns 64 consecutive channels of one
-// sequence, so every per-token load and store of x/delta/z/y is one
-// contiguous 64-element row segment, and the B/C row of a token is the same
-// for the whole wave (scalar loads, shared by all 64 channels).  Each lane
-// keeps its channel's N states in VGPRs for the whole token loop.
+// h0, h_final (B, D, N).
 //
-// Two schedules share the token-loop body:
-//  * sequential: one pass over all L tokens per wave (no extra work);
+// Work decomposition (split kernel).  A workgroup owns 64 consecutive
+// channels of one sequence; its W waves split the N states of those
+// channels (SPL = states per lane, W * SPL >= N).  Each lane keeps its SPL
+// states in VGPRs for the whole token loop, so the per-element work is the
+// bare recurrence: one v_exp_f32 and four fp32 VALU ops.  Splitting N over
+// waves multiplies the number of independent waves by W, which the chip
+// needs (B*D/64 alone is 640 waves at the 2.8B prefill shape, fewer than
+// the 1024 SIMDs).
+//  * x/delta/z rows of a block of TB tokens are loaded two blocks ahead,
+//    coalesced over the 64 channels, converted once, and staged in LDS as
+//    delta, u = delta*x, D*x and z (fp32); every wave reads them from there.
+//  * B/C rows are shared by all channels: a pre-pass packs them to fp32 as
+//    [b][t][wave][B(SPL), C(SPL)] so each wave fetches its token's slice with
+//    one scalar load into SGPRs (prefetched a token or two ahead).
+//  * Each wave's partial y (its states' share of sum_n C h) goes to LDS;
+//    after a barrier per block, every wave finishes 1/W of the block's
+//    tokens: sums the partials, applies the gate and stores y.
+//
+// Schedules:
+//  * sequential: one pass over all L tokens per workgroup;
 //  * chunked: the L axis is cut into segments processed in parallel.  A
 //    summary pass runs each segment from a zero state and records the
-//    segment's affine map (prod of dA, state reached); a carry pass composes
-//    the maps segment by segment from the seed (1, h0) -- the composition
-//    (a1, b1) then (a2, b2) = (a2 a1, a2 b1 + b2) of the scan pair
-//    (exp(delta A), state) -- and an output pass reruns each segment from its
-//    incoming state to produce y.  It costs a second exp per element and is
-//    used when B*D is too small to fill the chip.
+//    segment's affine map (prod of dA = exp(A sum delta), state reached); a
+//    carry pass composes the maps segment by segment from the seed (1, h0)
+//    -- the composition (a1, b1) then (a2, b2) = (a2 a1, a2 b1 + b2) of the
+//    scan pair (exp(delta A), state) -- and an output pass reruns each
+//    segment from its incoming state to produce y.  It costs a second exp per
+//    element and is chosen when B*D is too small to fill the chip.
+//
+// A third, workspace-free kernel keeps all N states of a channel in one lane
+// (no cross-wave reduction); the decode step uses it for shapes its
+// vectorised kernel does not cover.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -31,141 +51,231 @@ namespace ssm {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kPrefetch = 8;  // tokens of x/delta/z kept in flight per lane
+constexpr int kTB = 8;  // tokens per block (LDS stage + barrier granularity)
 
 enum Mode : int { kFull = 0, kSummary = 1, kOutput = 2 };
 
-template <typename T>
-__device__ __forceinline__ T ld(const T *p) { return *p; }
+template <int K>
+using f32v = float __attribute__((ext_vector_type(K)));
+template <int K>
+using cf32v = __attribute__((address_space(4))) const f32v<K>;
 
-// One kernel body for the three roles.  Grid: x = 64-channel tile, y =
-// segment, z = sequence b.
+// ---------------------------------------------------------------------------
+// B/C pre-pass: (B, L, N) of T -> fp32 groups of G tokens,
+// [b][t / G][wave][t % G][B(SPL), C(SPL)], zero for t >= L or n >= N, so a
+// wave fetches G tokens of its states' B and C with one 64-byte scalar load.
+// ---------------------------------------------------------------------------
+template <int SPL>
+struct BCGroup {
+  static constexpr int G = SPL >= 8 ? 1 : 8 / SPL;  // tokens per scalar group
+  static constexpr int kFloats = G * 2 * SPL;        // 16 (32 for SPL = 16)
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void pack_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm,
+                                                      float *__restrict__ bc, int64_t B, int64_t L,
+                                                      int N, int W, int SPL, int G) {
+  const int64_t Lg = (L + G - 1) / G;
+  const int64_t per_grp = static_cast<int64_t>(W) * G * 2 * SPL;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= B * Lg * per_grp) return;
+  const int64_t bg = i / per_grp;  // b * Lg + t / G
+  int rem = static_cast<int>(i - bg * per_grp);
+  const int w = rem / (G * 2 * SPL);
+  rem -= w * G * 2 * SPL;
+  const int jj = rem / (2 * SPL), k = rem % (2 * SPL);
+  const int64_t b = bg / Lg, t = (bg % Lg) * G + jj;
+  const int n = w * SPL + (k % SPL);
+  float v = 0.f;
+  if (t < L && n < N) v = to_f32((k < SPL ? Bm : Cm)[(b * L + t) * N + n]);
+  bc[i] = v;
+}
+
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// ---------------------------------------------------------------------------
+// Split kernel.  Grid: x = 64-channel tile, y = segment, z = sequence b.
 //   kFull:    segment = all of L; h starts at h0 (or 0); writes y, h_final.
 //   kSummary: h starts at 0; writes seg_a[n] = exp(A * sum delta) and
 //             seg_h[n] = state reached, per (b, seg, d, n).
-//   kOutput:  h starts at seg_h (overwritten with the incoming state by the
-//             carry pass); writes y.
-template <typename T, int NB, bool EXACT, int MODE>
-__global__ __launch_bounds__(kWave) void scan_kernel(ScanArgs a, int64_t seg_len, float *seg_a,
-                                                     float *seg_h) {
+//   kOutput:  h starts at seg_h (the state entering the segment, written by
+//             the carry pass); writes y.
+// Segment lengths are multiples of kTB.  Tokens past the end of the last
+// block are staged with delta = u = 0, for which dA = 1 and the update adds
+// 0, so the state passes through them unchanged and no per-token branch is
+// needed.
+// ---------------------------------------------------------------------------
+template <typename T, int SPL, int W, int MODE>
+__global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, const float *bc,
+                                                              int64_t seg_len, float *seg_a,
+                                                              float *seg_h) {
+  constexpr bool kY = MODE != kSummary;
+  constexpr int kTokPerThread = kTB / W;  // tokens each thread stages per block
+  static_assert(kTB % W == 0, "W must divide the block length");
+  constexpr int G = BCGroup<SPL>::G;
+  constexpr int kGB = kTB / G;  // scalar groups per block (even)
+  static_assert(kGB % 2 == 0, "groups per block must be even for the static ring");
+  using GV = f32v<BCGroup<SPL>::kFloats>;
+
+  __shared__ float s_dl[2][kTB][kWave];
+  __shared__ float s_u[2][kTB][kWave];
+  __shared__ float s_dx[3][kTB][kWave];  // D[d] * x
+  __shared__ float s_z[3][kTB][kWave];
+  __shared__ float s_y[2][W][kTB][kWave];
+
   const int64_t D = a.D, L = a.L;
-  const int N = EXACT ? NB : static_cast<int>(a.N);
-  const int lane = threadIdx.x;
+  const int N = static_cast<int>(a.N);
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kWave + lane;
   const bool active = d_raw < D;
-  const int64_t d = active ? d_raw : D - 1;  // clamped: loads stay in bounds
-  const int64_t seg = blockIdx.y;
-  const int64_t nseg = gridDim.y;
-  const int64_t b = blockIdx.z;
+  const int64_t d = active ? d_raw : D - 1;
+  const int64_t seg = blockIdx.y, nseg = gridDim.y, b = blockIdx.z;
   const int64_t t0 = seg * seg_len;
   const int64_t t1 = (t0 + seg_len < L) ? t0 + seg_len : L;
+  const int64_t nblk = (t1 - t0 + kTB - 1) / kTB;
+  const int n0 = wave * SPL;
 
-  float A2[NB];
-#pragma unroll
-  for (int n = 0; n < NB; ++n) A2[n] = (EXACT || n < N) ? a.A[d * N + n] * kLog2e : 0.f;
-
+  float A2[SPL], h[SPL];
   const int64_t ws_row = ((b * nseg + seg) * D + d) * N;
-  float h[NB];
 #pragma unroll
-  for (int n = 0; n < NB; ++n) {
+  for (int s = 0; s < SPL; ++s) {
+    const int n = n0 + s;
+    const bool ok = n < N;
+    A2[s] = ok ? a.A[d * N + n] * kLog2e : 0.f;
     float v = 0.f;
-    if (EXACT || n < N) {
-      if (MODE == kFull && a.h0 != nullptr) v = a.h0[(b * D + d) * N + n];
-      if (MODE == kOutput) v = seg_h[ws_row + n];
-    }
-    h[n] = v;
+    if (ok && MODE == kFull && a.h0 != nullptr) v = a.h0[(b * D + d) * N + n];
+    if (ok && MODE == kOutput) v = seg_h[ws_row + n];
+    h[s] = v;
   }
 
   const T *xp = static_cast<const T *>(a.x) + b * L * D + d;
   const T *dp = static_cast<const T *>(a.delta) + b * L * D + d;
-  const T *zp = a.z ? static_cast<const T *>(a.z) + b * L * D + d : nullptr;
+  const T *zp = (kY && a.z) ? static_cast<const T *>(a.z) + b * L * D + d : nullptr;
   T *yp = static_cast<T *>(a.y) + b * L * D + d;
-  const T *Bp = static_cast<const T *>(a.Bm) + b * L * N;
-  const T *Cp = static_cast<const T *>(a.Cm) + b * L * N;
-  const float Dd = a.D_skip ? a.D_skip[d] : 0.f;
+  const float Dd = (a.D_skip != nullptr) ? a.D_skip[d] : 0.f;
   const bool has_z = zp != nullptr;
+  const int64_t Lg = (L + G - 1) / G;
+  const cf32v<BCGroup<SPL>::kFloats> *bcp =
+      (const cf32v<BCGroup<SPL>::kFloats> *)(bc) + (b * Lg) * W + wave;
+  const int64_t g_last = Lg - 1;  // clamp for prefetches past the end
+
+  // raw x/delta/z of two blocks in flight
+  T rx[2][kTokPerThread], rd[2][kTokPerThread], rz[2][kTokPerThread];
+
+  auto issue = [&](int set, int64_t blk) {
+#pragma unroll
+    for (int i = 0; i < kTokPerThread; ++i) {
+      int64_t t = t0 + blk * kTB + wave + i * W;
+      t = t < t1 ? t : t1 - 1;
+      rx[set][i] = xp[t * D];
+      rd[set][i] = dp[t * D];
+      if (has_z) rz[set][i] = zp[t * D];
+    }
+  };
+  auto stage = [&](int set, int64_t blk) {
+    const int b2 = static_cast<int>(blk & 1), b3 = static_cast<int>(blk % 3);
+#pragma unroll
+    for (int i = 0; i < kTokPerThread; ++i) {
+      const int j = wave + i * W;
+      const bool ok = t0 + blk * kTB + j < t1;
+      const float dl = ok ? to_f32(rd[set][i]) : 0.f;
+      const float xv = ok ? to_f32(rx[set][i]) : 0.f;
+      s_dl[b2][j][lane] = dl;
+      s_u[b2][j][lane] = dl * xv;
+      if (kY) {
+        s_dx[b3][j][lane] = Dd * xv;
+        if (has_z) s_z[b3][j][lane] = to_f32(rz[set][i]);
+      }
+    }
+  };
 
   float dsum = 0.f;
+  GV ring[2];
+  ring[0] = bcp[(t0 / G < g_last ? t0 / G : g_last) * W];
 
-  T xr[kPrefetch], dr[kPrefetch], zr[kPrefetch];
+  // recurrence over the kTB tokens of block blk
+  auto run_block = [&](int64_t blk) {
+    const int b2 = static_cast<int>(blk & 1);
+    const int64_t g0 = (t0 + blk * kTB) / G;
 #pragma unroll
-  for (int j = 0; j < kPrefetch; ++j) {
-    int64_t t = t0 + j < t1 ? t0 + j : t1 - 1;
-    if (t < t0) t = t0;  // empty segment: never used, keep in bounds
-    if (t1 > t0) {
-      xr[j] = ld(xp + t * D);
-      dr[j] = ld(dp + t * D);
-      if (MODE != kSummary && has_z) zr[j] = ld(zp + t * D);
-    }
-  }
-
-  for (int64_t tb = t0; tb < t1; tb += kPrefetch) {
-    T xn[kPrefetch], dn[kPrefetch], zn[kPrefetch];
-    const bool more = tb + kPrefetch < t1;
-    if (more) {
+    for (int q = 0; q < kGB; ++q) {
+      float dl[G], u[G];
+      wait_lgkm0();  // group q's B/C (issued a group ago) and earlier LDS ops
 #pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) {
-        int64_t t = tb + kPrefetch + j;
-        t = t < t1 ? t : t1 - 1;
-        xn[j] = ld(xp + t * D);
-        dn[j] = ld(dp + t * D);
-        if (MODE != kSummary && has_z) zn[j] = ld(zp + t * D);
+      for (int jj = 0; jj < G; ++jj) {
+        dl[jj] = s_dl[b2][q * G + jj][lane];
+        u[jj] = s_u[b2][q * G + jj][lane];
+      }
+      wait_lgkm0();  // the LDS reads, so no later wait has to cover a scalar load
+      {
+        int64_t gn = g0 + q + 1;
+        gn = gn < g_last ? gn : g_last;
+        ring[(q + 1) & 1] = bcp[gn * W];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+      const GV cur = ring[q & 1];
+#pragma unroll
+      for (int jj = 0; jj < G; ++jj) {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          const float dA = fast_exp2(dl[jj] * A2[s]);
+          h[s] = fmaf(dA, h[s], u[jj] * cur[jj * 2 * SPL + s]);
+          if (kY) acc = fmaf(cur[jj * 2 * SPL + SPL + s], h[s], acc);
+        }
+        if (kY) s_y[b2][wave][q * G + jj][lane] = acc;
+        if (MODE == kSummary) dsum += dl[jj];
       }
     }
+  };
+  auto reduce_block = [&](int64_t blk) {
+    const int b2 = static_cast<int>(blk & 1), b3 = static_cast<int>(blk % 3);
+    const int64_t tb = t0 + blk * kTB;
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
+    for (int i = 0; i < kTokPerThread; ++i) {
+      const int j = wave * kTokPerThread + i;
       const int64_t t = tb + j;
-      if (t < t1) {
-        const float dl = to_f32(dr[j]);
-        const float xv = to_f32(xr[j]);
-        const float u = dl * xv;
-        const T *Bt = Bp + t * N;
-        const T *Ct = Cp + t * N;
-        float acc0 = 0.f, acc1 = 0.f;
+      float v = s_y[b2][0][j][lane];
 #pragma unroll
-        for (int n = 0; n < NB; ++n) {
-          if (EXACT || n < N) {
-            const float dA = fast_exp2(dl * A2[n]);
-            h[n] = fmaf(dA, h[n], u * to_f32(Bt[n]));
-            if (MODE != kSummary) {
-              if (n & 1)
-                acc1 = fmaf(to_f32(Ct[n]), h[n], acc1);
-              else
-                acc0 = fmaf(to_f32(Ct[n]), h[n], acc0);
-            }
-          }
-        }
-        if (MODE == kSummary) {
-          dsum += dl;
-        } else {
-          float v = fmaf(Dd, xv, acc0 + acc1);
-          if (has_z) v *= silu(to_f32(zr[j]));
-          if (active) yp[t * D] = from_f32<T>(v);
-        }
-      }
+      for (int w = 1; w < W; ++w) v += s_y[b2][w][j][lane];
+      v += s_dx[b3][j][lane];
+      if (has_z) v *= silu(s_z[b3][j][lane]);
+      if (t < t1 && active) yp[t * D] = from_f32<T>(v);
     }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) {
-        xr[j] = xn[j];
-        dr[j] = dn[j];
-        if (MODE != kSummary && has_z) zr[j] = zn[j];
-      }
-    }
+  };
+
+  if (nblk > 0) {
+    issue(0, 0);
+    issue(1, 1);
+    stage(0, 0);
+    __syncthreads();
+  }
+  for (int64_t k = 0; k < nblk; k += 2) {
+    // raw set 0 holds block k (already staged), set 1 holds block k+1
+    issue(0, k + 2);
+    run_block(k);
+    stage(1, k + 1);
+    __syncthreads();
+    if (kY) reduce_block(k);
+    if (k + 1 >= nblk) break;
+    issue(1, k + 3);
+    run_block(k + 1);
+    stage(0, k + 2);
+    __syncthreads();
+    if (kY) reduce_block(k + 1);
   }
 
   if (!active) return;
-  if (MODE == kFull && a.h_final != nullptr) {
 #pragma unroll
-    for (int n = 0; n < NB; ++n)
-      if (EXACT || n < N) a.h_final[(b * D + d) * N + n] = h[n];
-  }
-  if (MODE == kSummary) {
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      if (EXACT || n < N) {
-        seg_a[ws_row + n] = fast_exp2(A2[n] * dsum);
-        seg_h[ws_row + n] = h[n];
+  for (int s = 0; s < SPL; ++s) {
+    const int n = n0 + s;
+    if (n < N) {
+      if (MODE == kFull && a.h_final != nullptr) a.h_final[(b * D + d) * N + n] = h[s];
+      if (MODE == kSummary) {
+        seg_a[ws_row + n] = fast_exp2(A2[s] * dsum);
+        seg_h[ws_row + n] = h[s];
       }
     }
   }
@@ -195,63 +305,165 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(int64_t B, int64_t D, i
   if (h_final) h_final[i] = carry;
 }
 
+// ---------------------------------------------------------------------------
+// Per-lane kernel (no workspace): one lane holds all N states of a channel.
+// Used by the decode step for shapes its vectorised kernel does not cover;
+// h0 and h_final may alias (each lane reads its row before writing it).
+// ---------------------------------------------------------------------------
 template <typename T, int NB, bool EXACT>
-hipError_t launch_full_t(const ScanArgs &a, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>((a.D + kWave - 1) / kWave), 1, static_cast<unsigned>(a.B));
-  scan_kernel<T, NB, EXACT, kFull><<<grid, kWave, 0, s>>>(a, a.L, nullptr, nullptr);
-  return hipGetLastError();
-}
+__global__ __launch_bounds__(kWave) void scan_lane_kernel(ScanArgs a) {
+  const int64_t D = a.D, L = a.L;
+  const int N = EXACT ? NB : static_cast<int>(a.N);
+  const int lane = threadIdx.x;
+  const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+  const bool active = d_raw < D;
+  const int64_t d = active ? d_raw : D - 1;
+  const int64_t b = blockIdx.z;
 
-template <typename T, int NB, bool EXACT>
-hipError_t launch_chunked_t(const ScanArgs &a, int64_t seg_len, float *ws, hipStream_t s) {
-  const int64_t nseg = (a.L + seg_len - 1) / seg_len;
-  float *seg_a = ws;
-  float *seg_h = ws + a.B * nseg * a.D * a.N;
-  dim3 grid(static_cast<unsigned>((a.D + kWave - 1) / kWave), static_cast<unsigned>(nseg),
-            static_cast<unsigned>(a.B));
-  scan_kernel<T, NB, EXACT, kSummary><<<grid, kWave, 0, s>>>(a, seg_len, seg_a, seg_h);
-  const int64_t total = a.B * a.D * a.N;
-  scan_carry_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, s>>>(
-      a.B, a.D, a.N, nseg, a.h0, seg_a, seg_h, a.h_final);
-  scan_kernel<T, NB, EXACT, kOutput><<<grid, kWave, 0, s>>>(a, seg_len, seg_a, seg_h);
-  return hipGetLastError();
-}
-
-// N bucket dispatch: exact instantiations for the common N, guarded buckets
-// for the rest.
-template <typename T, template <typename, int, bool> class F, typename... Args>
-hipError_t dispatch_n(int64_t N, Args &&...args) {
-  switch (N) {
-    case 4: return F<T, 4, true>::run(args...);
-    case 8: return F<T, 8, true>::run(args...);
-    case 16: return F<T, 16, true>::run(args...);
-    case 32: return F<T, 32, true>::run(args...);
-    case 64: return F<T, 64, true>::run(args...);
-    default: break;
+  float A2[NB], h[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const bool ok = EXACT || n < N;
+    A2[n] = ok ? a.A[d * N + n] * kLog2e : 0.f;
+    h[n] = (ok && a.h0 != nullptr) ? a.h0[(b * D + d) * N + n] : 0.f;
   }
-  if (N <= 4) return F<T, 4, false>::run(args...);
-  if (N <= 8) return F<T, 8, false>::run(args...);
-  if (N <= 16) return F<T, 16, false>::run(args...);
-  if (N <= 32) return F<T, 32, false>::run(args...);
-  return F<T, 64, false>::run(args...);
+  // B/C rows are the same for every lane: scalar loads of the raw bits
+  using Bits = typename std::conditional<sizeof(T) == 2, uint16_t, float>::type;
+  using BT = __attribute__((address_space(4))) const Bits;
+  const BT *Bp = (const BT *)(a.Bm) + b * L * N;
+  const BT *Cp = (const BT *)(a.Cm) + b * L * N;
+  auto bc_f32 = [](Bits v) -> float {
+    if constexpr (sizeof(T) == 2) return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    else return v;
+  };
+  const T *xp = static_cast<const T *>(a.x) + b * L * D + d;
+  const T *dp = static_cast<const T *>(a.delta) + b * L * D + d;
+  const T *zp = a.z ? static_cast<const T *>(a.z) + b * L * D + d : nullptr;
+  T *yp = static_cast<T *>(a.y) + b * L * D + d;
+  const float Dd = a.D_skip ? a.D_skip[d] : 0.f;
+  for (int64_t t = 0; t < L; ++t) {
+    const float dl = to_f32(dp[t * D]);
+    const float xv = to_f32(xp[t * D]);
+    const float u = dl * xv;
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      if (EXACT || n < N) {
+        const float dA = fast_exp2(dl * A2[n]);
+        h[n] = fmaf(dA, h[n], u * bc_f32(Bp[t * N + n]));
+        if (n & 1)
+          acc1 = fmaf(bc_f32(Cp[t * N + n]), h[n], acc1);
+        else
+          acc0 = fmaf(bc_f32(Cp[t * N + n]), h[n], acc0);
+      }
+    }
+    float v = fmaf(Dd, xv, acc0 + acc1);
+    if (zp) v *= silu(to_f32(zp[t * D]));
+    if (active) yp[t * D] = from_f32<T>(v);
+  }
+  if (!active || a.h_final == nullptr) return;
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+    if (EXACT || n < N) a.h_final[(b * D + d) * N + n] = h[n];
 }
 
-template <typename T, int NB, bool EXACT>
-struct FullRunner {
-  static hipError_t run(const ScanArgs &a, hipStream_t s) { return launch_full_t<T, NB, EXACT>(a, s); }
-};
-template <typename T, int NB, bool EXACT>
-struct ChunkRunner {
-  static hipError_t run(const ScanArgs &a, int64_t seg_len, float *ws, hipStream_t s) {
-    return launch_chunked_t<T, NB, EXACT>(a, seg_len, ws, s);
-  }
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct SplitCfg {
+  int spl, w;
 };
 
 }  // namespace
 
-hipError_t launch_scan_sequential(const ScanArgs &a, hipStream_t s) {
-  if (a.dt == DType::BF16) return dispatch_n<bf16_t, FullRunner>(a.N, a, s);
-  return dispatch_n<float, FullRunner>(a.N, a, s);
+// States per lane and waves per workgroup for a given N (tuning may force spl).
+static SplitCfg split_cfg(int64_t N, int spl_req) {
+  if (spl_req == 2 || spl_req == 4 || spl_req == 8 || spl_req == 16) {
+    int w = static_cast<int>((N + spl_req - 1) / spl_req);
+    if (w < 1) w = 1;
+    if (w <= 8 && (w == 1 || w == 2 || w == 4 || w == 8)) return {spl_req, w};
+  }
+  if (N <= 4) return {4, 1};
+  if (N <= 8) return {4, 2};
+  if (N <= 16) return {4, 4};
+  if (N <= 32) return {8, 4};
+  return {16, 4};
+}
+
+int64_t scan_pack_floats(int64_t B, int64_t L, int64_t N, int spl_req) {
+  const SplitCfg c = split_cfg(N, spl_req);
+  const int G = c.spl >= 8 ? 1 : 8 / c.spl;
+  const int64_t Lg = (L + G - 1) / G;
+  return B * Lg * G * c.w * 2 * c.spl;
+}
+
+namespace {
+
+template <typename T, int SPL, int W>
+hipError_t launch_split_t(const ScanArgs &a, int64_t seg_len, float *bc, float *seg_a,
+                          float *seg_h, hipStream_t s) {
+  constexpr int G = BCGroup<SPL>::G;
+  const int64_t tot = a.B * ((a.L + G - 1) / G) * G * W * 2 * SPL;
+  if (tot > 0)
+    pack_bc_kernel<T><<<static_cast<unsigned>((tot + 255) / 256), 256, 0, s>>>(
+        static_cast<const T *>(a.Bm), static_cast<const T *>(a.Cm), bc, a.B, a.L,
+        static_cast<int>(a.N), W, SPL, G);
+  const unsigned tiles = static_cast<unsigned>((a.D + kWave - 1) / kWave);
+  if (seg_a == nullptr) {
+    dim3 grid(tiles, 1, static_cast<unsigned>(a.B));
+    scan_split_kernel<T, SPL, W, kFull><<<grid, kWave * W, 0, s>>>(a, bc, a.L, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  const int64_t nseg = (a.L + seg_len - 1) / seg_len;
+  dim3 grid(tiles, static_cast<unsigned>(nseg), static_cast<unsigned>(a.B));
+  scan_split_kernel<T, SPL, W, kSummary><<<grid, kWave * W, 0, s>>>(a, bc, seg_len, seg_a, seg_h);
+  const int64_t total = a.B * a.D * a.N;
+  scan_carry_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, s>>>(
+      a.B, a.D, a.N, nseg, a.h0, seg_a, seg_h, a.h_final);
+  scan_split_kernel<T, SPL, W, kOutput><<<grid, kWave * W, 0, s>>>(a, bc, seg_len, seg_a, seg_h);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_split(const ScanArgs &a, int spl_req, int64_t seg_len, float *bc,
+                          float *seg_a, float *seg_h, hipStream_t s) {
+  const SplitCfg c = split_cfg(a.N, spl_req);
+#define SSM_CASE(S, Wv)              \
+  if (c.spl == S && c.w == Wv)       \
+    return launch_split_t<T, S, Wv>(a, seg_len, bc, seg_a, seg_h, s);
+  SSM_CASE(4, 1) SSM_CASE(4, 2) SSM_CASE(4, 4) SSM_CASE(8, 4) SSM_CASE(16, 4)
+  SSM_CASE(2, 8) SSM_CASE(2, 4) SSM_CASE(2, 2) SSM_CASE(2, 1)
+  SSM_CASE(8, 1) SSM_CASE(8, 2) SSM_CASE(8, 8) SSM_CASE(16, 1) SSM_CASE(16, 2)
+  SSM_CASE(4, 8)
+#undef SSM_CASE
+  return hipErrorNotSupported;
+}
+
+template <typename T, int NB, bool EXACT>
+hipError_t launch_lane_t(const ScanArgs &a, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>((a.D + kWave - 1) / kWave), 1, static_cast<unsigned>(a.B));
+  scan_lane_kernel<T, NB, EXACT><<<grid, kWave, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_lane(const ScanArgs &a, hipStream_t s) {
+  switch (a.N) {
+    case 16: return launch_lane_t<T, 16, true>(a, s);
+    default: break;
+  }
+  if (a.N <= 4) return launch_lane_t<T, 4, false>(a, s);
+  if (a.N <= 8) return launch_lane_t<T, 8, false>(a, s);
+  if (a.N <= 16) return launch_lane_t<T, 16, false>(a, s);
+  if (a.N <= 32) return launch_lane_t<T, 32, false>(a, s);
+  return launch_lane_t<T, 64, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_scan_sequential(const ScanArgs &a, int spl_req, float *bc, hipStream_t s) {
+  if (a.dt == DType::BF16) return dispatch_split<bf16_t>(a, spl_req, 0, bc, nullptr, nullptr, s);
+  return dispatch_split<float>(a, spl_req, 0, bc, nullptr, nullptr, s);
 }
 
 int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg_len) {
@@ -259,9 +471,18 @@ int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64
   return 2 * B * nseg * D * N;
 }
 
-hipError_t launch_scan_chunked(const ScanArgs &a, int64_t seg_len, float *ws, hipStream_t s) {
-  if (a.dt == DType::BF16) return dispatch_n<bf16_t, ChunkRunner>(a.N, a, seg_len, ws, s);
-  return dispatch_n<float, ChunkRunner>(a.N, a, seg_len, ws, s);
+hipError_t launch_scan_chunked(const ScanArgs &a, int spl_req, int64_t seg_len, float *bc,
+                               float *ws, hipStream_t s) {
+  const int64_t nseg = (a.L + seg_len - 1) / seg_len;
+  float *seg_a = ws;
+  float *seg_h = ws + a.B * nseg * a.D * a.N;
+  if (a.dt == DType::BF16) return dispatch_split<bf16_t>(a, spl_req, seg_len, bc, seg_a, seg_h, s);
+  return dispatch_split<float>(a, spl_req, seg_len, bc, seg_a, seg_h, s);
+}
+
+hipError_t launch_scan_lane(const ScanArgs &a, hipStream_t s) {
+  if (a.dt == DType::BF16) return dispatch_lane<bf16_t>(a, s);
+  return dispatch_lane<float>(a, s);
 }
 
 }  // namespace ssm

@@ -7,8 +7,9 @@
 // holding four consecutive states each, so one 16-byte load per lane covers
 // the state tensor contiguously across the wave.  The y contraction over n is
 // finished with a butterfly over those N/4 lanes.  Sizes this layout does not
-// cover (N not a multiple of 4, N > 64) go to the sequential scan with L = 1,
-// whose lanes read and write only their own state row.
+// cover (N not a multiple of 4, or a state/A not 16-byte aligned) go to the
+// per-lane scan kernel with L = 1, whose lanes read and then write only their
+// own state row.
 #include "device_common.h"
 #include "launch.h"
 
@@ -78,8 +79,8 @@ hipError_t launch_dt(const StepArgs &a, hipStream_t st) {
     case 64: return launch_t<T, 16>(a, st);
     default: break;
   }
-  // Other N: the sequential scan over one token, state as both h0 and
-  // h_final (each lane reads its row before writing it).
+  // Other N or unaligned rows: the per-lane scan over one token, the state
+  // as both h0 and h_final (each lane reads its row before writing it).
   ScanArgs sa{};
   sa.B = a.S;
   sa.L = 1;
@@ -96,7 +97,7 @@ hipError_t launch_dt(const StepArgs &a, hipStream_t st) {
   sa.h0 = a.state;
   sa.y = a.y;
   sa.h_final = a.state;
-  return launch_scan_sequential(sa, st);
+  return launch_scan_lane(sa, st);
 }
 
 }  // namespace

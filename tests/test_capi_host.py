@@ -100,16 +100,22 @@ def test_scan_tuning_validation(lib):
 def test_scan_chunked_needs_workspace(lib):
     t = ssm.Tuning(2, 64)
     need = lib.ssm_scan_fwd_workspace_size(2, 1024, 64, 16, ctypes.byref(t))
-    assert need == 2 * 2 * 16 * 64 * 16 * 4
+    pack = 2 * 1024 * 4 * 2 * 4            # B*L rows x 4 waves x (B, C) x 4 states, fp32
+    summaries = 2 * 2 * 16 * 64 * 16       # (a, h) x B x segments x D x N
+    assert need == (pack + summaries) * 4
     assert scan(lib, L=1024, tun=t) == WORKSPACE
     assert scan(lib, L=1024, tun=t, ws=P[12], ws_len=need - 4) == WORKSPACE
     # workspace overlapping an input is rejected too
     assert scan(lib, L=1024, tun=t, ws=P[0], ws_len=need) == INVALID
 
 
-def test_sequential_needs_no_workspace(lib):
+def test_sequential_workspace_is_the_bc_pack(lib):
     t = ssm.Tuning(1, 0)
-    assert lib.ssm_scan_fwd_workspace_size(8, 4096, 5120, 16, ctypes.byref(t)) == 0
+    assert lib.ssm_scan_fwd_workspace_size(8, 4096, 5120, 16, ctypes.byref(t)) == 8 * 4096 * 32 * 4
+    t = ssm.Tuning(1, 0, 16)
+    assert lib.ssm_scan_fwd_workspace_size(8, 4096, 5120, 16, ctypes.byref(t)) == 8 * 4096 * 32 * 4
+    t = ssm.Tuning(1, 0, 3)
+    assert scan(lib, tun=t) == INVALID
 
 
 def step(lib, S=4, D=64, N=16, dt=BF16, **over):

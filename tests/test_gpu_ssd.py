@@ -1,0 +1,108 @@
+"""GPU parity of ssm_ssd_fwd (Mamba-2 SSD chunked scan) against the oracle's
+SSD recurrence on the same seeded inputs (bf16 inputs, fp32 state)."""
+
+import numpy as np
+import pytest
+import torch
+
+import ssm_inputs as gen
+from tests.helpers import assert_close, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def run_gpu(w, gate=None, h0=True, chunk=None):
+    import mamba_selective_scan_ssm_amd as ssm
+    z = w.z if gate is None else (w.z if gate else None)
+    y, hf = ssm.ssd_fwd(to_dev(w.x), to_dev(w.dt), to_dev(w.A), to_dev(w.Bm), to_dev(w.Cm),
+                        to_dev(w.D_skip), to_dev(z) if z is not None else None,
+                        to_dev(w.h0) if (h0 and w.h0 is not None) else None,
+                        chunk=chunk or w.chunk)
+    torch.cuda.synchronize()
+    return to_np(y), to_np(hf)
+
+
+def run_oracle(oracle_mod, w, h0=True, channels=None):
+    return oracle_mod.ssd(w.x.f32, w.dt.f32, w.A, w.Bm.f32, w.Cm.f32, w.D_skip,
+                          w.z.f32 if w.z is not None else None, w.h0 if h0 else None,
+                          channels=channels)
+
+
+@pytest.mark.parametrize("B,L,H,G,N,chunk,gate", [
+    (1, 256, 4, 2, 128, 256, False),     # one full chunk
+    (2, 1000, 4, 1, 128, 256, False),    # ragged last chunk, one group
+    (1, 640, 10, 2, 128, 128, True),     # gate on, chunk 128
+    (1, 300, 3, 3, 64, 64, False),       # chunk 64, N 64, one head per group
+    (1, 333, 2, 1, 32, 128, False),      # N 32
+    (1, 270, 2, 2, 256, 256, False),     # N 256
+    (2, 7, 4, 2, 128, 256, True),        # fewer tokens than a chunk
+])
+def test_ssd_small(oracle_mod, B, L, H, G, N, chunk, gate):
+    w = gen.make_ssd(B, L, H, 64, G, N, chunk=chunk, dtype="bf16", seed=400 + L + N, gate=gate)
+    _say("ssd", B, L, H, G, N, chunk, gate)
+    y, hf = run_gpu(w)
+    ry, rh = run_oracle(oracle_mod, w)
+    assert_close(y, ry, "bf16", "y")
+    assert_close(hf, rh, "bf16", "h_final")
+
+
+def test_ssd_no_h0(oracle_mod):
+    w = gen.make_ssd(1, 512, 4, 64, 2, 128, chunk=256, dtype="bf16", seed=410)
+    _say("ssd no h0")
+    y, hf = run_gpu(w, h0=False)
+    ry, rh = run_oracle(oracle_mod, w, h0=False)
+    assert_close(y, ry, "bf16", "y")
+    assert_close(hf, rh, "bf16", "h_final")
+
+
+def test_ssd_chunk_invariance(oracle_mod):
+    """Chunk lengths 64/128/256 all agree with the (chunk-free) recurrence."""
+    w = gen.make_ssd(1, 768, 4, 64, 2, 128, chunk=256, dtype="bf16", seed=411)
+    ry, rh = run_oracle(oracle_mod, w)
+    for ch in (64, 128, 256):
+        _say("ssd chunk", ch)
+        y, hf = run_gpu(w, chunk=ch)
+        assert_close(y, ry, "bf16", f"y chunk {ch}")
+        assert_close(hf, rh, "bf16", f"h chunk {ch}")
+
+
+def test_ssd_empty_sequence():
+    w = gen.make_ssd(1, 0, 4, 64, 2, 128, chunk=256, dtype="bf16", seed=412)
+    _say("ssd L=0")
+    y, hf = run_gpu(w)
+    assert y.shape == (1, 0, 4, 64)
+    np.testing.assert_array_equal(hf, w.h0.astype(np.float64))
+
+
+def test_ssd_mamba2_full_sampled(oracle_mod):
+    """The full Mamba-2 workload (B=2, L=8192, H=80, P=64, N=128, G=8,
+    chunk 256) in the bench's launch configuration, checked on sampled
+    (b, h, p) channels over the whole sequence, plus their final states."""
+    w = gen.make_workload("ssd_mamba2_bf16")
+    _say("ssd_mamba2_bf16 full size, sampled channels")
+    y, hf = run_gpu(w)
+    B, L, H, P = w.B, w.L, w.H, w.P
+    rng = np.random.default_rng(13)
+    ch = np.unique(np.concatenate([rng.integers(0, B * H * P, 48),
+                                   [0, P - 1, 9 * P, 79 * P + 63, B * H * P - 1]]))
+    ry, rh = run_oracle(oracle_mod, w, channels=ch)
+    p = ch % P
+    h = (ch // P) % H
+    b = ch // (P * H)
+    assert_close(y[b, :, h, p], ry, "bf16", "y")
+    assert_close(hf[b, h, p], rh, "bf16", "h_final")
+
+
+def test_ssd_determinism():
+    import mamba_selective_scan_ssm_amd as ssm
+    w = gen.make_ssd(1, 600, 4, 64, 2, 128, chunk=256, dtype="bf16", seed=413)
+    _say("ssd determinism")
+    args = [to_dev(w.x), to_dev(w.dt), to_dev(w.A), to_dev(w.Bm), to_dev(w.Cm), to_dev(w.D_skip),
+            None, to_dev(w.h0)]
+    a = ssm.ssd_fwd(*args)
+    b = ssm.ssd_fwd(*args)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
