@@ -105,11 +105,13 @@ typedef struct {
  *                  returned).  h_final must not overlap h0 or any input.
  * y must not overlap any input.  Inputs are never modified.
  * workspace      : device scratch of at least ssm_scan_fwd_workspace_size()
- *                  bytes (may be NULL when that size is 0): B/C repacked to
- *                  fp32 per token and wave, plus the segment summaries of the
- *                  chunked schedule.  Contents on entry are ignored; it must
- *                  not overlap any argument.
- * Sizes: B, L, D, N >= 0; N <= SSM_SCAN_MAX_N.  L == 0 writes h_final = h0
+ *                  bytes (may be NULL when that size is 0, which it is for
+ *                  the channel-sequential schedule): the segment summaries
+ *                  of the chunked schedule.  Contents on entry are ignored;
+ *                  it must not overlap any argument.
+ * Sizes: B, L, D, N >= 0; N <= SSM_SCAN_MAX_N; one sequence's x plane
+ * (L + 64) * D * sizeof(dtype) and B/C plane (L + 64) * N * sizeof(dtype)
+ * below 2^31 bytes (else SSM_ERR_UNSUPPORTED).  L == 0 writes h_final = h0
  * (or zeros); B or D == 0 is a no-op; N == 0 leaves y = D_skip x silu(z).
  * Returns SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED,
  * SSM_ERR_WORKSPACE or SSM_ERR_HIP.

@@ -94,23 +94,17 @@ const char *ssm_status_string(ssm_status s) {
 
 int ssm_version(void) { return 100; }  // 0.1.0
 
-// Workspace: the fp32 B/C pack, then (chunked only) the segment summaries.
-int64_t scan_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, const ssm_tuning *t,
-                       int64_t *pack_floats) {
-  *pack_floats = 0;
+// Workspace: the segment summaries of the chunked schedule (none otherwise).
+int64_t scan_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, const ssm_tuning *t) {
   if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
   const Plan p = plan_scan(L, D, t);
-  int64_t pk = ssm::scan_pack_floats(B, L, N, spl_of(t));
-  pk = (pk + 63) / 64 * 64;  // keep the summaries 256-byte aligned
-  *pack_floats = pk;
-  return pk + (p.variant == 2 ? ssm::scan_chunked_ws_floats(B, L, D, N, p.seg_len) : 0);
+  return p.variant == 2 ? ssm::scan_chunked_ws_floats(B, L, D, N, p.seg_len) : 0;
 }
 
 size_t ssm_scan_fwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N,
                                    const ssm_tuning *tuning) {
   if (!tuning_ok(tuning) || N > SSM_SCAN_MAX_N) return 0;
-  int64_t pk;
-  return static_cast<size_t>(scan_ws_floats(B, L, D, N, tuning, &pk)) * sizeof(float);
+  return static_cast<size_t>(scan_ws_floats(B, L, D, N, tuning)) * sizeof(float);
 }
 
 ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt, const void *x,
@@ -124,6 +118,9 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
   if (B == 0 || D == 0) return SSM_OK;
   if (B > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
   const int64_t es = esize(dt);
+  // one sequence's (L, D) and (L, N) planes are addressed with 32-bit offsets
+  if ((L + 64) * D * es >= (int64_t(1) << 31) || (L + 64) * N * es >= (int64_t(1) << 31))
+    return SSM_ERR_UNSUPPORTED;
   const int64_t nBLD = B * L * D, nBLN = B * L * N, nBDN = B * D * N;
   if (L > 0 && (!x || !delta || !y)) return SSM_ERR_INVALID_ARG;
   if (L > 0 && N > 0 && (!Bm || !Cm)) return SSM_ERR_INVALID_ARG;
@@ -142,20 +139,19 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const Plan p = plan_scan(L, D, tuning);
-  if (L == 0 || N == 0) return hip_status(ssm::launch_scan_lane(a, s));  // no B/C to pack
-  if (p.variant == 2 && (L + p.seg_len - 1) / p.seg_len > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
-  int64_t pack = 0;
-  const int64_t need_f = scan_ws_floats(B, L, D, N, tuning, &pack);
-  const size_t need = static_cast<size_t>(need_f) * sizeof(float);
-  if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
-  const Range wsr{workspace, static_cast<int64_t>(need)};
-  if (overlaps_any(wsr, ins) || overlap(wsr, Range{y, nBLD * es}) ||
-      overlap(wsr, Range{h_final, nBDN * 4}))
-    return SSM_ERR_INVALID_ARG;
-  float *ws = static_cast<float *>(workspace);
-  if (p.variant == 2)
-    return hip_status(ssm::launch_scan_chunked(a, spl_of(tuning), p.seg_len, ws, ws + pack, s));
-  return hip_status(ssm::launch_scan_sequential(a, spl_of(tuning), ws, s));
+  if (L == 0 || N == 0) return hip_status(ssm::launch_scan_lane(a, s));
+  if (p.variant == 2) {
+    if ((L + p.seg_len - 1) / p.seg_len > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+    const size_t need = static_cast<size_t>(scan_ws_floats(B, L, D, N, tuning)) * sizeof(float);
+    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+    const Range wsr{workspace, static_cast<int64_t>(need)};
+    if (overlaps_any(wsr, ins) || overlap(wsr, Range{y, nBLD * es}) ||
+        overlap(wsr, Range{h_final, nBDN * 4}))
+      return SSM_ERR_INVALID_ARG;
+    return hip_status(ssm::launch_scan_chunked(a, spl_of(tuning), p.seg_len,
+                                               static_cast<float *>(workspace), s));
+  }
+  return hip_status(ssm::launch_scan_sequential(a, spl_of(tuning), s));
 }
 
 ssm_status ssm_state_update(int64_t S, int64_t D, int64_t N, ssm_dtype dt, float *state,

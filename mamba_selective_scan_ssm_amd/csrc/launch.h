@@ -22,19 +22,16 @@ struct ScanArgs {
   float *h_final;
 };
 
-// fp32 B/C pack used by the split kernels: scan_pack_floats() floats.
-// spl_req = requested states per lane (0 = automatic).
-int64_t scan_pack_floats(int64_t B, int64_t L, int64_t N, int spl_req);
-
 // Channel-sequential scan: a workgroup per (b, 64 channels), its waves
-// splitting N, one pass over the L tokens.  bc: pack buffer.
-hipError_t launch_scan_sequential(const ScanArgs &a, int spl_req, float *bc, hipStream_t s);
+// splitting N, one pass over the L tokens.  spl_req = requested states per
+// lane (0 = automatic).
+hipError_t launch_scan_sequential(const ScanArgs &a, int spl_req, hipStream_t s);
 
 // Chunked scan: segment summaries, carry pass over segments, output pass.
-// ws must hold scan_chunked_ws_floats(...) floats besides the pack buffer.
+// ws must hold scan_chunked_ws_floats(...) floats.
 int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg_len);
-hipError_t launch_scan_chunked(const ScanArgs &a, int spl_req, int64_t seg_len, float *bc,
-                               float *ws, hipStream_t s);
+hipError_t launch_scan_chunked(const ScanArgs &a, int spl_req, int64_t seg_len, float *ws,
+                               hipStream_t s);
 
 // Workspace-free scan, one lane per channel holding all N states.  h0 and
 // h_final may alias (each lane reads its row before writing it).

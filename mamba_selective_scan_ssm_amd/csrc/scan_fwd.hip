@@ -21,9 +21,12 @@
 //  * x/delta/z rows of a block of TB tokens are loaded two blocks ahead,
 //    coalesced over the 64 channels, converted once, and staged in LDS as
 //    delta, u = delta*x, D*x and z (fp32); every wave reads them from there.
-//  * B/C rows are shared by all channels: a pre-pass packs them to fp32 as
-//    [b][t][wave][B(SPL), C(SPL)] so each wave fetches its token's slice with
-//    one scalar load into SGPRs (prefetched a token or two ahead).
+//  * B/C rows are shared by all channels: they are staged in LDS with the
+//    same two-block lead, converted to fp32 and laid out per wave, so each
+//    wave reads its token's SPL B and C values with uniform-address LDS
+//    reads (a broadcast to all 64 lanes).  LDS reads complete in order, so
+//    the compiler can keep them in flight across tokens with partial waits
+//    (scalar loads could only be waited for all at once).
 //  * Each wave's partial y (its states' share of sum_n C h) goes to LDS;
 //    after a barrier per block, every wave finishes 1/W of the block's
 //    tokens: sums the partials, applies the gate and stores y.
@@ -51,7 +54,6 @@ namespace ssm {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kTB = 8;  // tokens per block (LDS stage + barrier granularity)
 
 enum Mode : int { kFull = 0, kSummary = 1, kOutput = 2 };
 
@@ -61,38 +63,39 @@ template <int K>
 using cf32v = __attribute__((address_space(4))) const f32v<K>;
 
 // ---------------------------------------------------------------------------
-// B/C pre-pass: (B, L, N) of T -> fp32 groups of G tokens,
-// [b][t / G][wave][t % G][B(SPL), C(SPL)], zero for t >= L or n >= N, so a
-// wave fetches G tokens of its states' B and C with one 64-byte scalar load.
+// Buffer access to the per-sequence (L, D) planes of x, delta, z and y: the
+// lane offset (d * bytes) is fixed for the whole kernel and the token offset
+// (t * D * bytes) is a scalar, so a load or store costs no VALU address math.
+// Accesses past the plane (never issued here) would return 0.
 // ---------------------------------------------------------------------------
-template <int SPL>
-struct BCGroup {
-  static constexpr int G = SPL >= 8 ? 1 : 8 / SPL;  // tokens per scalar group
-  static constexpr int kFloats = G * 2 * SPL;        // 16 (32 for SPL = 16)
-};
+constexpr int kRsrcWord3 = 0x00020000;
 
 template <typename T>
-__global__ __launch_bounds__(256) void pack_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm,
-                                                      float *__restrict__ bc, int64_t B, int64_t L,
-                                                      int N, int W, int SPL, int G) {
-  const int64_t Lg = (L + G - 1) / G;
-  const int64_t per_grp = static_cast<int64_t>(W) * G * 2 * SPL;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= B * Lg * per_grp) return;
-  const int64_t bg = i / per_grp;  // b * Lg + t / G
-  int rem = static_cast<int>(i - bg * per_grp);
-  const int w = rem / (G * 2 * SPL);
-  rem -= w * G * 2 * SPL;
-  const int jj = rem / (2 * SPL), k = rem % (2 * SPL);
-  const int64_t b = bg / Lg, t = (bg % Lg) * G + jj;
-  const int n = w * SPL + (k % SPL);
-  float v = 0.f;
-  if (t < L && n < N) v = to_f32((k < SPL ? Bm : Cm)[(b * L + t) * N + n]);
-  bc[i] = v;
-}
-
-// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt left at their maxima).
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+struct Plane {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ Plane(const void *base, int64_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                            static_cast<int>(bytes > 0x7fffffff ? 0x7fffffff : bytes),
+                                            kRsrcWord3)) {}
+  __device__ __forceinline__ T load(uint32_t voff, uint32_t soff) const {
+    if constexpr (sizeof(T) == 2) {
+      bf16_t v;
+      v.bits = __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+      return v;
+    } else {
+      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff),
+                                                                  static_cast<int>(soff), 0));
+    }
+  }
+  __device__ __forceinline__ void store(T v, uint32_t voff, uint32_t soff) const {
+    if constexpr (sizeof(T) == 2) {
+      __builtin_amdgcn_raw_buffer_store_b16(v.bits, r, static_cast<int>(voff), static_cast<int>(soff), 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(voff),
+                                            static_cast<int>(soff), 0);
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Split kernel.  Grid: x = 64-channel tile, y = segment, z = sequence b.
@@ -101,40 +104,40 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 //             seg_h[n] = state reached, per (b, seg, d, n).
 //   kOutput:  h starts at seg_h (the state entering the segment, written by
 //             the carry pass); writes y.
-// Segment lengths are multiples of kTB.  Tokens past the end of the last
+// Segment lengths are multiples of TB.  Tokens past the end of the last
 // block are staged with delta = u = 0, for which dA = 1 and the update adds
 // 0, so the state passes through them unchanged and no per-token branch is
 // needed.
 // ---------------------------------------------------------------------------
-template <typename T, int SPL, int W, int MODE>
-__global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, const float *bc,
-                                                              int64_t seg_len, float *seg_a,
-                                                              float *seg_h) {
+template <typename T, int SPL, int W, int TB, int MODE, bool HAS_Z>
+__global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_t seg_len,
+                                                              float *seg_a, float *seg_h) {
   constexpr bool kY = MODE != kSummary;
-  constexpr int kTokPerThread = kTB / W;  // tokens each thread stages per block
-  static_assert(kTB % W == 0, "W must divide the block length");
-  constexpr int G = BCGroup<SPL>::G;
-  constexpr int kGB = kTB / G;  // scalar groups per block (even)
-  static_assert(kGB % 2 == 0, "groups per block must be even for the static ring");
-  using GV = f32v<BCGroup<SPL>::kFloats>;
+  constexpr int kNP = SPL * W;             // padded N
+  constexpr int kTokPerThread = TB / W;    // x/delta/z tokens each thread stages per block
+  static_assert(TB % W == 0, "W must divide the block length");
+  constexpr int kBC = TB * 2 * kNP;        // B/C values per block
+  constexpr int kBCPerThread = (kBC + kWave * W - 1) / (kWave * W);
+  constexpr uint32_t kES = sizeof(T);
 
-  __shared__ float s_dl[2][kTB][kWave];
-  __shared__ float s_u[2][kTB][kWave];
-  __shared__ float s_dx[3][kTB][kWave];  // D[d] * x
-  __shared__ float s_z[3][kTB][kWave];
-  __shared__ float s_y[2][W][kTB][kWave];
+  __shared__ float2 s_du[2][TB][kWave];  // (delta, u = delta * x)
+  __shared__ __attribute__((aligned(16))) float s_bc[2][TB][W][2][SPL];  // B, C per wave
+  __shared__ float s_dx[3][TB][kWave];   // D[d] * x
+  __shared__ float s_z[3][TB][kWave];
+  __shared__ float s_y[2][W][TB][kWave];
 
   const int64_t D = a.D, L = a.L;
   const int N = static_cast<int>(a.N);
-  const int lane = threadIdx.x % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kWave + lane;
   const bool active = d_raw < D;
   const int64_t d = active ? d_raw : D - 1;
   const int64_t seg = blockIdx.y, nseg = gridDim.y, b = blockIdx.z;
   const int64_t t0 = seg * seg_len;
   const int64_t t1 = (t0 + seg_len < L) ? t0 + seg_len : L;
-  const int64_t nblk = (t1 - t0 + kTB - 1) / kTB;
+  const int64_t nblk = (t1 - t0 + TB - 1) / TB;
   const int n0 = wave * SPL;
 
   float A2[SPL], h[SPL];
@@ -150,119 +153,145 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, const 
     h[s] = v;
   }
 
-  const T *xp = static_cast<const T *>(a.x) + b * L * D + d;
-  const T *dp = static_cast<const T *>(a.delta) + b * L * D + d;
-  const T *zp = (kY && a.z) ? static_cast<const T *>(a.z) + b * L * D + d : nullptr;
-  T *yp = static_cast<T *>(a.y) + b * L * D + d;
+  const int64_t plane = L * D * kES;  // bytes of one sequence's (L, D) plane
+  const Plane<T> px(static_cast<const char *>(a.x) + b * plane, plane);
+  const Plane<T> pd(static_cast<const char *>(a.delta) + b * plane, plane);
+  constexpr bool has_z = kY && HAS_Z;
+  const Plane<T> pz(has_z ? static_cast<const char *>(a.z) + b * plane : static_cast<const char *>(a.x),
+                    plane);
+  const Plane<T> py(static_cast<char *>(a.y) + b * plane, plane);
+  const uint32_t voff = static_cast<uint32_t>(d * kES);
+  const uint32_t row_bytes = static_cast<uint32_t>(D * kES);
+  const int64_t bcplane = L * N * kES;
+  const Plane<T> pb(static_cast<const char *>(a.Bm) + b * bcplane, bcplane);
+  const Plane<T> pc(static_cast<const char *>(a.Cm) + b * bcplane, bcplane);
   const float Dd = (a.D_skip != nullptr) ? a.D_skip[d] : 0.f;
-  const bool has_z = zp != nullptr;
-  const int64_t Lg = (L + G - 1) / G;
-  const cf32v<BCGroup<SPL>::kFloats> *bcp =
-      (const cf32v<BCGroup<SPL>::kFloats> *)(bc) + (b * Lg) * W + wave;
-  const int64_t g_last = Lg - 1;  // clamp for prefetches past the end
 
-  // raw x/delta/z of two blocks in flight
-  T rx[2][kTokPerThread], rd[2][kTokPerThread], rz[2][kTokPerThread];
+  // This thread's share of a block's B/C values: entry e = tid + i*64W of
+  // [which][token j][n] (n padded to kNP), read from (b, t, n) of B or C.
+  uint32_t bc_vo[kBCPerThread];
+  int bc_j[kBCPerThread], bc_n[kBCPerThread], bc_w[kBCPerThread];
+  bool bc_on[kBCPerThread];
+#pragma unroll
+  for (int i = 0; i < kBCPerThread; ++i) {
+    const int e = tid + i * kWave * W;
+    bc_on[i] = e < kBC;
+    const int ee = bc_on[i] ? e : 0;
+    bc_w[i] = ee / (TB * kNP);
+    bc_j[i] = (ee / kNP) % TB;
+    bc_n[i] = ee % kNP;
+    const int n = bc_n[i] < N ? bc_n[i] : N - 1;
+    bc_vo[i] = static_cast<uint32_t>((bc_j[i] * N + n) * kES);
+  }
+  const uint32_t tok0 = static_cast<uint32_t>(t0);        // first token of the segment
+  const uint32_t ntok = static_cast<uint32_t>(t1 - t0);   // tokens in the segment
 
-  auto issue = [&](int set, int64_t blk) {
+  // raw inputs of two blocks in flight.  Loads run past the segment end at
+  // most into the next segment or past the plane (which reads 0); stage()
+  // zeroes delta and u there.
+  struct RawBlock {
+    T x[kTokPerThread], d[kTokPerThread], z[kTokPerThread], bc[kBCPerThread];
+  };
+  RawBlock raw0, raw1;
+
+  auto issue = [&](RawBlock &r, int64_t blk) {
+    const uint32_t tb = tok0 + static_cast<uint32_t>(blk) * TB;
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i) {
-      int64_t t = t0 + blk * kTB + wave + i * W;
-      t = t < t1 ? t : t1 - 1;
-      rx[set][i] = xp[t * D];
-      rd[set][i] = dp[t * D];
-      if (has_z) rz[set][i] = zp[t * D];
+      const uint32_t so = (tb + wave + i * W) * row_bytes;
+      r.x[i] = px.load(voff, so);
+      r.d[i] = pd.load(voff, so);
+      if (has_z) r.z[i] = pz.load(voff, so);
+    }
+    const uint32_t bso = tb * static_cast<uint32_t>(N) * kES;
+#pragma unroll
+    for (int i = 0; i < kBCPerThread; ++i) {
+      const T vb = pb.load(bc_vo[i], bso);
+      const T vc = pc.load(bc_vo[i], bso);
+      r.bc[i] = bc_w[i] ? vc : vb;
     }
   };
-  auto stage = [&](int set, int64_t blk) {
+  auto stage = [&](const RawBlock &r, int64_t blk) {
     const int b2 = static_cast<int>(blk & 1), b3 = static_cast<int>(blk % 3);
+    const uint32_t jb = static_cast<uint32_t>(blk) * TB;  // block start within the segment
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i) {
       const int j = wave + i * W;
-      const bool ok = t0 + blk * kTB + j < t1;
-      const float dl = ok ? to_f32(rd[set][i]) : 0.f;
-      const float xv = ok ? to_f32(rx[set][i]) : 0.f;
-      s_dl[b2][j][lane] = dl;
-      s_u[b2][j][lane] = dl * xv;
+      const bool ok = jb + j < ntok;
+      const float dl = ok ? to_f32(r.d[i]) : 0.f;
+      const float xv = ok ? to_f32(r.x[i]) : 0.f;
+      s_du[b2][j][lane] = make_float2(dl, dl * xv);
       if (kY) {
         s_dx[b3][j][lane] = Dd * xv;
-        if (has_z) s_z[b3][j][lane] = to_f32(rz[set][i]);
+        if (has_z) s_z[b3][j][lane] = to_f32(r.z[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBCPerThread; ++i) {
+      if (bc_on[i]) {
+        const int n = bc_n[i];
+        s_bc[b2][bc_j[i]][n / SPL][bc_w[i]][n % SPL] = n < N ? to_f32(r.bc[i]) : 0.f;
       }
     }
   };
 
   float dsum = 0.f;
-  GV ring[2];
-  ring[0] = bcp[(t0 / G < g_last ? t0 / G : g_last) * W];
-
-  // recurrence over the kTB tokens of block blk
+  // recurrence over the TB tokens of block blk
   auto run_block = [&](int64_t blk) {
     const int b2 = static_cast<int>(blk & 1);
-    const int64_t g0 = (t0 + blk * kTB) / G;
 #pragma unroll
-    for (int q = 0; q < kGB; ++q) {
-      float dl[G], u[G];
-      wait_lgkm0();  // group q's B/C (issued a group ago) and earlier LDS ops
+    for (int j = 0; j < TB; ++j) {
+      const float2 du = s_du[b2][j][lane];
+      float Bv[SPL], Cv[SPL];
 #pragma unroll
-      for (int jj = 0; jj < G; ++jj) {
-        dl[jj] = s_dl[b2][q * G + jj][lane];
-        u[jj] = s_u[b2][q * G + jj][lane];
+      for (int s = 0; s < SPL; ++s) {
+        Bv[s] = s_bc[b2][j][wave][0][s];
+        Cv[s] = s_bc[b2][j][wave][1][s];
       }
-      wait_lgkm0();  // the LDS reads, so no later wait has to cover a scalar load
-      {
-        int64_t gn = g0 + q + 1;
-        gn = gn < g_last ? gn : g_last;
-        ring[(q + 1) & 1] = bcp[gn * W];
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-      const GV cur = ring[q & 1];
+      float acc = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < G; ++jj) {
-        float acc = 0.f;
-#pragma unroll
-        for (int s = 0; s < SPL; ++s) {
-          const float dA = fast_exp2(dl[jj] * A2[s]);
-          h[s] = fmaf(dA, h[s], u[jj] * cur[jj * 2 * SPL + s]);
-          if (kY) acc = fmaf(cur[jj * 2 * SPL + SPL + s], h[s], acc);
-        }
-        if (kY) s_y[b2][wave][q * G + jj][lane] = acc;
-        if (MODE == kSummary) dsum += dl[jj];
+      for (int s = 0; s < SPL; ++s) {
+        const float dA = fast_exp2(du.x * A2[s]);
+        h[s] = fmaf(dA, h[s], du.y * Bv[s]);
+        if (kY) acc = fmaf(Cv[s], h[s], acc);
       }
+      if (kY) s_y[b2][wave][j][lane] = acc;
+      if (MODE == kSummary) dsum += du.x;
     }
   };
   auto reduce_block = [&](int64_t blk) {
     const int b2 = static_cast<int>(blk & 1), b3 = static_cast<int>(blk % 3);
-    const int64_t tb = t0 + blk * kTB;
+    const uint32_t jb = static_cast<uint32_t>(blk) * TB;
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i) {
       const int j = wave * kTokPerThread + i;
-      const int64_t t = tb + j;
+      const uint32_t jj = jb + j;
       float v = s_y[b2][0][j][lane];
 #pragma unroll
       for (int w = 1; w < W; ++w) v += s_y[b2][w][j][lane];
       v += s_dx[b3][j][lane];
       if (has_z) v *= silu(s_z[b3][j][lane]);
-      if (t < t1 && active) yp[t * D] = from_f32<T>(v);
+      if (jj < ntok && active) py.store(from_f32<T>(v), voff, (tok0 + jj) * row_bytes);
     }
   };
 
   if (nblk > 0) {
-    issue(0, 0);
-    issue(1, 1);
-    stage(0, 0);
+    issue(raw0, 0);
+    issue(raw1, 1);
+    stage(raw0, 0);
     __syncthreads();
   }
   for (int64_t k = 0; k < nblk; k += 2) {
-    // raw set 0 holds block k (already staged), set 1 holds block k+1
-    issue(0, k + 2);
+    // raw0 holds block k (already staged), raw1 holds block k+1
+    issue(raw0, k + 2);
     run_block(k);
-    stage(1, k + 1);
+    stage(raw1, k + 1);
     __syncthreads();
     if (kY) reduce_block(k);
     if (k + 1 >= nblk) break;
-    issue(1, k + 3);
+    issue(raw1, k + 3);
     run_block(k + 1);
-    stage(0, k + 2);
+    stage(raw0, k + 2);
     __syncthreads();
     if (kY) reduce_block(k + 1);
   }
@@ -374,6 +403,12 @@ struct SplitCfg {
   int spl, w;
 };
 
+// tokens per LDS stage / barrier (segment lengths are multiples of it)
+#ifndef SSM_SCAN_BLOCK_TOKENS
+#define SSM_SCAN_BLOCK_TOKENS 8
+#endif
+constexpr int kBlockTokens = SSM_SCAN_BLOCK_TOKENS;
+
 }  // namespace
 
 // States per lane and waves per workgroup for a given N (tuning may force spl).
@@ -390,47 +425,41 @@ static SplitCfg split_cfg(int64_t N, int spl_req) {
   return {16, 4};
 }
 
-int64_t scan_pack_floats(int64_t B, int64_t L, int64_t N, int spl_req) {
-  const SplitCfg c = split_cfg(N, spl_req);
-  const int G = c.spl >= 8 ? 1 : 8 / c.spl;
-  const int64_t Lg = (L + G - 1) / G;
-  return B * Lg * G * c.w * 2 * c.spl;
-}
-
 namespace {
 
 template <typename T, int SPL, int W>
-hipError_t launch_split_t(const ScanArgs &a, int64_t seg_len, float *bc, float *seg_a,
-                          float *seg_h, hipStream_t s) {
-  constexpr int G = BCGroup<SPL>::G;
-  const int64_t tot = a.B * ((a.L + G - 1) / G) * G * W * 2 * SPL;
-  if (tot > 0)
-    pack_bc_kernel<T><<<static_cast<unsigned>((tot + 255) / 256), 256, 0, s>>>(
-        static_cast<const T *>(a.Bm), static_cast<const T *>(a.Cm), bc, a.B, a.L,
-        static_cast<int>(a.N), W, SPL, G);
+hipError_t launch_split_t(const ScanArgs &a, int64_t seg_len, float *seg_a, float *seg_h,
+                          hipStream_t s) {
+  constexpr int TB = kBlockTokens;
   const unsigned tiles = static_cast<unsigned>((a.D + kWave - 1) / kWave);
   if (seg_a == nullptr) {
     dim3 grid(tiles, 1, static_cast<unsigned>(a.B));
-    scan_split_kernel<T, SPL, W, kFull><<<grid, kWave * W, 0, s>>>(a, bc, a.L, nullptr, nullptr);
+    if (a.z)
+      scan_split_kernel<T, SPL, W, TB, kFull, true><<<grid, kWave * W, 0, s>>>(a, a.L, nullptr, nullptr);
+    else
+      scan_split_kernel<T, SPL, W, TB, kFull, false><<<grid, kWave * W, 0, s>>>(a, a.L, nullptr, nullptr);
     return hipGetLastError();
   }
   const int64_t nseg = (a.L + seg_len - 1) / seg_len;
   dim3 grid(tiles, static_cast<unsigned>(nseg), static_cast<unsigned>(a.B));
-  scan_split_kernel<T, SPL, W, kSummary><<<grid, kWave * W, 0, s>>>(a, bc, seg_len, seg_a, seg_h);
+  scan_split_kernel<T, SPL, W, TB, kSummary, false><<<grid, kWave * W, 0, s>>>(a, seg_len, seg_a, seg_h);
   const int64_t total = a.B * a.D * a.N;
   scan_carry_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, s>>>(
       a.B, a.D, a.N, nseg, a.h0, seg_a, seg_h, a.h_final);
-  scan_split_kernel<T, SPL, W, kOutput><<<grid, kWave * W, 0, s>>>(a, bc, seg_len, seg_a, seg_h);
+  if (a.z)
+    scan_split_kernel<T, SPL, W, TB, kOutput, true><<<grid, kWave * W, 0, s>>>(a, seg_len, seg_a, seg_h);
+  else
+    scan_split_kernel<T, SPL, W, TB, kOutput, false><<<grid, kWave * W, 0, s>>>(a, seg_len, seg_a, seg_h);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch_split(const ScanArgs &a, int spl_req, int64_t seg_len, float *bc,
-                          float *seg_a, float *seg_h, hipStream_t s) {
+hipError_t dispatch_split(const ScanArgs &a, int spl_req, int64_t seg_len, float *seg_a,
+                          float *seg_h, hipStream_t s) {
   const SplitCfg c = split_cfg(a.N, spl_req);
-#define SSM_CASE(S, Wv)              \
-  if (c.spl == S && c.w == Wv)       \
-    return launch_split_t<T, S, Wv>(a, seg_len, bc, seg_a, seg_h, s);
+#define SSM_CASE(S, Wv)        \
+  if (c.spl == S && c.w == Wv) \
+    return launch_split_t<T, S, Wv>(a, seg_len, seg_a, seg_h, s);
   SSM_CASE(4, 1) SSM_CASE(4, 2) SSM_CASE(4, 4) SSM_CASE(8, 4) SSM_CASE(16, 4)
   SSM_CASE(2, 8) SSM_CASE(2, 4) SSM_CASE(2, 2) SSM_CASE(2, 1)
   SSM_CASE(8, 1) SSM_CASE(8, 2) SSM_CASE(8, 8) SSM_CASE(16, 1) SSM_CASE(16, 2)
@@ -461,9 +490,9 @@ hipError_t dispatch_lane(const ScanArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_scan_sequential(const ScanArgs &a, int spl_req, float *bc, hipStream_t s) {
-  if (a.dt == DType::BF16) return dispatch_split<bf16_t>(a, spl_req, 0, bc, nullptr, nullptr, s);
-  return dispatch_split<float>(a, spl_req, 0, bc, nullptr, nullptr, s);
+hipError_t launch_scan_sequential(const ScanArgs &a, int spl_req, hipStream_t s) {
+  if (a.dt == DType::BF16) return dispatch_split<bf16_t>(a, spl_req, 0, nullptr, nullptr, s);
+  return dispatch_split<float>(a, spl_req, 0, nullptr, nullptr, s);
 }
 
 int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg_len) {
@@ -471,13 +500,13 @@ int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64
   return 2 * B * nseg * D * N;
 }
 
-hipError_t launch_scan_chunked(const ScanArgs &a, int spl_req, int64_t seg_len, float *bc,
-                               float *ws, hipStream_t s) {
+hipError_t launch_scan_chunked(const ScanArgs &a, int spl_req, int64_t seg_len, float *ws,
+                               hipStream_t s) {
   const int64_t nseg = (a.L + seg_len - 1) / seg_len;
   float *seg_a = ws;
   float *seg_h = ws + a.B * nseg * a.D * a.N;
-  if (a.dt == DType::BF16) return dispatch_split<bf16_t>(a, spl_req, seg_len, bc, seg_a, seg_h, s);
-  return dispatch_split<float>(a, spl_req, seg_len, bc, seg_a, seg_h, s);
+  if (a.dt == DType::BF16) return dispatch_split<bf16_t>(a, spl_req, seg_len, seg_a, seg_h, s);
+  return dispatch_split<float>(a, spl_req, seg_len, seg_a, seg_h, s);
 }
 
 hipError_t launch_scan_lane(const ScanArgs &a, hipStream_t s) {

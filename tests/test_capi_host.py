@@ -69,6 +69,7 @@ def test_scan_rejects_negative_sizes(lib):
 def test_scan_rejects_large_n_and_bad_dtype(lib):
     assert scan(lib, N=65) == UNSUPPORTED
     assert scan(lib, dt=7) == INVALID
+    assert scan(lib, B=1, L=1 << 20, D=1024, dt=BF16) == UNSUPPORTED   # 2 GiB plane
 
 
 def test_scan_rejects_null_required(lib):
@@ -100,20 +101,18 @@ def test_scan_tuning_validation(lib):
 def test_scan_chunked_needs_workspace(lib):
     t = ssm.Tuning(2, 64)
     need = lib.ssm_scan_fwd_workspace_size(2, 1024, 64, 16, ctypes.byref(t))
-    pack = 2 * 1024 * 4 * 2 * 4            # B*L rows x 4 waves x (B, C) x 4 states, fp32
-    summaries = 2 * 2 * 16 * 64 * 16       # (a, h) x B x segments x D x N
-    assert need == (pack + summaries) * 4
+    summaries = 2 * 2 * 16 * 64 * 16       # (a, h) x B x segments x D x N, fp32
+    assert need == summaries * 4
     assert scan(lib, L=1024, tun=t) == WORKSPACE
     assert scan(lib, L=1024, tun=t, ws=P[12], ws_len=need - 4) == WORKSPACE
     # workspace overlapping an input is rejected too
     assert scan(lib, L=1024, tun=t, ws=P[0], ws_len=need) == INVALID
 
 
-def test_sequential_workspace_is_the_bc_pack(lib):
-    t = ssm.Tuning(1, 0)
-    assert lib.ssm_scan_fwd_workspace_size(8, 4096, 5120, 16, ctypes.byref(t)) == 8 * 4096 * 32 * 4
-    t = ssm.Tuning(1, 0, 16)
-    assert lib.ssm_scan_fwd_workspace_size(8, 4096, 5120, 16, ctypes.byref(t)) == 8 * 4096 * 32 * 4
+def test_sequential_needs_no_workspace(lib):
+    for spl in (0, 2, 4, 8, 16):
+        t = ssm.Tuning(1, 0, spl)
+        assert lib.ssm_scan_fwd_workspace_size(8, 4096, 5120, 16, ctypes.byref(t)) == 0
     t = ssm.Tuning(1, 0, 3)
     assert scan(lib, tun=t) == INVALID
 
