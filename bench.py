@@ -183,7 +183,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true", help="skip the decode and SSD rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--cpu-seqs", type=int, default=8)
+    ap.add_argument("--only", choices=["scan", "decode", "ssd"], default=None,
+                    help="time one hot-path entry point only (for profiling); prints its row")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) so a "
+                         "counter run can scale FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -194,6 +199,19 @@ def main():
 
     import mamba_selective_scan_ssm_amd as ssm
     import ssm_inputs as gen
+
+    if args.copy_calib:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)   # elementwise copy kernel: 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        del src, dst
+    if args.only == "decode":
+        print(json.dumps({"decode": bench_decode(torch, ssm, gen)}))
+        return
+    if args.only == "ssd":
+        print(json.dumps({"ssd": bench_ssd(torch, ssm, gen, steps=args.steps)}))
+        return
 
     name = "mamba2p8b_prefill_bf16"
     inp = gen.make_workload(name)
@@ -243,9 +261,9 @@ def main():
         "hbm_GBs": hbm_gbs, "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
         "roofline": roofline,
     }
-    if not args.no_rows:
+    if not args.no_rows and args.only is None:
         out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen)}
-    if not args.no_cpu:
+    if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
     print(json.dumps(out))
 
