@@ -63,14 +63,21 @@ typedef enum {
 } ssm_status;
 
 /* Kernel-variant selection for ssm_scan_fwd.  Pass NULL for the defaults.
- * The default choice depends only on (L, D, N) -- never on B or on the
+ * The default schedule depends only on (L, D, N) -- never on B or on the
  * device -- so a sequence gives bitwise the same result whatever batch it
- * is part of.  */
+ * is part of.  (Within the channel-sequential schedule the automatic choice
+ * also looks at the alignment of Bm and Cm; variants 1 and 3 give bitwise
+ * identical results.)  */
 typedef struct {
-    int32_t variant;   /* 0 = automatic; 1 = channel-sequential (a workgroup
-                          per 64-channel tile whose waves split the N states,
-                          one pass over the L tokens); 2 = chunked over L
-                          (segment summaries, carry pass, output pass) */
+    int32_t variant;   /* 0 = automatic; 1 = channel-sequential, a workgroup
+                          per 64-channel tile whose waves split the N states;
+                          2 = chunked over L (segment summaries, carry pass,
+                          output pass); 3 = channel-sequential, the N states
+                          of a channel split over 1, 2 or 4 lanes of one wave
+                          (N in {4, 8, 16, 32, 64} and Bm, Cm 16-byte
+                          aligned, else SSM_ERR_UNSUPPORTED).  Automatic:
+                          variant 3 where it applies, else 1, when L <= 256
+                          or D >= 4096; variant 2 otherwise. */
     int32_t chunk_len; /* variant 2: tokens per segment (multiple of 8,
                           >= 8); 0 = automatic */
     int32_t states_per_lane; /* 0 = automatic; else 2, 4, 8 or 16: each lane

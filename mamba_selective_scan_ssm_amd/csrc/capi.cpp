@@ -40,7 +40,7 @@ bool tuning_ok(const ssm_tuning *t) {
   if (!t) return true;
   for (int i = 0; i < 5; ++i)
     if (t->reserved[i] != 0) return false;
-  if (t->variant < 0 || t->variant > 2) return false;
+  if (t->variant < 0 || t->variant > 3) return false;
   if (t->chunk_len < 0 || (t->chunk_len != 0 && (t->chunk_len < 8 || t->chunk_len % 8 != 0)))
     return false;
   const int s = t->states_per_lane;
@@ -55,7 +55,7 @@ int spl_of(const ssm_tuning *t) { return t ? t->states_per_lane : 0; }
 // brings enough 64-channel waves or L is short; otherwise chunked with
 // segments sized so one sequence yields ~2048 waves.
 struct Plan {
-  int variant;  // 1 sequential, 2 chunked
+  int variant;  // 1 sequential (waves split N), 2 chunked, 3 sequential (lanes split N)
   int64_t seg_len;
 };
 
@@ -151,6 +151,14 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
     return hip_status(ssm::launch_scan_chunked(a, spl_of(tuning), p.seg_len,
                                                static_cast<float *>(workspace), s));
   }
+  const bool auto_variant = tuning == nullptr || tuning->variant == 0;
+  const bool lanesplit_ok = ssm::scan_lanesplit_supported(a);
+  if (p.variant == 3) {
+    if (!lanesplit_ok) return SSM_ERR_UNSUPPORTED;
+    return hip_status(ssm::launch_scan_lanesplit(a, s));
+  }
+  if (auto_variant && spl_of(tuning) == 0 && lanesplit_ok)
+    return hip_status(ssm::launch_scan_lanesplit(a, s));
   return hip_status(ssm::launch_scan_sequential(a, spl_of(tuning), s));
 }
 

@@ -27,6 +27,13 @@ struct ScanArgs {
 // lane (0 = automatic).
 hipError_t launch_scan_sequential(const ScanArgs &a, int spl_req, hipStream_t s);
 
+// Channel-sequential scan with a channel's N states split over 1, 2 or 4
+// adjacent lanes of one wave (no workgroup barrier).  Supported for N in
+// {4, 8, 16, 32, 64}, even D, 16-byte aligned Bm and Cm, and x, delta, z, y
+// aligned to two elements.
+bool scan_lanesplit_supported(const ScanArgs &a);
+hipError_t launch_scan_lanesplit(const ScanArgs &a, hipStream_t s);
+
 // Chunked scan: segment summaries, carry pass over segments, output pass.
 // ws must hold scan_chunked_ws_floats(...) floats.
 int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg_len);

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_
 
   __shared__ float2 s_du[2][TB][kWave];  // (delta, u = delta * x)
   __shared__ __attribute__((aligned(16))) float s_bc[2][TB][W][2][SPL];  // B, C per wave
-  __shared__ float s_dx[3][TB][kWave];   // D[d] * x
+  __shared__ float s_xv[3][TB][kWave];   // x (for the skip term)
   __shared__ float s_z[3][TB][kWave];
   __shared__ float s_y[2][W][TB][kWave];
 
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_
       const float xv = ok ? to_f32(r.x[i]) : 0.f;
       s_du[b2][j][lane] = make_float2(dl, dl * xv);
       if (kY) {
-        s_dx[b3][j][lane] = Dd * xv;
+        s_xv[b3][j][lane] = xv;
         if (has_z) s_z[b3][j][lane] = to_f32(r.z[i]);
       }
     }
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_
       float v = s_y[b2][0][j][lane];
 #pragma unroll
       for (int w = 1; w < W; ++w) v += s_y[b2][w][j][lane];
-      v += s_dx[b3][j][lane];
+      v = fmaf(Dd, s_xv[b3][j][lane], v);  // skip term D x
       if (has_z) v *= silu(s_z[b3][j][lane]);
       if (jj < ntok && active) py.store(from_f32<T>(v), voff, (tok0 + jj) * row_bytes);
     }
@@ -308,6 +308,323 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Lane-split kernel.  A wave owns kCPW = 64/LPC consecutive channels; the LPC
+// adjacent lanes of a channel hold SPL states each (N = LPC * SPL).  Nothing
+// is shared between waves, so there is no workgroup barrier; each wave works
+// through blocks of TB tokens:
+//  * every lane loads two adjacent channels of one token row of x, delta and
+//    z (one 32-bit load each for bf16), converts them once and writes
+//    (delta, u = delta*x) per (token, channel) to wave-private LDS, from
+//    which the LPC lanes of a channel read them;
+//  * the block's B/C rows (shared by all channels) are loaded by the wave,
+//    converted once and put in wave-private LDS laid out so lane q of a
+//    channel reads its SPL values of B and of C with vector LDS reads;
+//  * each lane writes its partial sum_n C h per token to wave-private LDS;
+//    the lane that loaded a (token, channel pair) adds the LPC partials of
+//    each channel, the skip term and the gate, and stores the pair of y.
+// LDS executes one wave's instructions in order, so a wave's LDS reads see
+// its own earlier LDS writes; fences at wavefront scope keep the compiler
+// from reordering the cross-lane accesses.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// kBytes bytes at byte offset voff + soff of a buffer, as raw 32-bit words.
+template <int kBytes>
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                           uint32_t *w) {
+  const int vo = static_cast<int>(voff), so = static_cast<int>(soff);
+  if constexpr (kBytes == 2) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
+  } else if constexpr (kBytes == 4) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0);
+  } else if constexpr (kBytes == 8) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  } else {
+    static_assert(kBytes % 16 == 0, "unsupported load width");
+#pragma unroll
+    for (int k = 0; k < kBytes / 16; ++k) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, vo + 16 * k, so, 0);
+      w[4 * k] = v[0];
+      w[4 * k + 1] = v[1];
+      w[4 * k + 2] = v[2];
+      w[4 * k + 3] = v[3];
+    }
+  }
+}
+
+// element e of words holding consecutive values of type T, as fp32
+template <typename T>
+__device__ __forceinline__ float word_elem(const uint32_t *w, int e) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t v = w[e / 2];
+    return __uint_as_float((e & 1) ? (v & 0xffff0000u) : (v << 16));
+  } else {
+    return __uint_as_float(w[e]);
+  }
+}
+
+#ifndef SSM_LS_CYCLE
+#define SSM_LS_CYCLE 4
+#endif
+
+template <typename T, int LPC, int SPL, bool HAS_Z>
+__global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
+  constexpr int TB = 8;                 // tokens per block
+  constexpr int kCPW = kWave / LPC;     // channels per wave
+  constexpr int kN = LPC * SPL;         // = N
+  constexpr int kPairs = kCPW / 16;     // (token, channel pair) slots per lane per block
+  constexpr int kPPR = kCPW / 2;        // channel pairs per token row
+  constexpr int kPW = 2 * static_cast<int>(sizeof(T)) / 4;  // words per channel pair
+  constexpr int kV = kN / 4;            // B or C values each lane converts per block
+  constexpr int kWords = (kV * static_cast<int>(sizeof(T)) + 3) / 4;
+  constexpr uint32_t kES = sizeof(T);
+  constexpr int kCyc = SSM_LS_CYCLE;    // blocks per load cycle
+  static_assert(LPC == 1 || LPC == 2 || LPC == 4, "LPC must be 1, 2 or 4");
+  static_assert(SPL % kV == 0, "a loader lane's values must fall in one lane's slice");
+  static_assert(kPairs * 64 * 2 == TB * kCPW, "pair slots must tile the block");
+
+  // per wave and block of the cycle: B/C [token][q][B|C][SPL] and
+  // (delta, u) [token][channel]; per wave: partial sums [token][channel *
+  // LPC + q], rows padded by 4 words so the two rows read by a group of 16
+  // lanes fall in different banks
+  constexpr int kRow = kCPW * LPC + 4;
+  __shared__ __attribute__((aligned(16))) float s_bc[4][kCyc][TB][LPC][2][SPL];
+  __shared__ __attribute__((aligned(16))) float2 s_du[4][kCyc][TB][kCPW];
+  __shared__ __attribute__((aligned(16))) float s_y[4][TB][kRow];
+
+  const int64_t D = a.D, L = a.L;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t d0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * kCPW;  // first channel of the wave
+  const int64_t b = blockIdx.z;
+
+  // compute role: channel c, state slice q
+  const int c = lane / LPC, q = lane % LPC;
+  const int64_t dc = (d0 + c < D) ? d0 + c : D - 1;
+  float A2[SPL], h[SPL];
+  {
+    const float *Ap = a.A + dc * kN + q * SPL;
+    const float *hp = a.h0 ? a.h0 + (b * D + dc) * kN + q * SPL : nullptr;
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) {
+      A2[s] = Ap[s] * kLog2e;
+      h[s] = hp ? hp[s] : 0.f;
+    }
+  }
+
+  // load/finish role: slot m covers token row rr[m] of a block and the
+  // channel pair pp[m] (wave-local channels 2pp, 2pp+1; D is even, so a pair
+  // is either wholly inside D or wholly past it)
+  const int64_t plane = L * D * kES;
+  const uint32_t row_bytes = static_cast<uint32_t>(D * kES);
+  int rr[kPairs], pp[kPairs];
+  uint32_t vo[kPairs], vo_st[kPairs];
+  float Dd[kPairs][2];
+#pragma unroll
+  for (int m = 0; m < kPairs; ++m) {
+    const int e = lane + 64 * m;
+    rr[m] = e / kPPR;
+    pp[m] = e % kPPR;
+    const int64_t dp = d0 + 2 * pp[m];
+    const bool on = dp < D;
+    const int64_t dpc = on ? dp : D - 2;
+    vo[m] = static_cast<uint32_t>(dpc * kES) + static_cast<uint32_t>(rr[m]) * row_bytes;
+    // stores of pairs past D get an offset past the plane (dropped by the
+    // range check); rows past L lie past the plane anyway
+    vo_st[m] = on ? vo[m] : 0x80000000u;
+    Dd[m][0] = a.D_skip ? a.D_skip[dpc] : 0.f;
+    Dd[m][1] = a.D_skip ? a.D_skip[dpc + 1] : 0.f;
+  }
+  auto rsrc = [&](const void *p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(p)), 0,
+                                             static_cast<int>(bytes), kRsrcWord3);
+  };
+  const __amdgpu_buffer_rsrc_t rx = rsrc(static_cast<const char *>(a.x) + b * plane, plane);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(static_cast<const char *>(a.delta) + b * plane, plane);
+  const __amdgpu_buffer_rsrc_t rz =
+      rsrc(HAS_Z ? static_cast<const char *>(a.z) + b * plane : static_cast<const char *>(a.x), plane);
+  const __amdgpu_buffer_rsrc_t ry = rsrc(static_cast<char *>(a.y) + b * plane, plane);
+
+  // B/C: even lanes convert B, odd lanes C (the LDS writes of 16 consecutive
+  // lanes then cover distinct banks); lane l handles the flat elements
+  // [kV*(l/2), kV*(l/2) + kV) of a block's (TB, N) rows
+  const int64_t bcplane = L * kN * kES;
+  const __amdgpu_buffer_rsrc_t rb = rsrc(static_cast<const char *>(a.Bm) + b * bcplane, bcplane);
+  const __amdgpu_buffer_rsrc_t rc = rsrc(static_cast<const char *>(a.Cm) + b * bcplane, bcplane);
+  const int ld = lane / 2;
+  const bool ld_c = lane & 1;
+  const int ld_j = (kV * ld) / kN, ld_n = (kV * ld) % kN;
+  const uint32_t ld_vo = static_cast<uint32_t>(kV * ld) * kES;
+
+  const uint32_t ntok = static_cast<uint32_t>(L);
+  const int64_t nblk = (L + TB - 1) / TB;
+  const int64_t ncyc = (nblk + kCyc - 1) / kCyc;
+
+  // Raw inputs of one cycle of kCyc blocks.  Two sets alternate: while one
+  // cycle is computed, the next one's loads are in flight.
+  struct Raw {
+    uint32_t x[kCyc][kPairs][kPW], d[kCyc][kPairs][kPW], z[kCyc][kPairs][kPW];
+    uint32_t b[kCyc][kWords], c[kCyc][kWords];
+  };
+  // Loads past the end of a plane return 0 (buffer range check), so the
+  // blocks past the last one need no special case.
+  auto issue = [&](Raw &w, int64_t cyc) {
+#pragma unroll
+    for (int u = 0; u < kCyc; ++u) {
+      const uint32_t blk = static_cast<uint32_t>(cyc * kCyc + u);
+      const uint32_t so = __builtin_amdgcn_readfirstlane(blk * TB * row_bytes);
+#pragma unroll
+      for (int m = 0; m < kPairs; ++m) {
+        load_words<2 * kES>(rx, vo[m], so, w.x[u][m]);
+        load_words<2 * kES>(rd, vo[m], so, w.d[u][m]);
+        if (HAS_Z) load_words<2 * kES>(rz, vo[m], so, w.z[u][m]);
+      }
+      // buffer resources must be wave-uniform: every lane loads its slice
+      // of both B and C and converts one of them when the cycle is staged
+      const uint32_t bso = __builtin_amdgcn_readfirstlane(blk * TB * kN * kES);
+      load_words<kV * kES>(rb, ld_vo, bso, w.b[u]);
+      load_words<kV * kES>(rc, ld_vo, bso, w.c[u]);
+    }
+  };
+
+  // convert a cycle's delta, u = delta*x and B/C into LDS; tokens past L get
+  // delta = u = 0, for which dA = 1 and the state passes through unchanged
+  auto stage = [&](const Raw &w, int64_t cyc) {
+#pragma unroll
+    for (int u = 0; u < kCyc; ++u) {
+      const uint32_t tb = static_cast<uint32_t>(cyc * kCyc + u) * TB;
+#pragma unroll
+      for (int m = 0; m < kPairs; ++m) {
+        const bool ok = tb + rr[m] < ntok;
+        float du[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float xv = word_elem<T>(w.x[u][m], hh);
+          const float dv = ok ? word_elem<T>(w.d[u][m], hh) : 0.f;
+          du[2 * hh] = dv;
+          du[2 * hh + 1] = dv * xv;
+        }
+        *reinterpret_cast<float4 *>(&s_du[wave][u][rr[m]][2 * pp[m]]) =
+            make_float4(du[0], du[1], du[2], du[3]);
+      }
+      uint32_t bc[kWords];
+#pragma unroll
+      for (int k = 0; k < kWords; ++k) bc[k] = ld_c ? w.c[u][k] : w.b[u][k];
+      float *dst = &s_bc[wave][u][ld_j][ld_n / SPL][ld_c ? 1 : 0][ld_n % SPL];
+#pragma unroll
+      for (int e = 0; e < kV; ++e) dst[e] = word_elem<T>(bc, e);
+    }
+  };
+
+  auto run_block = [&](int u) {
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const float2 du = s_du[wave][u][j][c];
+      float Bv[SPL], Cv[SPL];
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) {
+        Bv[s] = s_bc[wave][u][j][q][0][s];
+        Cv[s] = s_bc[wave][u][j][q][1][s];
+      }
+      float acc = 0.f;
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) {
+        const float dA = fast_exp2(du.x * A2[s]);
+        h[s] = fmaf(dA, h[s], du.y * Bv[s]);
+        acc = fmaf(Cv[s], h[s], acc);
+      }
+      s_y[wave][j][c * LPC + q] = acc;
+    }
+  };
+
+  // y of the slots of a block, packed as stored
+  uint32_t yv[kCyc][kPairs][kPW];
+  auto finish_block = [&](const Raw &w, int u) {
+#pragma unroll
+    for (int m = 0; m < kPairs; ++m) {
+      float v[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float *py = &s_y[wave][rr[m]][(2 * pp[m] + hh) * LPC];
+        float t = py[0];
+#pragma unroll
+        for (int k = 1; k < LPC; ++k) t += py[k];
+        t = fmaf(Dd[m][hh], word_elem<T>(w.x[u][m], hh), t);  // skip term D x
+        if (HAS_Z) t *= silu(word_elem<T>(w.z[u][m], hh));
+        v[hh] = t;
+      }
+      if constexpr (sizeof(T) == 2) {
+        yv[u][m][0] = static_cast<uint32_t>(from_f32<T>(v[0]).bits) |
+                      (static_cast<uint32_t>(from_f32<T>(v[1]).bits) << 16);
+      } else {
+        yv[u][m][0] = __float_as_uint(v[0]);
+        yv[u][m][1] = __float_as_uint(v[1]);
+      }
+    }
+  };
+  auto store_cycle = [&](int64_t cyc) {
+#pragma unroll
+    for (int u = 0; u < kCyc; ++u) {
+      const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cyc * kCyc + u) * TB * row_bytes);
+#pragma unroll
+      for (int m = 0; m < kPairs; ++m) {
+        const int vov = static_cast<int>(vo_st[m]), sov = static_cast<int>(so);
+        if constexpr (sizeof(T) == 2) {
+          __builtin_amdgcn_raw_buffer_store_b32(yv[u][m][0], ry, vov, sov, 0);
+        } else {
+          using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
+          const u32x2 pv = {yv[u][m][0], yv[u][m][1]};
+          __builtin_amdgcn_raw_buffer_store_b64(pv, ry, vov, sov, 0);
+        }
+      }
+    }
+  };
+
+  // One cycle: stage its inputs (this waits for its loads, issued a cycle
+  // earlier, and for the previous cycle's stores), store the previous
+  // cycle's y, issue the next cycle's loads, then compute.  Loads and stores
+  // share one counter whose waits cannot skip a pending store, so no store is
+  // issued between a load and the wait for it except a whole cycle earlier.
+  auto cycle = [&](Raw &cur, Raw &nxt, int64_t cyc) {
+    stage(cur, cyc);
+    if (cyc > 0) store_cycle(cyc - 1);
+    issue(nxt, cyc + 1);
+    wave_sync_lds();
+#pragma unroll
+    for (int u = 0; u < kCyc; ++u) {
+      run_block(u);
+      wave_sync_lds();
+      finish_block(cur, u);
+      wave_sync_lds();
+    }
+  };
+
+  Raw r0, r1;
+  issue(r0, 0);
+  int64_t cyc = 0;
+  for (; cyc + 1 < ncyc; cyc += 2) {
+    cycle(r0, r1, cyc);
+    cycle(r1, r0, cyc + 1);
+  }
+  if (cyc < ncyc) {
+    cycle(r0, r1, cyc);
+    ++cyc;
+  }
+  if (ncyc > 0) store_cycle(cyc - 1);
+
+  if (d0 + c >= D || a.h_final == nullptr) return;
+  float *hf = a.h_final + (b * D + dc) * kN + q * SPL;
+#pragma unroll
+  for (int s = 0; s < SPL; ++s) hf[s] = h[s];
 }
 
 // Carry pass: one thread per (b, d, n); walks the segments in order,
@@ -468,6 +785,36 @@ hipError_t dispatch_split(const ScanArgs &a, int spl_req, int64_t seg_len, float
   return hipErrorNotSupported;
 }
 
+template <typename T, int LPC, int SPL>
+hipError_t launch_lanesplit_t(const ScanArgs &a, hipStream_t s) {
+  constexpr int kChPerWG = 4 * (kWave / LPC);
+  dim3 grid(static_cast<unsigned>((a.D + kChPerWG - 1) / kChPerWG), 1, static_cast<unsigned>(a.B));
+  if (a.z)
+    scan_lanesplit_kernel<T, LPC, SPL, true><<<grid, kWave * 4, 0, s>>>(a);
+  else
+    scan_lanesplit_kernel<T, LPC, SPL, false><<<grid, kWave * 4, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_lanesplit(const ScanArgs &a, hipStream_t s) {
+  switch (a.N) {
+    case 4: return launch_lanesplit_t<T, 1, 4>(a, s);
+    case 8: return launch_lanesplit_t<T, 2, 4>(a, s);
+    case 16:
+#if defined(SSM_LS_N16_LPC) && SSM_LS_N16_LPC == 2
+      return launch_lanesplit_t<T, 2, 8>(a, s);
+#elif defined(SSM_LS_N16_LPC) && SSM_LS_N16_LPC == 1
+      return launch_lanesplit_t<T, 1, 16>(a, s);
+#else
+      return launch_lanesplit_t<T, 4, 4>(a, s);
+#endif
+    case 32: return launch_lanesplit_t<T, 4, 8>(a, s);
+    case 64: return launch_lanesplit_t<T, 4, 16>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
 template <typename T, int NB, bool EXACT>
 hipError_t launch_lane_t(const ScanArgs &a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((a.D + kWave - 1) / kWave), 1, static_cast<unsigned>(a.B));
@@ -493,6 +840,20 @@ hipError_t dispatch_lane(const ScanArgs &a, hipStream_t s) {
 hipError_t launch_scan_sequential(const ScanArgs &a, int spl_req, hipStream_t s) {
   if (a.dt == DType::BF16) return dispatch_split<bf16_t>(a, spl_req, 0, nullptr, nullptr, s);
   return dispatch_split<float>(a, spl_req, 0, nullptr, nullptr, s);
+}
+
+bool scan_lanesplit_supported(const ScanArgs &a) {
+  const bool n_ok = a.N == 4 || a.N == 8 || a.N == 16 || a.N == 32 || a.N == 64;
+  auto al = [](const void *p, uintptr_t k) { return reinterpret_cast<uintptr_t>(p) % k == 0; };
+  const uintptr_t pair = a.dt == DType::BF16 ? 4 : 8;  // a channel pair is loaded as one word
+  const bool aligned = al(a.Bm, 16) && al(a.Cm, 16) && al(a.x, pair) && al(a.delta, pair) &&
+                       al(a.y, pair) && (a.z == nullptr || al(a.z, pair));
+  return n_ok && aligned && a.D % 2 == 0;
+}
+
+hipError_t launch_scan_lanesplit(const ScanArgs &a, hipStream_t s) {
+  if (a.dt == DType::BF16) return dispatch_lanesplit<bf16_t>(a, s);
+  return dispatch_lanesplit<float>(a, s);
 }
 
 int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg_len) {

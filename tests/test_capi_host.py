@@ -89,7 +89,7 @@ def test_scan_empty_batch_is_noop(lib):
 
 
 def test_scan_tuning_validation(lib):
-    t = ssm.Tuning(3, 0)
+    t = ssm.Tuning(4, 0)
     assert scan(lib, tun=t) == INVALID
     t = ssm.Tuning(2, 12)
     assert scan(lib, tun=t) == INVALID
@@ -150,3 +150,13 @@ def test_ssd_validation(lib):
     assert ssd(lib, H=8, G=3) == UNSUPPORTED
     assert ssd(lib, y=P[0]) == INVALID
     assert ssd(lib, B=0) == OK
+
+
+def test_scan_lanesplit_variant_limits(lib):
+    """Variant 3 (states split over lanes) exists for N in {4, 8, 16, 32, 64}
+    with 16-byte aligned B and C; elsewhere it is refused before any launch."""
+    t = ssm.Tuning(3, 0)
+    assert scan(lib, N=5, tun=t) == UNSUPPORTED
+    assert scan(lib, N=12, tun=t) == UNSUPPORTED
+    odd = ctypes.c_void_p(P[3].value + 2)
+    assert scan(lib, Bm=odd, tun=t) == UNSUPPORTED

@@ -12,7 +12,8 @@ from tests.helpers import assert_close, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [(1, 0), (2, 8), (2, 64)]  # (variant, chunk_len)
+VARIANTS = [(1, 0), (2, 8), (2, 64), (3, 0)]  # (variant, chunk_len)
+LANESPLIT_N = (4, 8, 16, 32, 64)  # N the lane-split kernel (variant 3) is built for
 
 
 def _say(*a):
@@ -47,7 +48,7 @@ def test_tiny_fp32(oracle_mod, variant, chunk, gate, h0):
     assert_close(hf, rh, "f32", "h_final")
 
 
-@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 0), (2, 128)])
+@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 0), (2, 128), (3, 0)])
 @pytest.mark.parametrize("h0", [False, True])
 def test_mamba130m_fp32(oracle_mod, variant, chunk, h0):
     inp = gen.make_workload("mamba130m_fp32")
@@ -58,7 +59,7 @@ def test_mamba130m_fp32(oracle_mod, variant, chunk, h0):
     assert_close(hf, rh, "f32", "h_final")
 
 
-@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 0)])
+@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 0), (3, 0)])
 def test_mamba130m_split_sequence(oracle_mod, variant, chunk):
     """Two calls of L/2 with h_final fed back as h0 equal one oracle scan of L."""
     import mamba_selective_scan_ssm_amd as ssm
@@ -121,10 +122,15 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("B,L,D,N,dtype", SHAPES)
-@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 16)])
+@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 16), (3, 0)])
 def test_shapes(oracle_mod, B, L, D, N, dtype, variant, chunk):
+    import mamba_selective_scan_ssm_amd as ssm
     inp = gen.make_scan(B, L, D, N, dtype=dtype, seed=100 + L + D + N)
     _say("shape", B, L, D, N, dtype, variant, chunk)
+    if variant == 3 and N not in LANESPLIT_N:
+        with pytest.raises(ssm.SSMError):
+            run_gpu(inp, variant=variant, chunk_len=chunk)
+        return
     y, hf = run_gpu(inp, variant=variant, chunk_len=chunk)
     ry, rh = run_oracle(oracle_mod, inp)
     assert_close(y, ry, dtype, "y")
@@ -172,7 +178,7 @@ def test_repeat_determinism():
     _say("determinism")
     t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
     A, Ds, h0 = to_dev(inp.A), to_dev(inp.D_skip), to_dev(inp.h0)
-    for variant in (1, 2):
+    for variant in (1, 2, 3):
         outs = [ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0,
                              variant=variant) for _ in range(3)]
         for y, hf in outs[1:]:
@@ -199,7 +205,7 @@ def test_guard_bands_untouched():
     t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
     A, Ds, h0 = to_dev(inp.A), to_dev(inp.D_skip), to_dev(inp.h0)
     G = 4096
-    for variant in (1, 2):
+    for variant in (1, 2, 3):
         ybuf = torch.full((G + 2 * 45 * 100 + G,), float("nan"), dtype=torch.bfloat16, device="cuda")
         hbuf = torch.full((G + 2 * 100 * 16 + G,), float("nan"), dtype=torch.float32, device="cuda")
         y = ybuf[G:G + 2 * 45 * 100].view(2, 45, 100)
@@ -237,3 +243,50 @@ def test_rejects_non_contiguous():
     with pytest.raises(ValueError):
         ssm.scan_fwd(xz[..., :64], to_dev(inp.delta), to_dev(inp.A), to_dev(inp.Bm),
                      to_dev(inp.Cm))
+
+
+KERNEL_PAIR_SHAPES = [
+    (2, 300, 1536, 16, "bf16"), (3, 37, 1500, 16, "f32"), (2, 77, 200, 4, "bf16"),
+    (1, 129, 96, 8, "f32"), (2, 65, 130, 32, "bf16"), (1, 50, 64, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,L,D,N,dtype", KERNEL_PAIR_SHAPES)
+@pytest.mark.parametrize("gate", [False, True])
+def test_lanesplit_matches_wavesplit_bitwise(B, L, D, N, dtype, gate):
+    """The two channel-sequential kernels (states split over waves, variant 1;
+    over lanes, variant 3) do the same fp32 operations in the same order, so
+    the automatic choice between them (which also depends on the alignment of
+    Bm and Cm) never changes a result."""
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(B, L, D, N, dtype=dtype, seed=300 + L + N)
+    _say("lanesplit vs wavesplit", B, L, D, N, dtype, gate)
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds, h0 = to_dev(inp.A), to_dev(inp.D_skip), to_dev(inp.h0)
+    z = t["z"] if gate else None
+    y1, h1 = ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, z, h0, variant=1)
+    y3, h3 = ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, z, h0, variant=3)
+    assert torch.equal(y1, y3) and torch.equal(h1, h3)
+
+
+def test_unaligned_bc_falls_back_bitwise():
+    """B/C views that are not 16-byte aligned take the wave-split kernel and
+    give the same bits as aligned copies (which take the lane-split one)."""
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(1, 90, 256, 16, dtype="bf16", seed=29)
+    _say("unaligned B/C")
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds, h0 = to_dev(inp.A), to_dev(inp.D_skip), to_dev(inp.h0)
+    n = t["Bm"].numel()
+    bbuf = torch.empty(n + 1, dtype=t["Bm"].dtype, device="cuda")
+    cbuf = torch.empty(n + 1, dtype=t["Cm"].dtype, device="cuda")
+    bu = bbuf[1:].view(t["Bm"].shape)
+    cu = cbuf[1:].view(t["Cm"].shape)
+    bu.copy_(t["Bm"])
+    cu.copy_(t["Cm"])
+    assert bu.data_ptr() % 16 != 0
+    ya, ha = ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0)
+    yu, hu = ssm.scan_fwd(t["x"], t["delta"], A, bu, cu, Ds, t["z"], h0)
+    assert torch.equal(ya, yu) and torch.equal(ha, hu)
+    with pytest.raises(ssm.SSMError):
+        ssm.scan_fwd(t["x"], t["delta"], A, bu, cu, Ds, t["z"], h0, variant=3)
