@@ -243,10 +243,268 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(int64_t B, int64_t 
 // ---------------------------------------------------------------------------
 // 3. chunk outputs
 // ---------------------------------------------------------------------------
+// One workgroup of 8 waves per (chunk, group), looping over the group's
+// heads.  The chunk's B rows are staged in LDS once (row-major, as the
+// A-operand of CB^T = B C^T needs them) and each wave keeps the C fragments
+// of its row blocks in registers, so CB^T is recomputed per head from
+// on-chip operands only.  Per head, x^T and the state entering the chunk
+// (split into bf16 hi + lo) are staged in LDS; the next head's x, state and
+// dt are loaded into registers while the current head computes.  Per wave
+// and row block I (rows i), one 32-wide p tile:
+//   Y_I = exp(S_i) C_I h_in^T + sum_{J <= I} M_IJ X_J,
+//   M_IJ[i][j] = CB^T[j][i] exp(S_i - S_j) dt_j (j <= i),
+// on the matrix cores with M formed in registers.  With 8 row blocks, wave w
+// takes blocks 7 - w%4 and w%4 of p tile w/4: 9 (I, J) blocks per wave.
 constexpr int kQPad = 256 + 8;
+constexpr int kScanThreads = 1024;
 
 template <int N>
-__global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(SSDArgs a, const float *ws_states) {
+__global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs a, const float *ws_states) {
+  const int Q = static_cast<int>(a.chunk);
+  const int64_t c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int64_t nc = gridDim.x, H = a.H, L = a.L, G = a.G;
+  const int64_t HPG = H / G;
+  const int64_t t0 = c * Q;
+  const int nvalid = static_cast<int>((L - t0) < Q ? (L - t0) : Q);
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64, lg = lane / 32, l32 = lane % 32;
+  constexpr int KS = N / 16;   // K steps over n
+  constexpr int kNPad = N + 8;
+  constexpr int kXU = (256 / 2) * (kP / 8) / kScanThreads;  // x staging units per thread (Q = 256)
+  constexpr int kHTot = kP * N / 4;                          // state float4s
+  constexpr int kHU = (kHTot + kScanThreads - 1) / kScanThreads;
+  static_assert(kXU >= 1 && kXU * kScanThreads == (256 / 2) * (kP / 8), "x staging must tile");
+
+  __shared__ float s_S[256];   // in-chunk cumulative log2 decay of the current head
+  __shared__ float s_T[256];   // log2(dt_j) - S_j
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[256 * kNPad];  // B rows: [j][n]
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kP * kQPad];   // x^T: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t s_hh[kP * kNPad];  // h_in hi: [p][n]
+  __shared__ __attribute__((aligned(16))) uint16_t s_hl[kP * kNPad];  // h_in lo
+
+  const uint16_t *Bp = static_cast<const uint16_t *>(a.Bm);
+  const uint16_t *Cp = static_cast<const uint16_t *>(a.Cm);
+  const uint16_t *xp = static_cast<const uint16_t *>(a.x);
+  const uint16_t *dtp = static_cast<const uint16_t *>(a.dt);
+  uint16_t *yp = static_cast<uint16_t *>(a.y);
+  const uint16_t *zp = static_cast<const uint16_t *>(a.z);
+  const int nIB = Q / 32;
+
+  // this wave's row block IA (IA < 0: none; IB is never used) and p tile.
+  // Wave k runs on SIMD k % 4; with 8 row blocks the four waves of a SIMD
+  // take blocks s and 7 - s of both p tiles, 18 (I, J) blocks per SIMD.
+  int IA, IB = -1, pt;
+  {
+    const int sm = wave % 4, m = wave / 4;
+    if (nIB == 8) {
+      IA = (m % 2 == 0) ? sm : 7 - sm; pt = m / 2;
+    } else if (nIB == 4) {
+      IA = wave < 8 ? wave % 4 : -1; pt = (wave / 4) % 2;
+    } else {
+      IA = wave < 4 ? wave % 2 : -1; pt = (wave / 2) % 2;
+    }
+  }
+  const bool active = IA >= 0;
+  const int iA = (active ? IA : 0) * 32 + l32;  // C row of this lane
+  const int p_lane = pt * 32 + l32;
+
+  // stage the chunk's B rows (zeros past the end)
+  for (int u = tid; u < 256 * (N / 8); u += kScanThreads) {
+    const int j = u / (N / 8), n8 = u % (N / 8);
+    const uint4 v = load8_raw(Bp + ((b * L + t0 + j) * G + g) * N + n8 * 8, j < nvalid);
+    *reinterpret_cast<uint4 *>(&s_b[j * kNPad + n8 * 8]) = v;
+  }
+  // C fragments of the row blocks (B-operand columns i of CB^T, A-operand
+  // rows i of Y_off)
+  bf16x8 cfA[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    cfA[ks] = load8(Cp + ((b * L + t0 + iA) * G + g) * N + ks * 16 + 8 * lg, active && iA < nvalid);
+  auto cb_block = [&](int J, const bf16x8 *cf) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(&s_b[(J * 32 + l32) * kNPad + ks * 16 + 8 * lg]);
+      acc = mfma(bfr, cf[ks], acc);
+    }
+    return acc;
+  };
+
+  // per-head inputs in flight: x (pairs of rows, 8 columns each) and (wave
+  // 0) dt of tokens 4 lane .. 4 lane + 3
+  uint4 px[kXU][2];
+  float pdt[4] = {0.f, 0.f, 0.f, 0.f};
+  // x of one (chunk, head) through a buffer resource: row j, column p at
+  // ((j * H) * P + p) * 2 bytes; rows past the valid tokens read zeros
+  const int x_bytes = static_cast<int>(((nvalid - 1) * H * kP + kP) * 2);
+  auto prefetch = [&](int64_t h) {
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(xp + ((b * L + t0) * H + h) * kP), 0, x_bytes, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < kXU; ++k) {
+      const int u = tid + k * kScanThreads;
+      const int jp = u / (kP / 8), pc = u % (kP / 8);
+      const int j0 = 2 * jp;
+      const int off = (j0 * static_cast<int>(H) * kP + pc * 8) * 2;
+      const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(rx, off + static_cast<int>(H) * kP * 2, 0, 0);
+      px[k][0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+      px[k][1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * lane + e;
+        pdt[e] = j < nvalid ? bf_to_f(bf16_bits(dtp[(b * L + t0 + j) * H + h])) : 0.f;
+      }
+    }
+  };
+
+  prefetch(g * HPG);
+  __syncthreads();  // B rows staged
+  for (int64_t hh = 0; hh < HPG; ++hh) {
+    const int64_t h = g * HPG + hh;
+    if (hh > 0) __syncthreads();  // the previous head's LDS reads are done
+    // stage x^T and the state split into hi + lo
+    const float *hin = ws_states + ((b * nc + c) * H + h) * (int64_t)kP * N;
+    float4 ph[kHU];
+#pragma unroll
+    for (int k = 0; k < kHU; ++k) {
+      const int u = tid + k * kScanThreads;
+      ph[k] = u < kHTot ? *reinterpret_cast<const float4 *>(hin + 4 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < kXU; ++k) {
+      const int u = tid + k * kScanThreads;
+      const int jp = u / (kP / 8), pc = u % (kP / 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int off = (pc * 8 + e) * kQPad + 2 * jp;
+        *reinterpret_cast<uint32_t *>(&s_x[off]) = pack2(elem16(px[k][0], e), elem16(px[k][1], e));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kHU; ++k) {
+      const int u = tid + k * kScanThreads;
+      if (u >= kHTot) break;
+      const int p = u / (N / 4), n4 = u % (N / 4);
+      const float vv[4] = {ph[k].x, ph[k].y, ph[k].z, ph[k].w};
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        __bf16 h0v, l0v, h1v, l1v;
+        split_bf16(vv[2 * e], h0v, l0v);
+        split_bf16(vv[2 * e + 1], h1v, l1v);
+        hw[e] = pack2(__builtin_bit_cast(uint16_t, h0v), __builtin_bit_cast(uint16_t, h1v));
+        lw[e] = pack2(__builtin_bit_cast(uint16_t, l0v), __builtin_bit_cast(uint16_t, l1v));
+      }
+      *reinterpret_cast<uint2 *>(&s_hh[p * kNPad + 4 * n4]) = make_uint2(hw[0], hw[1]);
+      *reinterpret_cast<uint2 *>(&s_hl[p * kNPad + 4 * n4]) = make_uint2(lw[0], lw[1]);
+    }
+    // wave 0: S = inclusive cumsum of dt A (log2 units) and T = log2(dt) - S
+    if (wave == 0) {
+      const float A2 = a.A[h] * kLog2e;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = pdt[e] * A2 + (e > 0 ? v[e - 1] : 0.f);
+      float run = v[3];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(run, off, 64);
+        if (lane >= off) run += o;
+      }
+      const float excl = run - v[3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float S = v[e] + excl;
+        s_S[4 * lane + e] = S;
+        s_T[4 * lane + e] = __builtin_amdgcn_logf(pdt[e]) - S;  // log2; dt = 0 gives -inf
+      }
+    }
+    __syncthreads();
+    if (hh + 1 < HPG) prefetch(h + 1);
+    if (!active) continue;
+
+    // one row block at a time: Y_off = exp(S_i) C_I h_in^T, then Y_diag
+    // (CB^T masked and decayed into M, Y += M X_J), then + D x, gate, store
+    const float Dh = a.D_skip ? a.D_skip[h] : 0.f;
+    const int64_t head0 = ((b * L + t0) * H + h) * kP;  // element (token t0, head h, p 0)
+    const int yz_bytes = static_cast<int>(((nvalid - 1) * H * kP + kP) * 2);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(yp + head0, 0, yz_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(zp ? zp + head0 : yp + head0), 0, yz_bytes, 0x00020000);
+    auto row_block = [&](int I, const bf16x8 *cf) {
+      const int i_lane = I * 32 + l32;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = p_lane * kNPad + ks * 16 + 8 * lg;
+        const bf16x8 vh = *reinterpret_cast<const bf16x8 *>(&s_hh[off]);
+        const bf16x8 vl = *reinterpret_cast<const bf16x8 *>(&s_hl[off]);
+        acc = mfma(cf[ks], vh, acc);
+        acc = mfma(cf[ks], vl, acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] *= fast_exp2(s_S[I * 32 + 8 * (r / 4) + 4 * lg + (r % 4)]);
+      const float S_i = s_S[i_lane < Q ? i_lane : Q - 1];
+      for (int J = 0; J <= I; ++J) {
+        const f32x16 cb = cb_block(J, cf);
+        bf16x8 mh[2], ml[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = J * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+          float m = cb[r] * fast_exp2(S_i + s_T[j]);
+          if (J == I && j > i_lane) m = 0.f;
+          __bf16 x1, x2;
+          split_bf16(m, x1, x2);
+          mh[r / 8][r % 8] = x1;
+          ml[r / 8][r % 8] = x2;
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int jb = J * 32 + 16 * k2 + 4 * lg;
+          const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&s_x[p_lane * kQPad + jb]);
+          const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&s_x[p_lane * kQPad + jb + 8]);
+          const bf16x8 xf = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          acc = mfma(mh[k2], xf, acc);
+          acc = mfma(ml[k2], xf, acc);
+        }
+      }
+      // y and z of this (chunk, head) through buffer resources with 32-bit
+      // offsets: row i, column p at ((i * H) * P + p) * 2 bytes
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = I * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        const float xv = bf_to_f(bf16_bits(s_x[p_lane * kQPad + i]));
+        float v = fmaf(Dh, xv, acc[r]);
+        const int off = (i * static_cast<int>(H) * kP + p_lane) * 2;
+        if (zp) {
+          const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
+          v *= silu(__uint_as_float(zb << 16));
+        }
+        // rows past the chunk's valid tokens lie past the resource: dropped
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)), ry, off, 0, 0);
+      }
+    };
+    row_block(IA, cfA);
+  }
+}
+
+// Per-(chunk, head) variant for N > 128, whose B rows do not fit in LDS
+// beside x and the state: B fragments come from global memory.
+
+// One 32-row block I of a chunk's outputs: the C_I fragments, the running
+// Y accumulators (rows i, cols p in two 32-wide p tiles) and S_i.
+template <int KS>
+struct RowBlock {
+  int I;
+  int i_lane;
+  bf16x8 cf[KS];
+  f32x16 acc[2];
+  float S_i;
+};
+
+template <int N>
+__global__ __launch_bounds__(kThreads) void ssd_chunk_scan_head_kernel(SSDArgs a, const float *ws_states) {
   const int Q = static_cast<int>(a.chunk);
   const int64_t c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t nc = gridDim.x, H = a.H, L = a.L, G = a.G;
@@ -254,11 +512,15 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(SSDArgs a, con
   const int64_t t0 = c * Q;
   const int nvalid = static_cast<int>((L - t0) < Q ? (L - t0) : Q);
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64, lg = lane / 32, l32 = lane % 32;
+  constexpr int KS = N / 16;   // K steps over n
+  constexpr int kNPad = N + 8;
 
   __shared__ float s_S[256];
   __shared__ float s_dt[256];
   __shared__ float s_wave[4];
-  __shared__ __attribute__((aligned(16))) uint16_t s_x[kP * kQPad];  // x^T: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kP * kQPad];   // x^T: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t s_hh[kP * kNPad];  // h_in hi: [p][n]
+  __shared__ __attribute__((aligned(16))) uint16_t s_hl[kP * kNPad];  // h_in lo
 
   const uint16_t *dtp = static_cast<const uint16_t *>(a.dt);
   const float A2 = a.A[h] * kLog2e;
@@ -280,112 +542,130 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_kernel(SSDArgs a, con
       *reinterpret_cast<uint32_t *>(&s_x[off]) = pack2(elem16(r0, e), elem16(r1, e));
     }
   }
+  // the state entering the chunk, split once into bf16 hi + lo
+  const float *hin = ws_states + ((b * nc + c) * H + h) * (int64_t)kP * N;
+  for (int u = tid; u < kP * N / 4; u += kThreads) {
+    const int p = u / (N / 4), n4 = u % (N / 4);
+    const float4 v = *reinterpret_cast<const float4 *>(hin + p * N + 4 * n4);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      __bf16 h0v, l0v, h1v, l1v;
+      split_bf16(vv[2 * e], h0v, l0v);
+      split_bf16(vv[2 * e + 1], h1v, l1v);
+      hw[e] = pack2(__builtin_bit_cast(uint16_t, h0v), __builtin_bit_cast(uint16_t, h1v));
+      lw[e] = pack2(__builtin_bit_cast(uint16_t, l0v), __builtin_bit_cast(uint16_t, l1v));
+    }
+    *reinterpret_cast<uint2 *>(&s_hh[p * kNPad + 4 * n4]) = make_uint2(hw[0], hw[1]);
+    *reinterpret_cast<uint2 *>(&s_hl[p * kNPad + 4 * n4]) = make_uint2(lw[0], lw[1]);
+  }
   __syncthreads();
 
   const uint16_t *Bp = static_cast<const uint16_t *>(a.Bm);
   const uint16_t *Cp = static_cast<const uint16_t *>(a.Cm);
-  const float *hin = ws_states + ((b * nc + c) * H + h) * (int64_t)kP * N;
   const float Dh = a.D_skip ? a.D_skip[h] : 0.f;
   uint16_t *yp = static_cast<uint16_t *>(a.y);
   const uint16_t *zp = static_cast<const uint16_t *>(a.z);
-  constexpr int KS = N / 16;   // K steps over n
   const int nIB = Q / 32;
 
-  // wave -> i-blocks: pair a short and a long block when there are 8
-  for (int slot = 0; slot < 2; ++slot) {
-    int I;
-    if (nIB == 8) I = slot == 0 ? wave : 7 - wave;
-    else if (nIB == 4) I = slot == 0 ? wave : -1;
-    else I = (slot == 0 && wave < nIB) ? wave : -1;
-    if (I < 0) continue;
-    const int i_lane = I * 32 + l32;            // this lane's column i in CB^T / row in C frags
-    const bool i_ok = i_lane < nvalid;
+  // wave -> row blocks: with 8 blocks a long one (7 - w) and a short one (w),
+  // which share the B fragments of their common column blocks J <= w
+  RowBlock<KS> rb[2];
+  rb[0].I = nIB == 8 ? 7 - wave : (wave < nIB ? wave : -1);
+  rb[1].I = nIB == 8 ? wave : -1;
 
-    // C_I fragments (A-operand rows i for Y_off, B-operand cols i for CB^T)
-    bf16x8 cf[KS];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    RowBlock<KS> &R = rb[s];
+    if (R.I < 0) continue;
+    R.i_lane = R.I * 32 + l32;
+    const bool i_ok = R.i_lane < nvalid;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      cf[ks] = load8(Cp + ((b * L + t0 + i_lane) * G + g) * N + ks * 16 + 8 * lg, i_ok);
-
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
-    // Y_off = C h_in^T  (rows i, cols p), h_in split hi/lo
+      R.cf[ks] = load8(Cp + ((b * L + t0 + R.i_lane) * G + g) * N + ks * 16 + 8 * lg, i_ok);
+    R.S_i = s_S[R.i_lane < Q ? R.i_lane : Q - 1];
+    // Y_off = C_I h_in^T (rows i, cols p), then row i scaled by exp(S_i)
+    R.acc[0] = R.acc[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        const float *hr = hin + (pt * 32 + l32) * N + ks * 16 + 8 * lg;
-        const float4 v0 = *reinterpret_cast<const float4 *>(hr);
-        const float4 v1 = *reinterpret_cast<const float4 *>(hr + 4);
-        const float hv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        bf16x8 hh, hl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          __bf16 x1, x2;
-          split_bf16(hv[e], x1, x2);
-          hh[e] = x1;
-          hl[e] = x2;
-        }
-        acc[pt] = mfma(cf[ks], hh, acc[pt]);
-        acc[pt] = mfma(cf[ks], hl, acc[pt]);
+        const int off = (pt * 32 + l32) * kNPad + ks * 16 + 8 * lg;
+        const bf16x8 hh = *reinterpret_cast<const bf16x8 *>(&s_hh[off]);
+        const bf16x8 hl = *reinterpret_cast<const bf16x8 *>(&s_hl[off]);
+        R.acc[pt] = mfma(R.cf[ks], hh, R.acc[pt]);
+        R.acc[pt] = mfma(R.cf[ks], hl, R.acc[pt]);
       }
     }
-    // scale row i by exp(S_i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = I * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+      const int i = R.I * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
       const float sc = fast_exp2(s_S[i]);
-      acc[0][r] *= sc;
-      acc[1][r] *= sc;
+      R.acc[0][r] *= sc;
+      R.acc[1][r] *= sc;
     }
+  }
 
-    // Y_diag
-    const float S_i = s_S[i_lane < Q ? i_lane : Q - 1];
-    for (int J = 0; J <= I; ++J) {
-      const int j_lane = J * 32 + l32;
-      const bool j_ok = j_lane < nvalid;
-      f32x16 cb = f32x16{};
+  // Y_diag: for each column block J, CB^T[j][i] = B_J C_I^T on the matrix
+  // cores, masked and decayed into M[i][j] = CB^T[j][i] exp(S_i - S_j) dt_j
+  // (j <= i), then Y += M X_J.
+  auto diag_block = [&](RowBlock<KS> &R, const f32x16 &cb, int J) {
+    bf16x8 mh[2], ml[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 bfr = load8(Bp + ((b * L + t0 + j_lane) * G + g) * N + ks * 16 + 8 * lg, j_ok);
-        cb = mfma(bfr, cf[ks], cb);        // CB^T[j][i]
-      }
-      // M[i][j] = CB^T[j][i] * exp(S_i - S_j) * dt_j for j <= i
-      bf16x8 mh[2], ml[2];
+    for (int r = 0; r < 16; ++r) {
+      const int j = J * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+      float m = 0.f;
+      if (j <= R.i_lane) m = cb[r] * fast_exp2(R.S_i - s_S[j]) * s_dt[j];
+      __bf16 x1, x2;
+      split_bf16(m, x1, x2);
+      mh[r / 8][r % 8] = x1;
+      ml[r / 8][r % 8] = x2;
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = J * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-        float m = 0.f;
-        if (j <= i_lane) m = cb[r] * fast_exp2(S_i - s_S[j]) * s_dt[j];
-        __bf16 x1, x2;
-        split_bf16(m, x1, x2);
-        mh[r / 8][r % 8] = x1;
-        ml[r / 8][r % 8] = x2;
-      }
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int jb = J * 32 + 16 * k2 + 4 * lg;
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int jb = J * 32 + 16 * k2 + 4 * lg;
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          const int p = pt * 32 + l32;
-          const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&s_x[p * kQPad + jb]);
-          const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&s_x[p * kQPad + jb + 8]);
-          const bf16x8 xf = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          acc[pt] = mfma(mh[k2], xf, acc[pt]);
-          acc[pt] = mfma(ml[k2], xf, acc[pt]);
-        }
+      for (int pt = 0; pt < 2; ++pt) {
+        const int p = pt * 32 + l32;
+        const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&s_x[p * kQPad + jb]);
+        const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&s_x[p * kQPad + jb + 8]);
+        const bf16x8 xf = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        R.acc[pt] = mfma(mh[k2], xf, R.acc[pt]);
+        R.acc[pt] = mfma(ml[k2], xf, R.acc[pt]);
       }
     }
+  };
+  const int Jmax = rb[0].I;  // rb[0] holds the larger block when there are two
+  for (int J = 0; J <= Jmax; ++J) {
+    const int j_lane = J * 32 + l32;
+    const bool j_ok = j_lane < nvalid;
+    const bool both = rb[1].I >= 0 && J <= rb[1].I;
+    f32x16 cb0 = f32x16{}, cb1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 bfr = load8(Bp + ((b * L + t0 + j_lane) * G + g) * N + ks * 16 + 8 * lg, j_ok);
+      cb0 = mfma(bfr, rb[0].cf[ks], cb0);
+      if (both) cb1 = mfma(bfr, rb[1].cf[ks], cb1);
+    }
+    diag_block(rb[0], cb0, J);
+    if (both) diag_block(rb[1], cb1, J);
+  }
 
-    // epilogue: + D x, gate, store (rows i, cols p)
+  // epilogue: + D x, gate, store (rows i, cols p)
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    RowBlock<KS> &R = rb[s];
+    if (R.I < 0) continue;
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
       const int p = pt * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = I * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        const int i = R.I * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
         if (i < nvalid) {
           const float xv = bf_to_f(bf16_bits(s_x[p * kQPad + i]));
-          float v = fmaf(Dh, xv, acc[pt][r]);
+          float v = fmaf(Dh, xv, R.acc[pt][r]);
           const int64_t idx = ((b * L + t0 + i) * H + h) * kP + p;
           if (zp) v *= silu(bf_to_f(bf16_bits(zp[idx])));
           yp[idx] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
@@ -411,7 +691,12 @@ hipError_t launch_n(const SSDArgs &a, void *ws, hipStream_t s) {
   const int64_t tot = a.B * a.H * kP * N;
   ssd_state_pass_kernel<<<static_cast<unsigned>((tot + 255) / 256), 256, 0, s>>>(
       a.B, a.H, kP * N, nc, a.h0, decay, states, a.h_final);
-  ssd_chunk_scan_kernel<N><<<grid, kThreads, 0, s>>>(a, states);
+  if constexpr (N <= 128) {
+    dim3 grid_g(static_cast<unsigned>(nc), static_cast<unsigned>(a.G), static_cast<unsigned>(a.B));
+    ssd_chunk_scan_kernel<N><<<grid_g, kScanThreads, 0, s>>>(a, states);
+  } else {
+    ssd_chunk_scan_head_kernel<N><<<grid, kThreads, 0, s>>>(a, states);
+  }
   return hipGetLastError();
 }
 
