@@ -163,7 +163,7 @@ def bench_ssd(torch, ssm, gen, steps=10):
         one()
     except Exception as e:  # not built for this configuration
         return {"workload": "ssd_mamba2_bf16", "error": str(e)}
-    mean_ms, min_ms, wall_ms = time_calls(one, steps, 3, torch)
+    mean_ms, min_ms, wall_ms = time_calls(one, steps, 10, torch)
     B, L, H, P, G, N = w.B, w.L, w.H, w.P, w.G, w.N
     alg = (B * L * H * P * 2 * 2 + B * L * H * 2 + 2 * B * L * G * N * 2 + H * 8
            + 2 * B * H * P * N * 4)
@@ -179,8 +179,8 @@ def bench_ssd(torch, ssm, gen, steps=10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-rows", action="store_true", help="skip the decode and SSD rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=8)
@@ -262,7 +262,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_rows and args.only is None:
-        out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen)}
+        out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen, steps=20)}
     if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
     print(json.dumps(out))
