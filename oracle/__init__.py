@@ -51,6 +51,10 @@ def _load():
         lib.oracle_state_update.restype = None
         lib.oracle_ssd.argtypes = [i64] * 6 + [fp] * 8 + [fp, i64, dp, dp]
         lib.oracle_ssd.restype = None
+        lib.oracle_conv1d.argtypes = [i64] * 4 + [fp] * 4 + [ctypes.c_int, dp, dp]
+        lib.oracle_conv1d.restype = None
+        lib.oracle_conv1d_update.argtypes = [i64] * 3 + [dp] + [fp] * 3 + [ctypes.c_int, dp]
+        lib.oracle_conv1d_update.restype = None
         _lib = lib
     return _lib
 
@@ -161,3 +165,35 @@ def ssd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threads=N
     if full:
         return (y.reshape(B, H, P, L).transpose(0, 3, 1, 2).copy(), h.reshape(B, H, P, N))
     return y, h
+
+
+def conv1d(x, w, bias=None, state0=None, act=False):
+    """Short causal convolution (width K) ahead of the scan.
+
+    Shapes: x (B, L, D); w (D, K); bias (D,); state0 (B, D, K-1), the K-1
+    previous inputs of each channel, oldest first (zeros when None).  Returns
+    y (B, L, D) and the new state (B, D, K-1), both fp64.
+    """
+    lib = _load()
+    x, w, bias, state0 = map(_f32, (x, w, bias, state0))
+    B, L, D = x.shape
+    K = w.shape[1]
+    y = np.empty((B, L, D), dtype=np.float64)
+    st = np.empty((B, D, K - 1), dtype=np.float64)
+    lib.oracle_conv1d(B, L, D, K, _ptr(x), _ptr(w), _ptr(bias), _ptr(state0), int(bool(act)),
+                      y.ctypes.data, st.ctypes.data)
+    return y, st
+
+
+def conv1d_update(state, x, w, bias=None, act=False):
+    """One decode step of the causal convolution.  state (S, D, K-1) fp64 is
+    updated in place; returns y (S, D)."""
+    lib = _load()
+    assert state.dtype == np.float64 and state.flags.c_contiguous
+    x, w, bias = map(_f32, (x, w, bias))
+    S, D = x.shape
+    K = w.shape[1]
+    y = np.empty((S, D), dtype=np.float64)
+    lib.oracle_conv1d_update(S, D, K, state.ctypes.data, _ptr(x), _ptr(w), _ptr(bias),
+                             int(bool(act)), y.ctypes.data)
+    return y

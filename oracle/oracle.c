@@ -44,12 +44,24 @@
  *   MambaMixer2".  The chunked SSD algorithm reaches this recurrence exactly
  *   (up to rounding order); the chunk length does not enter the definition.
  *
+ * - Short causal convolution ahead of the scan (ggml's SSM_CONV op of the
+ *   llama.cpp page, whose signature ggml_ssm_conv(ctx, s, x, c) and tensor
+ *   shapes s {d_conv-1, d_inner, n_seqs}, x {d_inner, n_seq_tokens, n_seqs},
+ *   c {d_conv, d_inner} appear in compilade's test patch; the conv bias
+ *   tensor ssm_conv1d_b {d_inner} in the ctx_layer diff; the concat of the
+ *   carried state with the new tokens in compilade's im2col/concat notes;
+ *   Megatron's causal_conv1d_update for the decode step): per channel the
+ *   state holds the previous d_conv - 1 inputs, oldest first; the window
+ *   xp = [state, x] gives y_t = sum_k c[d][k] xp[t + k] (+ bias, then the
+ *   optional SiLU), and the new state is the last d_conv - 1 entries of xp.
+ *
  * Layouts: row-major, last index fastest.
  *   scan:   x, delta, z: (B, L, D); Bm, Cm: (B, L, N); A: (D, N); D_skip: (D);
  *           h0: (B, D, N)
  *   step:   state: (S, D, N); x, delta, z: (S, D); Bm, Cm: (S, N)
  *   SSD:    x, z: (B, L, H, P); dt: (B, L, H); A, D_skip: (H); Bm, Cm:
  *           (B, L, G, N); h0: (B, H, P, N)
+ *   conv:   x, y: (B, L, D); w: (D, K); bias: (D); state: (B, D, K-1)
  * Outputs are written per requested channel so that a test can evaluate a
  * sample of channels of a full-size problem:
  *   y_out[k*L + t] and h_out[k*N + n] for the k-th requested channel.
@@ -57,6 +69,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 static double silu(double v) { return v / (1.0 + exp(-v)); }
 
@@ -165,6 +178,65 @@ void oracle_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N
             if (D_skip) v += (double)D_skip[hd] * u;
             if (z) v *= silu((double)z[(tok * H + hd) * P + p]);
             y_out[k * L + t] = v;
+        }
+    }
+}
+
+/*
+ * Causal convolution of width K over L tokens for every (b, d).  state0 may
+ * be NULL (zeros), bias may be NULL; act = 1 applies SiLU to the output.
+ * y: (B, L, D); state_out: (B, D, K-1), the last K-1 entries of [state0, x].
+ */
+void oracle_conv1d(int64_t B, int64_t L, int64_t D, int64_t K,
+                   const float *x, const float *w, const float *bias,
+                   const float *state0, int act, double *y, double *state_out)
+{
+    const int64_t W = K - 1 + L;  /* length of the padded sequence */
+    double *xp = (double *)malloc((size_t)(W > 0 ? W : 1) * sizeof(double));
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            for (int64_t j = 0; j < K - 1; ++j)
+                xp[j] = state0 ? (double)state0[(b * D + d) * (K - 1) + j] : 0.0;
+            for (int64_t t = 0; t < L; ++t)
+                xp[K - 1 + t] = x[(b * L + t) * D + d];
+            for (int64_t t = 0; t < L; ++t) {
+                double v = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    v += (double)w[d * K + k] * xp[t + k];
+                if (bias) v += (double)bias[d];
+                if (act) v = silu(v);
+                y[(b * L + t) * D + d] = v;
+            }
+            for (int64_t j = 0; j < K - 1; ++j)
+                state_out[(b * D + d) * (K - 1) + j] = xp[L + j];
+        }
+    }
+    free(xp);
+}
+
+/*
+ * One decode step of the causal convolution for S sequences: window =
+ * [state, x_t], y = sum_k w[d][k] window[k] (+ bias, SiLU), and the state
+ * drops its oldest entry and appends x_t (fp64 state, updated in place).
+ */
+void oracle_conv1d_update(int64_t S, int64_t D, int64_t K, double *state,
+                          const float *x, const float *w, const float *bias,
+                          int act, double *y)
+{
+    for (int64_t s = 0; s < S; ++s) {
+        for (int64_t d = 0; d < D; ++d) {
+            double *st = state + (s * D + d) * (K - 1);
+            const double xt = x[s * D + d];
+            double v = 0.0;
+            for (int64_t k = 0; k < K - 1; ++k)
+                v += (double)w[d * K + k] * st[k];
+            v += (double)w[d * K + K - 1] * xt;
+            if (bias) v += (double)bias[d];
+            if (act) v = silu(v);
+            y[s * D + d] = v;
+            for (int64_t k = 0; k + 1 < K - 1; ++k)
+                st[k] = st[k + 1];
+            if (K > 1) st[K - 2] = xt;
         }
     }
 }

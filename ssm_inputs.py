@@ -30,6 +30,13 @@ Mamba-1 scan:  x, delta, z, y: (B, L, D); Bm, Cm: (B, L, N); A: (D, N);
 Decode:        per step x, delta, z: (S, D); Bm, Cm: (S, N); state (S, D, N).
 Mamba-2 SSD:   x, z, y: (B, L, H, P); dt: (B, L, H); Bm, Cm: (B, L, G, N);
                A, D_skip: (H,); h0, h_final: (B, H, P, N).
+Causal conv:   x, y: (B, L, D); w: (D, K); bias: (D,); state: (B, D, K-1)
+               (decode: x per step (S, D), state (S, D, K-1)).
+
+The short causal convolution's inputs draw from streams of their own:
+x ~ N(0, 1) and state ~ N(0, 1) (the state holds earlier inputs); weights
+and bias ~ U(-1/sqrt(K), 1/sqrt(K)), the range of a freshly initialised
+depthwise convolution of width K.
 """
 
 from __future__ import annotations
@@ -213,7 +220,70 @@ def make_ssd(B, L, H, P, G, N, *, chunk=256, dtype="bf16", seed=0, gate=False, h
 
 
 # ---------------------------------------------------------------------------
-# The five workloads, by what they are
+# Short causal convolution inputs
+# ---------------------------------------------------------------------------
+
+_CONV_STREAMS = ("conv_x", "conv_w", "conv_bias", "conv_state")
+
+
+def _conv_children(seed: int):
+    # children after the scan's, so the scan streams of a seed never move
+    kids = np.random.SeedSequence(seed).spawn(len(_STREAMS) + len(_CONV_STREAMS))[len(_STREAMS):]
+    return {name: np.random.default_rng(k) for name, k in zip(_CONV_STREAMS, kids)}
+
+
+def _uniform_sym(rng, shape, bound):
+    return rng.uniform(-bound, bound, size=shape).astype(np.float32)
+
+
+@dataclasses.dataclass
+class ConvInputs:
+    B: int
+    L: int
+    D: int
+    K: int
+    dtype: str                 # storage dtype of x (and y)
+    x: Tensor                  # (B, L, D)
+    w: np.ndarray              # fp32 (D, K)
+    bias: np.ndarray | None    # fp32 (D,)
+    state0: np.ndarray | None  # fp32 (B, D, K-1)
+
+
+def make_conv(B, L, D, K, *, dtype="bf16", seed=0, bias=True, state=True) -> ConvInputs:
+    r = _conv_children(seed)
+    bound = 1.0 / math.sqrt(K)
+    x = _store(_normal(r["conv_x"], (B, L, D)), dtype)
+    w = _uniform_sym(r["conv_w"], (D, K), bound)
+    bb = _uniform_sym(r["conv_bias"], (D,), bound) if bias else None
+    st = _normal(r["conv_state"], (B, D, K - 1)) if state else None
+    return ConvInputs(B, L, D, K, dtype, x, w, bb, st)
+
+
+@dataclasses.dataclass
+class ConvDecodeInputs:
+    S: int
+    D: int
+    K: int
+    steps: int
+    dtype: str
+    x: Tensor               # (steps, S, D)
+    w: np.ndarray           # fp32 (D, K)
+    bias: np.ndarray        # fp32 (D,)
+    state0: np.ndarray      # fp32 (S, D, K-1)
+
+
+def make_conv_decode(S, D, K, steps, *, dtype="bf16", seed=0) -> ConvDecodeInputs:
+    r = _conv_children(seed)
+    bound = 1.0 / math.sqrt(K)
+    x = _store(_normal(r["conv_x"], (steps, S, D)), dtype)
+    w = _uniform_sym(r["conv_w"], (D, K), bound)
+    bb = _uniform_sym(r["conv_bias"], (D,), bound)
+    st = _normal(r["conv_state"], (S, D, K - 1))
+    return ConvDecodeInputs(S, D, K, steps, dtype, x, w, bb, st)
+
+
+# ---------------------------------------------------------------------------
+# The workloads, by what they are
 # ---------------------------------------------------------------------------
 
 WORKLOADS = {
@@ -230,6 +300,11 @@ WORKLOADS = {
     # Mamba-2 SSD chunked scan, bf16 inputs, fp32 state, random h0
     "ssd_mamba2_bf16": dict(kind="ssd", B=2, L=8192, H=80, P=64, G=8, N=128, chunk=256,
                             dtype="bf16", gate=False, seed=1004),
+    # the width-4 causal convolution ahead of the 2.8B-shaped prefill scan
+    "conv_mamba2p8b_bf16": dict(kind="conv", B=8, L=4096, D=5120, K=4, dtype="bf16", seed=1005),
+    # its decode step: 256 sequences, 128 single-token steps
+    "conv_decode_256x5120_bf16": dict(kind="conv_decode", S=256, D=5120, K=4, steps=128,
+                                      dtype="bf16", seed=1006),
 }
 
 
@@ -246,4 +321,8 @@ def make_workload(name: str, **overrides):
     if kind == "ssd":
         return make_ssd(w["B"], w["L"], w["H"], w["P"], w["G"], w["N"], chunk=w["chunk"],
                         dtype=w["dtype"], seed=w["seed"], gate=w["gate"], h0=w.get("h0", True))
+    if kind == "conv":
+        return make_conv(w["B"], w["L"], w["D"], w["K"], dtype=w["dtype"], seed=w["seed"])
+    if kind == "conv_decode":
+        return make_conv_decode(w["S"], w["D"], w["K"], w["steps"], dtype=w["dtype"], seed=w["seed"])
     raise ValueError(kind)
