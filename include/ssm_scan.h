@@ -32,9 +32,10 @@
  *              output (compilade's follow-up); non-contiguous x/z views as a
  *              source of wrong results (slaren's ggml_cont diff).
  * [megatron#6444] "Clean up SSM ops directory structure - #6444": the decode
- *              op selective_state_update and the Mamba-2 state-space-duality
+ *              op selective_state_update, the Mamba-2 state-space-duality
  *              kernels ssd_bmm, ssd_chunk_state, ssd_state_passing,
- *              ssd_chunk_scan, ssd_combined.
+ *              ssd_chunk_scan, ssd_combined, and the short causal
+ *              convolution's causal_conv1d_update.
  * [fastllm#333] "Tensor-parallel SSM #333": head groups (repeat_interleave of
  *              groups to heads) for Mamba-2.
  * [mixer2-tp]  "Current Implementation of TP in MambaMixer2": the number of
@@ -179,6 +180,43 @@ ssm_status ssm_ssd_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
 
 size_t ssm_ssd_fwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P,
                                   int64_t G, int64_t N, int64_t chunk);
+
+/*
+ * ssm_conv1d_fwd -- the short causal convolution that precedes the scan
+ * (ggml's SSM_CONV, [ggml#6758]: ggml_ssm_conv(s, x, c) with the state s
+ * holding each channel's d_conv - 1 previous inputs and the conv bias
+ * ssm_conv1d_b), over a prefill of L tokens.  For every b, d, with
+ * xp = [state_in[b,d,:], x[b,0,d], ..., x[b,L-1,d]]:
+ *   y[b,t,d] = act(sum_{k<K} w[d,k] * xp[t+k] + bias[d])
+ *   state_out[b,d,j] = xp[L + j],  j < K - 1   (the last K - 1 entries)
+ * act is the identity (activation == 0) or SiLU (activation == 1).
+ *
+ * x, y           : (B, L, D), dtype `dt`
+ * w              : (D, K) fp32;  bias : (D) fp32 or NULL
+ * state_in       : (B, D, K-1) fp32, oldest first, or NULL (zeros)
+ * state_out      : (B, D, K-1) fp32 or NULL (not returned)
+ * y must not overlap x, w, bias or the states; state_out must not overlap
+ * state_in (the segments of L run in parallel).  2 <= K <= 8.  L == 0 only
+ * writes state_out.  Sizes as ssm_scan_fwd (the (L + 64) * D plane limit).
+ */
+ssm_status ssm_conv1d_fwd(int64_t B, int64_t L, int64_t D, int64_t K, ssm_dtype dt,
+                          const void *x, const float *w, const float *bias,
+                          const float *state_in, int32_t activation, void *y,
+                          float *state_out, void *stream);
+
+/*
+ * ssm_conv1d_update -- one decode step of the causal convolution for S
+ * sequences (causal_conv1d_update, [megatron#6444]): window = [state, x],
+ * y = act(sum_k w[d,k] window[k] + bias[d]), and the state drops its oldest
+ * entry and appends x, IN PLACE.
+ *
+ * state : (S, D, K-1) fp32 in/out;  x, y : (S, D) dtype `dt`
+ * w : (D, K) fp32;  bias : (D) fp32 or NULL.  y must not overlap the other
+ * arguments.  2 <= K <= 8.
+ */
+ssm_status ssm_conv1d_update(int64_t S, int64_t D, int64_t K, ssm_dtype dt, float *state,
+                             const void *x, const float *w, const float *bias,
+                             int32_t activation, void *y, void *stream);
 
 /* Static description of a status code. */
 const char *ssm_status_string(ssm_status s);

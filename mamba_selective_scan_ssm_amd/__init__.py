@@ -58,6 +58,10 @@ def lib():
         L.ssm_ssd_fwd.restype = ctypes.c_int
         L.ssm_ssd_fwd_workspace_size.argtypes = [i64] * 7
         L.ssm_ssd_fwd_workspace_size.restype = sz
+        L.ssm_conv1d_fwd.argtypes = [i64] * 4 + [ctypes.c_int] + [vp] * 4 + [ctypes.c_int32, vp, vp, vp]
+        L.ssm_conv1d_fwd.restype = ctypes.c_int
+        L.ssm_conv1d_update.argtypes = [i64] * 3 + [ctypes.c_int] + [vp] * 4 + [ctypes.c_int32, vp, vp]
+        L.ssm_conv1d_update.restype = ctypes.c_int
         L.ssm_status_string.argtypes = [ctypes.c_int]
         L.ssm_status_string.restype = ctypes.c_char_p
         L.ssm_version.argtypes = []
@@ -212,3 +216,60 @@ def ssd_fwd_workspace_size(B, L, H, P, G, N, chunk) -> int:
 
 def version() -> int:
     return int(lib().ssm_version())
+
+
+def _act_code(activation) -> int:
+    if activation in (None, "none", "identity"):
+        return 0
+    if activation == "silu":
+        return 1
+    raise ValueError(f"activation must be None or 'silu', got {activation!r}")
+
+
+def conv1d_fwd(x, w, bias=None, state=None, *, activation="silu", y=None, state_out=None,
+               return_state=True):
+    """Short causal convolution ahead of the scan (ssm_conv1d_fwd).
+
+    x: (B, L, D) float32 or bfloat16; w: (D, K) float32; bias: (D,) float32;
+    state: (B, D, K-1) float32, the K-1 previous inputs of each channel,
+    oldest first (zeros when None).  Returns (y, state_out); y has the input
+    dtype, state_out (B, D, K-1) float32 (None if return_state is False).
+    """
+    if x.dim() != 3 or w.dim() != 2:
+        raise ValueError("x must be (B, L, D) and w (D, K)")
+    B, L, D = x.shape
+    K = w.shape[1]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _check("x", x, (B, L, D), dt, dev)
+    _check("w", w, (D, K), torch.float32, dev)
+    _check("bias", bias, (D,), torch.float32, dev)
+    _check("state", state, (B, D, K - 1), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, L, D), dtype=dt, device=dev)
+    _check("y", y, (B, L, D), dt, dev)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, D, K - 1), dtype=torch.float32, device=dev)
+    _check("state_out", state_out, (B, D, K - 1), torch.float32, dev)
+    _call("ssm_conv1d_fwd", B, L, D, K, code, _ptr(x), _ptr(w), _ptr(bias), _ptr(state),
+          _act_code(activation), _ptr(y), _ptr(state_out), _stream(dev))
+    return y, state_out
+
+
+def conv1d_update(state, x, w, bias=None, *, activation="silu", y=None):
+    """One decode step of the causal convolution (ssm_conv1d_update); `state`
+    (S, D, K-1) float32 is updated in place.  x: (S, D).  Returns y (S, D)."""
+    S, D, Km1 = state.shape
+    K = Km1 + 1
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _check("state", state, (S, D, Km1), torch.float32, dev)
+    _check("x", x, (S, D), dt, dev)
+    _check("w", w, (D, K), torch.float32, dev)
+    _check("bias", bias, (D,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((S, D), dtype=dt, device=dev)
+    _check("y", y, (S, D), dt, dev)
+    _call("ssm_conv1d_update", S, D, K, code, _ptr(state), _ptr(x), _ptr(w), _ptr(bias),
+          _act_code(activation), _ptr(y), _stream(dev))
+    return y

@@ -81,6 +81,54 @@ ssm_status hip_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_
 
 extern "C" {
 
+ssm_status ssm_conv1d_fwd(int64_t B, int64_t L, int64_t D, int64_t K, ssm_dtype dt,
+                          const void *x, const float *w, const float *bias,
+                          const float *state_in, int32_t activation, void *y,
+                          float *state_out, void *stream) {
+  if (B < 0 || L < 0 || D < 0 || K < 0) return SSM_ERR_INVALID_ARG;
+  if (!valid_dtype(dt) || (activation != 0 && activation != 1)) return SSM_ERR_INVALID_ARG;
+  if (K < 2 || K > 8) return SSM_ERR_UNSUPPORTED;
+  if (B == 0 || D == 0) return SSM_OK;
+  if (B > kMaxGridYZ || (L + 63) / 64 > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  const int64_t es = esize(dt);
+  if ((L + 64) * D * es >= (int64_t(1) << 31)) return SSM_ERR_UNSUPPORTED;
+  if (!w || (L > 0 && (!x || !y))) return SSM_ERR_INVALID_ARG;
+  const int64_t nBLD = B * L * D, nSt = B * D * (K - 1);
+  const Range ins[] = {{x, nBLD * es}, {w, D * K * 4}, {bias, D * 4}, {state_in, nSt * 4}};
+  if (overlaps_any(Range{y, nBLD * es}, ins)) return SSM_ERR_INVALID_ARG;
+  if (overlaps_any(Range{state_out, nSt * 4}, ins)) return SSM_ERR_INVALID_ARG;
+  if (overlap(Range{y, nBLD * es}, Range{state_out, nSt * 4})) return SSM_ERR_INVALID_ARG;
+  ssm::ConvArgs a{};
+  a.B = B; a.L = L; a.D = D; a.K = K;
+  a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
+  a.x = x; a.w = w; a.bias = bias; a.state_in = state_in; a.state_out = state_out;
+  a.y = y; a.act = activation == 1;
+  return hip_status(ssm::launch_conv1d_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+ssm_status ssm_conv1d_update(int64_t S, int64_t D, int64_t K, ssm_dtype dt, float *state,
+                             const void *x, const float *w, const float *bias,
+                             int32_t activation, void *y, void *stream) {
+  if (S < 0 || D < 0 || K < 0) return SSM_ERR_INVALID_ARG;
+  if (!valid_dtype(dt) || (activation != 0 && activation != 1)) return SSM_ERR_INVALID_ARG;
+  if (K < 2 || K > 8) return SSM_ERR_UNSUPPORTED;
+  if (S == 0 || D == 0) return SSM_OK;
+  if (!state || !x || !w || !y) return SSM_ERR_INVALID_ARG;
+  const int64_t es = esize(dt);
+  const Range ins[] = {{x, S * D * es}, {w, D * K * 4}, {bias, D * 4}, {state, S * D * (K - 1) * 4}};
+  if (overlaps_any(Range{y, S * D * es}, ins)) return SSM_ERR_INVALID_ARG;
+  const Range st{state, S * D * (K - 1) * 4};
+  if (overlap(st, Range{x, S * D * es}) || overlap(st, Range{w, D * K * 4}) ||
+      overlap(st, Range{bias, D * 4}))
+    return SSM_ERR_INVALID_ARG;
+  ssm::ConvArgs a{};
+  a.B = S; a.L = 1; a.D = D; a.K = K;
+  a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
+  a.x = x; a.w = w; a.bias = bias; a.state_in = state; a.state_out = state;
+  a.y = y; a.act = activation == 1;
+  return hip_status(ssm::launch_conv1d_update(a, static_cast<hipStream_t>(stream)));
+}
+
 const char *ssm_status_string(ssm_status s) {
   switch (s) {
     case SSM_OK: return "ok";

@@ -71,6 +71,23 @@ struct SSDArgs {
   float *h_final;
 };
 
+// Short causal convolution.  Prefill: x, y (B, L, D); state_in/state_out
+// (B, D, K-1) (either may be null; they do not overlap).  Decode step (B =
+// sequences, L = 1): state_out is the state, updated in place.
+struct ConvArgs {
+  int64_t B, L, D, K;
+  DType dt;
+  const void *x;
+  const float *w, *bias;
+  const float *state_in;
+  float *state_out;
+  void *y;
+  bool act;  // SiLU on the output
+};
+
+hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t s);
+hipError_t launch_conv1d_update(const ConvArgs &a, hipStream_t s);
+
 int64_t ssd_ws_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t chunk);
 hipError_t launch_ssd(const SSDArgs &a, void *ws, hipStream_t s);
 

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ssm_scan_fwd", "ssm_scan_fwd_workspace_size", "ssm_state_update", "ssm_ssd_fwd",
-              "ssm_ssd_fwd_workspace_size", "ssm_status_string", "ssm_version"):
+              "ssm_ssd_fwd_workspace_size", "ssm_conv1d_fwd", "ssm_conv1d_update",
+              "ssm_status_string", "ssm_version"):
         assert n in names
 
 
@@ -160,3 +161,42 @@ def test_scan_lanesplit_variant_limits(lib):
     assert scan(lib, N=12, tun=t) == UNSUPPORTED
     odd = ctypes.c_void_p(P[3].value + 2)
     assert scan(lib, Bm=odd, tun=t) == UNSUPPORTED
+
+
+def conv(lib, B=2, L=8, D=64, K=4, dt=F32, act=1, **over):
+    p = dict(x=P[0], w=P[1], bias=P[2], s_in=P[3], y=P[4], s_out=P[5])
+    p.update(over)
+    return lib.ssm_conv1d_fwd(B, L, D, K, dt, p["x"], p["w"], p["bias"], p["s_in"], act, p["y"],
+                              p["s_out"], None)
+
+
+def conv_upd(lib, S=2, D=64, K=4, dt=F32, act=1, **over):
+    p = dict(state=P[0], x=P[1], w=P[2], bias=P[3], y=P[4])
+    p.update(over)
+    return lib.ssm_conv1d_update(S, D, K, dt, p["state"], p["x"], p["w"], p["bias"], act, p["y"], None)
+
+
+def test_conv_validation(lib):
+    assert conv(lib, B=-1) == INVALID
+    assert conv(lib, act=2) == INVALID
+    assert conv(lib, dt=7) == INVALID
+    assert conv(lib, K=1) == UNSUPPORTED
+    assert conv(lib, K=9) == UNSUPPORTED
+    assert conv(lib, B=0) == OK
+    assert conv(lib, D=0) == OK
+    assert conv(lib, w=None) == INVALID
+    assert conv(lib, x=None) == INVALID
+    assert conv(lib, y=None) == INVALID
+    assert conv(lib, y=P[0]) == INVALID                  # y on x
+    assert conv(lib, s_out=P[3]) == INVALID              # state_out on state_in
+    assert conv(lib, L=1 << 30) == UNSUPPORTED
+
+
+def test_conv_update_validation(lib):
+    assert conv_upd(lib, S=-1) == INVALID
+    assert conv_upd(lib, act=-1) == INVALID
+    assert conv_upd(lib, K=9) == UNSUPPORTED
+    assert conv_upd(lib, S=0) == OK
+    assert conv_upd(lib, state=None) == INVALID
+    assert conv_upd(lib, y=P[0]) == INVALID              # y on the state
+    assert conv_upd(lib, x=P[0]) == INVALID              # x on the state
