@@ -13,8 +13,9 @@ The JSON line also carries
 * cpu_baseline: the fp64 CPU oracle (untuned, threads over channels) timed
   on a bounded sample of the same workload;
 * rows: the other hot-path entry points measured the same way -- the decode
-  step (S=256, D=5120, N=16, 128 steps) and the Mamba-2 SSD chunked scan
-  (B=2, L=8192, H=80, P=64, N=128, G=8, chunk 256).
+  step (S=256, D=5120, N=16, 128 steps), the Mamba-2 SSD chunked scan
+  (B=2, L=8192, H=80, P=64, N=128, G=8, chunk 256) and the width-4 causal
+  convolution ahead of the scan (B=8, L=4096, D=5120) with its decode step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -176,6 +177,45 @@ def bench_ssd(torch, ssm, gen, steps=10):
             "mfma_frac_bf16": flops / (mean_ms * 1e-3) / 2.5e15, "workspace_bytes": ws_n}
 
 
+def bench_conv(torch, ssm, gen, steps=50):
+    """Width-4 causal convolution ahead of the 2.8B-shaped scan (prefill) and
+    its decode step; both HBM-bound."""
+    c = gen.make_workload("conv_mamba2p8b_bf16")
+    B, L, D, K = c.B, c.L, c.D, c.K
+    x, w, bias, s0 = upload(c.x, torch), upload(c.w, torch), upload(c.bias, torch), upload(c.state0, torch)
+    y = torch.empty((B, L, D), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty((B, D, K - 1), dtype=torch.float32, device="cuda")
+
+    def one():
+        ssm.conv1d_fwd(x, w, bias, s0, y=y, state_out=st)
+
+    mean_ms, min_ms, _ = time_calls(one, steps, 10, torch)
+    alg = B * L * D * 2 * 2 + D * K * 4 + D * 4 + 2 * B * D * (K - 1) * 4
+    out = {"workload": "conv_mamba2p8b_bf16 (B=8, L=4096, D=5120, K=4, bf16, SiLU)",
+           "ms": mean_ms, "alg_bytes": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
+           "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    d = gen.make_workload("conv_decode_256x5120_bf16")
+    S, Dd, Kd = d.S, d.D, d.K
+    state = upload(d.state0, torch)
+    xs = upload(d.x, torch)
+    wd, bd = upload(d.w, torch), upload(d.bias, torch)
+    yd = torch.empty((S, Dd), dtype=torch.bfloat16, device="cuda")
+    it = [0]
+
+    def step():
+        t = it[0] % d.steps
+        it[0] += 1
+        ssm.conv1d_update(state, xs[t], wd, bd, y=yd)
+
+    dm, _, dwall = time_calls(step, 128, 8, torch)
+    dalg = S * Dd * (Kd - 1) * 4 * 2 + S * Dd * 2 * 2 + Dd * Kd * 4 + Dd * 4
+    out["decode"] = {"workload": "conv_decode_256x5120_bf16 (S=256, D=5120, K=4)",
+                     "kernel_ms_per_step": dm, "wall_ms_per_step": dwall, "alg_bytes_per_step": dalg,
+                     "hbm_GBs": dalg / (dm * 1e-3) / 1e9,
+                     "hbm_frac": dalg / (dm * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,7 +224,7 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the decode and SSD rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=8)
-    ap.add_argument("--only", choices=["scan", "decode", "ssd"], default=None,
+    ap.add_argument("--only", choices=["scan", "decode", "ssd", "conv"], default=None,
                     help="time one hot-path entry point only (for profiling); prints its row")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) so a "
@@ -211,6 +251,9 @@ def main():
         return
     if args.only == "ssd":
         print(json.dumps({"ssd": bench_ssd(torch, ssm, gen, steps=args.steps)}))
+        return
+    if args.only == "conv":
+        print(json.dumps({"conv": bench_conv(torch, ssm, gen, steps=args.steps)}))
         return
 
     name = "mamba2p8b_prefill_bf16"
@@ -262,7 +305,8 @@ def main():
         "roofline": roofline,
     }
     if not args.no_rows and args.only is None:
-        out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen, steps=20)}
+        out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen, steps=20),
+                       "conv": bench_conv(torch, ssm, gen)}
     if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
     print(json.dumps(out))
