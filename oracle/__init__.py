@@ -45,11 +45,11 @@ def _load():
             build()
         lib = ctypes.CDLL(_LIB)
         i64, fp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
-        lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [fp] * 8 + [fp, i64, dp, dp]
+        lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [fp] * 8 + [fp, i64, dp, dp, fp, ctypes.c_int]
         lib.oracle_scan.restype = None
-        lib.oracle_state_update.argtypes = [i64, i64, i64, dp] + [fp] * 7 + [dp]
+        lib.oracle_state_update.argtypes = [i64, i64, i64, dp] + [fp] * 7 + [dp, fp, ctypes.c_int]
         lib.oracle_state_update.restype = None
-        lib.oracle_ssd.argtypes = [i64] * 6 + [fp] * 8 + [fp, i64, dp, dp]
+        lib.oracle_ssd.argtypes = [i64] * 6 + [fp] * 8 + [fp, i64, dp, dp, fp, ctypes.c_int]
         lib.oracle_ssd.restype = None
         lib.oracle_conv1d.argtypes = [i64] * 4 + [fp] * 4 + [ctypes.c_int, dp, dp]
         lib.oracle_conv1d.restype = None
@@ -97,16 +97,19 @@ def _run_channels(fn, channels: np.ndarray, L: int, N: int, threads: int):
     return y, h
 
 
-def scan(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threads=None):
+def scan(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threads=None,
+         delta_bias=None, delta_softplus=False):
     """Mamba-1 selective scan.
 
     Shapes: x, delta, z (B, L, D); Bm, Cm (B, L, N); A (D, N); D_skip (D,);
     h0 (B, D, N).  With ``channels=None`` returns y (B, L, D) and h_final
     (B, D, N) in fp64; otherwise ``channels`` lists flat indices b*D + d and
-    the result is y (k, L), h_final (k, N) for those channels.
+    the result is y (k, L), h_final (k, N) for those channels.  The step
+    size is delta (+ delta_bias (D,)) (then softplus when delta_softplus).
     """
     lib = _load()
     x, delta, A, Bm, Cm = map(_f32, (x, delta, A, Bm, Cm))
+    delta_bias = _f32(delta_bias)
     D_skip, z, h0 = map(_f32, (D_skip, z, h0))
     B, L, D = x.shape
     N = A.shape[1]
@@ -117,7 +120,7 @@ def scan(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threa
     def fn(c, ys, hs):
         lib.oracle_scan(B, L, D, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
                         _ptr(D_skip), _ptr(z), _ptr(h0), c.ctypes.data, len(c),
-                        ys.ctypes.data, hs.ctypes.data)
+                        ys.ctypes.data, hs.ctypes.data, _ptr(delta_bias), int(bool(delta_softplus)))
 
     y, h = _run_channels(fn, ch, L, N, threads)
     if full:
@@ -125,20 +128,23 @@ def scan(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threa
     return y, h
 
 
-def state_update(state, x, delta, A, Bm, Cm, D_skip=None, z=None):
+def state_update(state, x, delta, A, Bm, Cm, D_skip=None, z=None, delta_bias=None,
+                 delta_softplus=False):
     """One decode step.  state (S, D, N) fp64 is updated in place; returns y (S, D)."""
     lib = _load()
     assert state.dtype == np.float64 and state.flags.c_contiguous
-    x, delta, A, Bm, Cm, D_skip, z = map(_f32, (x, delta, A, Bm, Cm, D_skip, z))
+    x, delta, A, Bm, Cm, D_skip, z, delta_bias = map(_f32, (x, delta, A, Bm, Cm, D_skip, z, delta_bias))
     S, D = x.shape
     N = A.shape[1]
     y = np.empty((S, D), dtype=np.float64)
     lib.oracle_state_update(S, D, N, state.ctypes.data, _ptr(x), _ptr(delta), _ptr(A),
-                            _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z), y.ctypes.data)
+                            _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z), y.ctypes.data,
+                            _ptr(delta_bias), int(bool(delta_softplus)))
     return y
 
 
-def ssd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threads=None):
+def ssd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threads=None,
+        dt_bias=None, dt_softplus=False):
     """Mamba-2 SSD recurrence.
 
     Shapes: x, z (B, L, H, P); dt (B, L, H); A, D_skip (H,); Bm, Cm
@@ -147,7 +153,7 @@ def ssd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threads=N
     indices (b*H + h)*P + p and the result is y (k, L), h_final (k, N).
     """
     lib = _load()
-    x, dt, A, Bm, Cm, D_skip, z, h0 = map(_f32, (x, dt, A, Bm, Cm, D_skip, z, h0))
+    x, dt, A, Bm, Cm, D_skip, z, h0, dt_bias = map(_f32, (x, dt, A, Bm, Cm, D_skip, z, h0, dt_bias))
     B, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
     if H % G != 0:
@@ -159,7 +165,7 @@ def ssd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threads=N
     def fn(c, ys, hs):
         lib.oracle_ssd(B, L, H, P, G, N, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm),
                        _ptr(D_skip), _ptr(z), _ptr(h0), c.ctypes.data, len(c),
-                       ys.ctypes.data, hs.ctypes.data)
+                       ys.ctypes.data, hs.ctypes.data, _ptr(dt_bias), int(bool(dt_softplus)))
 
     y, h = _run_channels(fn, ch, L, N, threads)
     if full:

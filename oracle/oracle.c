@@ -33,6 +33,10 @@
  * - Inputs are not modified and the final state is a separate output: the
  *   llama.cpp page, compilade's note that ggml_ssm_scan no longer modifies its
  *   inputs and returns the final state with its output.
+ * - Optionally the step size is delta + delta_bias[d] (per head for SSD) and
+ *   then softplus(v) = log(1 + e^v): the fused dt-bias/softplus input
+ *   transform of Mamba's scan (the bias is a model tensor on the llama.cpp
+ *   page); off by default.
  * - Decode (single-token state update, Megatron's selective_state_update in
  *   "Clean up SSM ops directory structure - #6444"): the same step with L = 1,
  *   state updated in place.
@@ -74,6 +78,19 @@
 static double silu(double v) { return v / (1.0 + exp(-v)); }
 
 /*
+ * The step size as the scan uses it: delta + delta_bias[c] when a bias is
+ * given, then softplus(v) = log(1 + e^v) when asked (Mamba's dt projection
+ * bias and softplus; the bias tensor exists as a model tensor on the
+ * llama.cpp page).  Both off: delta unchanged.
+ */
+static double step_size(double v, const float *delta_bias, int64_t c, int softplus)
+{
+    if (delta_bias) v += (double)delta_bias[c];
+    if (softplus) v = v > 30.0 ? v : log1p(exp(v));
+    return v;
+}
+
+/*
  * Mamba-1 selective scan for channels c = b*D + d listed in `channels`.
  * D_skip, z and h0 may be NULL (no skip term, no gate, zero initial state).
  */
@@ -82,7 +99,8 @@ void oracle_scan(int64_t B, int64_t L, int64_t D, int64_t N,
                  const float *Bm, const float *Cm, const float *D_skip,
                  const float *z, const float *h0,
                  const int64_t *channels, int64_t n_channels,
-                 double *y_out, double *h_out)
+                 double *y_out, double *h_out,
+                 const float *delta_bias, int delta_softplus)
 {
     (void)B;
     for (int64_t k = 0; k < n_channels; ++k) {
@@ -94,7 +112,7 @@ void oracle_scan(int64_t B, int64_t L, int64_t D, int64_t N,
 
         for (int64_t t = 0; t < L; ++t) {
             const int64_t row = b * L + t;           /* token (b, t) */
-            const double dl = delta[row * D + d];
+            const double dl = step_size(delta[row * D + d], delta_bias, d, delta_softplus);
             const double u = x[row * D + d];
             double acc = 0.0;
             for (int64_t n = 0; n < N; ++n) {
@@ -118,12 +136,13 @@ void oracle_scan(int64_t B, int64_t L, int64_t D, int64_t N,
 void oracle_state_update(int64_t S, int64_t D, int64_t N, double *state,
                          const float *x, const float *delta, const float *A,
                          const float *Bm, const float *Cm, const float *D_skip,
-                         const float *z, double *y)
+                         const float *z, double *y,
+                         const float *delta_bias, int delta_softplus)
 {
     for (int64_t s = 0; s < S; ++s) {
         for (int64_t d = 0; d < D; ++d) {
             double *h = state + (s * D + d) * N;
-            const double dl = delta[s * D + d];
+            const double dl = step_size(delta[s * D + d], delta_bias, d, delta_softplus);
             const double u = x[s * D + d];
             double acc = 0.0;
             for (int64_t n = 0; n < N; ++n) {
@@ -149,7 +168,8 @@ void oracle_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N
                 const float *Bm, const float *Cm, const float *D_skip,
                 const float *z, const float *h0,
                 const int64_t *channels, int64_t n_channels,
-                double *y_out, double *h_out)
+                double *y_out, double *h_out,
+                const float *dt_bias, int dt_softplus)
 {
     (void)B;
     const int64_t heads_per_group = H / G;
@@ -165,7 +185,7 @@ void oracle_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N
 
         for (int64_t t = 0; t < L; ++t) {
             const int64_t tok = b * L + t;
-            const double dl = dt[tok * H + hd];
+            const double dl = step_size(dt[tok * H + hd], dt_bias, hd, dt_softplus);
             const double u = x[(tok * H + hd) * P + p];
             const double dA = exp(dl * (double)A[hd]);
             double acc = 0.0;
