@@ -88,6 +88,19 @@ typedef struct {
     int32_t reserved[5]; /* must be zero */
 } ssm_tuning;
 
+/* Optional transform of the step size before it enters the recurrence:
+ * delta' = delta + bias[c] (bias may be NULL), then softplus(delta') =
+ * log(1 + e^delta') when softplus == 1 -- Mamba's dt-projection bias and
+ * softplus fused into the scan (the bias exists as a model tensor on the
+ * llama.cpp page, [ggml#6758]).  c is the channel d for the Mamba-1 scan and
+ * decode step, the head h for SSD.  Tokens past the end of a sequence are not
+ * affected.  NULL options = delta used as given. */
+typedef struct {
+    const float *bias;   /* device pointer: (D) fp32, (H) for SSD; or NULL */
+    int32_t softplus;    /* 0 or 1 */
+    int32_t reserved[3]; /* must be zero */
+} ssm_delta_opts;
+
 /* Largest N the Mamba-1 kernels (scan and decode) are built for. */
 #define SSM_SCAN_MAX_N 64
 /* Largest N the SSD kernels are built for, and the supported head dim P. */
@@ -131,6 +144,16 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
                         void *workspace, size_t workspace_bytes,
                         const ssm_tuning *tuning, void *stream);
 
+/* ssm_scan_fwd with the step-size transform of ssm_delta_opts (NULL = none).
+ * The bias must not overlap y or h_final. */
+ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                           const void *x, const void *delta, const float *A,
+                           const void *Bm, const void *Cm, const float *D_skip,
+                           const void *z, const float *h0, void *y, float *h_final,
+                           void *workspace, size_t workspace_bytes,
+                           const ssm_tuning *tuning, const ssm_delta_opts *dopts,
+                           void *stream);
+
 /* Device workspace ssm_scan_fwd needs for these sizes and tuning (bytes). */
 size_t ssm_scan_fwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N,
                                    const ssm_tuning *tuning);
@@ -150,6 +173,13 @@ ssm_status ssm_state_update(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
                             const float *A, const void *Bm, const void *Cm,
                             const float *D_skip, const void *z, void *y,
                             void *stream);
+
+/* ssm_state_update with the step-size transform of ssm_delta_opts. */
+ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
+                               float *state, const void *x, const void *delta,
+                               const float *A, const void *Bm, const void *Cm,
+                               const float *D_skip, const void *z, void *y,
+                               const ssm_delta_opts *dopts, void *stream);
 
 /*
  * ssm_ssd_fwd -- Mamba-2 state-space-duality (SSD) chunked scan
@@ -177,6 +207,15 @@ ssm_status ssm_ssd_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                        const void *Cm, const float *D_skip, const void *z,
                        const float *h0, void *y, float *h_final,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ssm_ssd_fwd with the step-size transform of ssm_delta_opts (bias per head). */
+ssm_status ssm_ssd_fwd_ex(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                          int64_t N, int64_t chunk, ssm_dtype dt, const void *x,
+                          const void *dt_in, const float *A, const void *Bm,
+                          const void *Cm, const float *D_skip, const void *z,
+                          const float *h0, void *y, float *h_final,
+                          void *workspace, size_t workspace_bytes,
+                          const ssm_delta_opts *dopts, void *stream);
 
 size_t ssm_ssd_fwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P,
                                   int64_t G, int64_t N, int64_t chunk);

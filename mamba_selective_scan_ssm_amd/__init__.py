@@ -37,6 +37,18 @@ class Tuning(ctypes.Structure):
                 ("states_per_lane", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
+class DeltaOpts(ctypes.Structure):
+    """ssm_delta_opts: step size delta + bias, then softplus (optional)."""
+    _fields_ = [("bias", ctypes.c_void_p), ("softplus", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
+
+
+def _dopts(bias, softplus):
+    if bias is None and not softplus:
+        return None
+    return ctypes.byref(DeltaOpts(None if bias is None else bias.data_ptr(), 1 if softplus else 0))
+
+
 _lib = None
 
 
@@ -58,6 +70,12 @@ def lib():
         L.ssm_ssd_fwd.restype = ctypes.c_int
         L.ssm_ssd_fwd_workspace_size.argtypes = [i64] * 7
         L.ssm_ssd_fwd_workspace_size.restype = sz
+        L.ssm_scan_fwd_ex.argtypes = [i64, i64, i64, i64, ctypes.c_int] + [vp] * 10 + [vp, sz, vp, vp, vp]
+        L.ssm_scan_fwd_ex.restype = ctypes.c_int
+        L.ssm_state_update_ex.argtypes = [i64, i64, i64, ctypes.c_int] + [vp] * 9 + [vp, vp]
+        L.ssm_state_update_ex.restype = ctypes.c_int
+        L.ssm_ssd_fwd_ex.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 10 + [vp, sz, vp, vp]
+        L.ssm_ssd_fwd_ex.restype = ctypes.c_int
         L.ssm_conv1d_fwd.argtypes = [i64] * 4 + [ctypes.c_int] + [vp] * 4 + [ctypes.c_int32, vp, vp, vp]
         L.ssm_conv1d_fwd.restype = ctypes.c_int
         L.ssm_conv1d_update.argtypes = [i64] * 3 + [ctypes.c_int] + [vp] * 4 + [ctypes.c_int32, vp, vp]
@@ -109,11 +127,13 @@ def _call(fn_name, *args):
 
 
 def scan_fwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, y=None, h_final=None,
-             return_final=True, variant=0, chunk_len=0, states_per_lane=0, workspace=None):
+             return_final=True, variant=0, chunk_len=0, states_per_lane=0, workspace=None,
+             delta_bias=None, delta_softplus=False):
     """Mamba-1 selective scan (ssm_scan_fwd).
 
     x, delta, z: (B, L, D); Bm, Cm: (B, L, N), all float32 or all bfloat16;
     A: (D, N) float32; D_skip: (D,) float32; h0: (B, D, N) float32.
+    delta_bias: (D,) float32 added to delta, then softplus if delta_softplus.
     Returns (y, h_final); y has the input dtype, h_final is float32.
     """
     if x.dim() != 3 or Bm.dim() != 3:
@@ -130,6 +150,7 @@ def scan_fwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, y=None, h_fin
     _check("A", A, (D, N), torch.float32, dev)
     _check("D_skip", D_skip, (D,), torch.float32, dev)
     _check("h0", h0, (B, D, N), torch.float32, dev)
+    _check("delta_bias", delta_bias, (D,), torch.float32, dev)
     if y is None:
         y = torch.empty((B, L, D), dtype=dt, device=dev)
     _check("y", y, (B, L, D), dt, dev)
@@ -141,9 +162,9 @@ def scan_fwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, y=None, h_fin
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("ssm_scan_fwd", B, L, D, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+    _call("ssm_scan_fwd_ex", B, L, D, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
           _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), ws_len,
-          ctypes.byref(tun), _stream(dev))
+          ctypes.byref(tun), _dopts(delta_bias, delta_softplus), _stream(dev))
     return y, h_final
 
 
@@ -152,7 +173,8 @@ def scan_fwd_workspace_size(B, L, D, N, variant=0, chunk_len=0, states_per_lane=
     return int(lib().ssm_scan_fwd_workspace_size(B, L, D, N, ctypes.byref(t)))
 
 
-def state_update(state, x, delta, A, Bm, Cm, D_skip=None, z=None, *, y=None):
+def state_update(state, x, delta, A, Bm, Cm, D_skip=None, z=None, *, y=None, delta_bias=None,
+                 delta_softplus=False):
     """One decode step (ssm_state_update); `state` (S, D, N) float32 is updated in place.
 
     x, delta, z: (S, D); Bm, Cm: (S, N) float32 or bfloat16.  Returns y (S, D).
@@ -167,20 +189,22 @@ def state_update(state, x, delta, A, Bm, Cm, D_skip=None, z=None, *, y=None):
     _check("Cm", Cm, (S, N), dt, dev)
     _check("A", A, (D, N), torch.float32, dev)
     _check("D_skip", D_skip, (D,), torch.float32, dev)
+    _check("delta_bias", delta_bias, (D,), torch.float32, dev)
     if y is None:
         y = torch.empty((S, D), dtype=dt, device=dev)
     _check("y", y, (S, D), dt, dev)
-    _call("ssm_state_update", S, D, N, code, _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
-          _ptr(Cm), _ptr(D_skip), _ptr(z), _ptr(y), _stream(dev))
+    _call("ssm_state_update_ex", S, D, N, code, _ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
+          _ptr(Cm), _ptr(D_skip), _ptr(z), _ptr(y), _dopts(delta_bias, delta_softplus), _stream(dev))
     return y
 
 
 def ssd_fwd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, *, chunk=256, y=None, h_final=None,
-            return_final=True, workspace=None):
+            return_final=True, workspace=None, dt_bias=None, dt_softplus=False):
     """Mamba-2 SSD chunked scan (ssm_ssd_fwd).
 
     x, z: (B, L, H, P); dt: (B, L, H); Bm, Cm: (B, L, G, N) bfloat16;
-    A, D_skip: (H,) float32; h0: (B, H, P, N) float32.  Returns (y, h_final).
+    A, D_skip: (H,) float32; h0: (B, H, P, N) float32.  dt_bias: (H,)
+    float32 added to dt, then softplus if dt_softplus.  Returns (y, h_final).
     """
     B, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
@@ -194,6 +218,7 @@ def ssd_fwd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, *, chunk=256, y=None
     _check("A", A, (H,), torch.float32, dev)
     _check("D_skip", D_skip, (H,), torch.float32, dev)
     _check("h0", h0, (B, H, P, N), torch.float32, dev)
+    _check("dt_bias", dt_bias, (H,), torch.float32, dev)
     if y is None:
         y = torch.empty((B, L, H, P), dtype=typ, device=dev)
     _check("y", y, (B, L, H, P), typ, dev)
@@ -204,9 +229,9 @@ def ssd_fwd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, *, chunk=256, y=None
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("ssm_ssd_fwd", B, L, H, P, G, N, chunk, code, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm),
+    _call("ssm_ssd_fwd_ex", B, L, H, P, G, N, chunk, code, _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm),
           _ptr(Cm), _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace),
-          ws_len, _stream(dev))
+          ws_len, _dopts(dt_bias, dt_softplus), _stream(dev))
     return y, h_final
 
 

@@ -50,6 +50,15 @@ bool tuning_ok(const ssm_tuning *t) {
 
 int spl_of(const ssm_tuning *t) { return t ? t->states_per_lane : 0; }
 
+bool dopts_ok(const ssm_delta_opts *o) {
+  if (!o) return true;
+  for (int i = 0; i < 3; ++i)
+    if (o->reserved[i] != 0) return false;
+  return o->softplus == 0 || o->softplus == 1;
+}
+const float *dbias_of(const ssm_delta_opts *o) { return o ? o->bias : nullptr; }
+bool dsoft_of(const ssm_delta_opts *o) { return o && o->softplus == 1; }
+
 // Variant choice: a function of (L, D, N) only, so a sequence's result does
 // not depend on the batch it is in.  Sequential when one sequence already
 // brings enough 64-channel waves or L is short; otherwise chunked with
@@ -160,8 +169,17 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
                         const float *D_skip, const void *z, const float *h0, void *y,
                         float *h_final, void *workspace, size_t workspace_bytes,
                         const ssm_tuning *tuning, void *stream) {
+  return ssm_scan_fwd_ex(B, L, D, N, dt, x, delta, A, Bm, Cm, D_skip, z, h0, y, h_final, workspace,
+                         workspace_bytes, tuning, nullptr, stream);
+}
+
+ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt, const void *x,
+                           const void *delta, const float *A, const void *Bm, const void *Cm,
+                           const float *D_skip, const void *z, const float *h0, void *y,
+                           float *h_final, void *workspace, size_t workspace_bytes,
+                           const ssm_tuning *tuning, const ssm_delta_opts *dopts, void *stream) {
   if (B < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_INVALID_ARG;
-  if (!valid_dtype(dt) || !tuning_ok(tuning)) return SSM_ERR_INVALID_ARG;
+  if (!valid_dtype(dt) || !tuning_ok(tuning) || !dopts_ok(dopts)) return SSM_ERR_INVALID_ARG;
   if (N > SSM_SCAN_MAX_N) return SSM_ERR_UNSUPPORTED;
   if (B == 0 || D == 0) return SSM_OK;
   if (B > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
@@ -174,7 +192,8 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
   if (L > 0 && N > 0 && (!Bm || !Cm)) return SSM_ERR_INVALID_ARG;
   if (N > 0 && !A) return SSM_ERR_INVALID_ARG;
   const Range ins[] = {{x, nBLD * es},   {delta, nBLD * es}, {A, D * N * 4}, {Bm, nBLN * es},
-                       {Cm, nBLN * es},  {D_skip, D * 4},    {z, nBLD * es}, {h0, nBDN * 4}};
+                       {Cm, nBLN * es},  {D_skip, D * 4},    {z, nBLD * es}, {h0, nBDN * 4},
+                       {dbias_of(dopts), D * 4}};
   if (overlaps_any(Range{y, nBLD * es}, ins)) return SSM_ERR_INVALID_ARG;
   if (overlaps_any(Range{h_final, nBDN * 4}, ins)) return SSM_ERR_INVALID_ARG;
   if (overlap(Range{y, nBLD * es}, Range{h_final, nBDN * 4})) return SSM_ERR_INVALID_ARG;
@@ -184,6 +203,7 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
   a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
   a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
   a.D_skip = D_skip; a.z = z; a.h0 = h0; a.y = y; a.h_final = h_final;
+  a.delta_bias = dbias_of(dopts); a.delta_softplus = dsoft_of(dopts);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const Plan p = plan_scan(L, D, tuning);
@@ -214,7 +234,14 @@ ssm_status ssm_state_update(int64_t S, int64_t D, int64_t N, ssm_dtype dt, float
                             const void *x, const void *delta, const float *A, const void *Bm,
                             const void *Cm, const float *D_skip, const void *z, void *y,
                             void *stream) {
-  if (S < 0 || D < 0 || N < 0 || !valid_dtype(dt)) return SSM_ERR_INVALID_ARG;
+  return ssm_state_update_ex(S, D, N, dt, state, x, delta, A, Bm, Cm, D_skip, z, y, nullptr, stream);
+}
+
+ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt, float *state,
+                               const void *x, const void *delta, const float *A, const void *Bm,
+                               const void *Cm, const float *D_skip, const void *z, void *y,
+                               const ssm_delta_opts *dopts, void *stream) {
+  if (S < 0 || D < 0 || N < 0 || !valid_dtype(dt) || !dopts_ok(dopts)) return SSM_ERR_INVALID_ARG;
   if (N > SSM_SCAN_MAX_N) return SSM_ERR_UNSUPPORTED;
   if (S == 0 || D == 0) return SSM_OK;
   if (S > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
@@ -222,7 +249,8 @@ ssm_status ssm_state_update(int64_t S, int64_t D, int64_t N, ssm_dtype dt, float
   if (N > 0 && (!state || !A || !Bm || !Cm)) return SSM_ERR_INVALID_ARG;
   const int64_t es = esize(dt);
   const Range ins[] = {{x, S * D * es},  {delta, S * D * es}, {A, D * N * 4}, {Bm, S * N * es},
-                       {Cm, S * N * es}, {D_skip, D * 4},     {z, S * D * es}};
+                       {Cm, S * N * es}, {D_skip, D * 4},     {z, S * D * es},
+                       {dbias_of(dopts), D * 4}};
   const Range st{state, S * D * N * 4};
   if (overlaps_any(Range{y, S * D * es}, ins) || overlap(Range{y, S * D * es}, st))
     return SSM_ERR_INVALID_ARG;
@@ -233,6 +261,7 @@ ssm_status ssm_state_update(int64_t S, int64_t D, int64_t N, ssm_dtype dt, float
   a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
   a.state = state; a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
   a.D_skip = D_skip; a.z = z; a.y = y;
+  a.delta_bias = dbias_of(dopts); a.delta_softplus = dsoft_of(dopts);
   // The vectorised step needs 16-byte aligned state and A rows.
   const bool aligned = (reinterpret_cast<uintptr_t>(state) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(A) % 16 == 0);
@@ -251,7 +280,17 @@ ssm_status ssm_ssd_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, in
                        const float *A, const void *Bm, const void *Cm, const float *D_skip,
                        const void *z, const float *h0, void *y, float *h_final, void *workspace,
                        size_t workspace_bytes, void *stream) {
-  if (B < 0 || L < 0 || H < 0 || P < 0 || G < 0 || N < 0 || chunk < 0 || !valid_dtype(dt))
+  return ssm_ssd_fwd_ex(B, L, H, P, G, N, chunk, dt, x, dt_in, A, Bm, Cm, D_skip, z, h0, y, h_final,
+                        workspace, workspace_bytes, nullptr, stream);
+}
+
+ssm_status ssm_ssd_fwd_ex(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                          int64_t chunk, ssm_dtype dt, const void *x, const void *dt_in,
+                          const float *A, const void *Bm, const void *Cm, const float *D_skip,
+                          const void *z, const float *h0, void *y, float *h_final, void *workspace,
+                          size_t workspace_bytes, const ssm_delta_opts *dopts, void *stream) {
+  if (B < 0 || L < 0 || H < 0 || P < 0 || G < 0 || N < 0 || chunk < 0 || !valid_dtype(dt) ||
+      !dopts_ok(dopts))
     return SSM_ERR_INVALID_ARG;
   if (dt != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (P != 64 || N % 32 != 0 || N > SSM_SSD_MAX_N || N == 0) return SSM_ERR_UNSUPPORTED;
@@ -265,7 +304,8 @@ ssm_status ssm_ssd_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, in
   const int64_t es = 2;
   const int64_t nX = B * L * H * P, nB = B * L * G * N, nS = B * H * P * N;
   const Range ins[] = {{x, nX * es},  {dt_in, B * L * H * es}, {A, H * 4},  {Bm, nB * es},
-                       {Cm, nB * es}, {D_skip, H * 4},         {z, nX * es}, {h0, nS * 4}};
+                       {Cm, nB * es}, {D_skip, H * 4},         {z, nX * es}, {h0, nS * 4},
+                       {dbias_of(dopts), H * 4}};
   if (overlaps_any(Range{y, nX * es}, ins)) return SSM_ERR_INVALID_ARG;
   if (overlaps_any(Range{h_final, nS * 4}, ins)) return SSM_ERR_INVALID_ARG;
   if (overlap(Range{y, nX * es}, Range{h_final, nS * 4})) return SSM_ERR_INVALID_ARG;
@@ -282,6 +322,7 @@ ssm_status ssm_ssd_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, in
   a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N; a.chunk = chunk;
   a.x = x; a.dt = dt_in; a.A = A; a.Bm = Bm; a.Cm = Cm; a.D_skip = D_skip; a.z = z;
   a.h0 = h0; a.y = y; a.h_final = h_final;
+  a.dt_bias = dbias_of(dopts); a.dt_softplus = dsoft_of(dopts);
   return hip_status(ssm::launch_ssd(a, workspace, static_cast<hipStream_t>(stream)));
 }
 

@@ -41,4 +41,22 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Step size as the recurrence uses it: delta + bias, then (if asked)
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).  log1p(w) is
+// log(1 + w) corrected for the rounding of 1 + w: log(u) * w / (u - 1) with
+// u = 1 + w (or w itself when u rounds to 1), which stays accurate for the
+// small w of large |v|.
+__device__ __forceinline__ float step_size(float v, float bias, bool softplus) {
+  v += bias;
+  if (softplus) {
+    constexpr float kLn2 = 0.6931471805599453f;
+    const float w = fast_exp2(-fabsf(v) * kLog2e);
+    const float u = 1.0f + w;
+    const float um1 = u - 1.0f;
+    const float lp = um1 == 0.f ? w : __builtin_amdgcn_logf(u) * kLn2 * (w / um1);
+    v = fmaxf(v, 0.f) + lp;
+  }
+  return v;
+}
+
 }  // namespace ssm

@@ -20,6 +20,8 @@ struct ScanArgs {
   const float *h0;
   void *y;
   float *h_final;
+  const float *delta_bias;  // (D) or null: added to delta
+  bool delta_softplus;      // softplus of (delta + bias)
 };
 
 // Channel-sequential scan: a workgroup per (b, 64 channels), its waves
@@ -55,6 +57,8 @@ struct StepArgs {
   const void *z;
   void *y;
   bool vec_ok;  // state and A rows 16-byte aligned: vectorised lanes allowed
+  const float *delta_bias;  // (D) or null
+  bool delta_softplus;
 };
 
 hipError_t launch_state_update(const StepArgs &a, hipStream_t s);
@@ -69,6 +73,8 @@ struct SSDArgs {
   const float *h0;
   void *y;
   float *h_final;
+  const float *dt_bias;  // (H) or null: added to dt
+  bool dt_softplus;      // softplus of (dt + bias)
 };
 
 // Short causal convolution.  Prefill: x, y (B, L, D); state_in/state_out

@@ -166,6 +166,8 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_
   const Plane<T> pb(static_cast<const char *>(a.Bm) + b * bcplane, bcplane);
   const Plane<T> pc(static_cast<const char *>(a.Cm) + b * bcplane, bcplane);
   const float Dd = (a.D_skip != nullptr) ? a.D_skip[d] : 0.f;
+  const float dbias = a.delta_bias ? a.delta_bias[d] : 0.f;
+  const bool dsoft = a.delta_softplus;
 
   // This thread's share of a block's B/C values: entry e = tid + i*64W of
   // [which][token j][n] (n padded to kNP), read from (b, t, n) of B or C.
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_
     for (int i = 0; i < kTokPerThread; ++i) {
       const int j = wave + i * W;
       const bool ok = jb + j < ntok;
-      const float dl = ok ? to_f32(r.d[i]) : 0.f;
+      const float dl = ok ? step_size(to_f32(r.d[i]), dbias, dsoft) : 0.f;
       const float xv = ok ? to_f32(r.x[i]) : 0.f;
       s_du[b2][j][lane] = make_float2(dl, dl * xv);
       if (kY) {
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   const uint32_t row_bytes = static_cast<uint32_t>(D * kES);
   int rr[kPairs], pp[kPairs];
   uint32_t vo[kPairs], vo_st[kPairs];
-  float Dd[kPairs][2];
+  float Dd[kPairs][2], Db[kPairs][2];
 #pragma unroll
   for (int m = 0; m < kPairs; ++m) {
     const int e = lane + 64 * m;
@@ -443,7 +445,10 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
     vo_st[m] = on ? vo[m] : 0x80000000u;
     Dd[m][0] = a.D_skip ? a.D_skip[dpc] : 0.f;
     Dd[m][1] = a.D_skip ? a.D_skip[dpc + 1] : 0.f;
+    Db[m][0] = a.delta_bias ? a.delta_bias[dpc] : 0.f;
+    Db[m][1] = a.delta_bias ? a.delta_bias[dpc + 1] : 0.f;
   }
+  const bool dsoft = a.delta_softplus;
   auto rsrc = [&](const void *p, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(p)), 0,
                                              static_cast<int>(bytes), kRsrcWord3);
@@ -509,7 +514,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const float xv = word_elem<T>(w.x[u][m], hh);
-          const float dv = ok ? word_elem<T>(w.d[u][m], hh) : 0.f;
+          const float dv = ok ? step_size(word_elem<T>(w.d[u][m], hh), Db[m][hh], dsoft) : 0.f;
           du[2 * hh] = dv;
           du[2 * hh + 1] = dv * xv;
         }
@@ -687,8 +692,9 @@ __global__ __launch_bounds__(kWave) void scan_lane_kernel(ScanArgs a) {
   const T *zp = a.z ? static_cast<const T *>(a.z) + b * L * D + d : nullptr;
   T *yp = static_cast<T *>(a.y) + b * L * D + d;
   const float Dd = a.D_skip ? a.D_skip[d] : 0.f;
+  const float dbias = a.delta_bias ? a.delta_bias[d] : 0.f;
   for (int64_t t = 0; t < L; ++t) {
-    const float dl = to_f32(dp[t * D]);
+    const float dl = step_size(to_f32(dp[t * D]), dbias, a.delta_softplus);
     const float xv = to_f32(xp[t * D]);
     const float u = dl * xv;
     float acc0 = 0.f, acc1 = 0.f;

@@ -125,7 +125,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(SSDArgs a, fl
   const uint16_t *dtp = static_cast<const uint16_t *>(a.dt);
   const float A2 = a.A[h] * kLog2e;
   float dtv = 0.f;
-  if (tid < nvalid) dtv = bf_to_f(bf16_bits(dtp[(b * L + t0 + tid) * H + h]));
+  if (tid < nvalid)
+    dtv = step_size(bf_to_f(bf16_bits(dtp[(b * L + t0 + tid) * H + h])), a.dt_bias ? a.dt_bias[h] : 0.f,
+                    a.dt_softplus);
   block_inclusive_scan(dtv * A2, s_S, s_wave, Q);
   const float S_end = s_S[Q - 1];
   if (tid < Q) s_w[tid] = fast_exp2(S_end - s_S[tid]) * dtv;
@@ -354,7 +356,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * lane + e;
-        pdt[e] = j < nvalid ? bf_to_f(bf16_bits(dtp[(b * L + t0 + j) * H + h])) : 0.f;
+        pdt[e] = j < nvalid ? step_size(bf_to_f(bf16_bits(dtp[(b * L + t0 + j) * H + h])),
+                                        a.dt_bias ? a.dt_bias[h] : 0.f, a.dt_softplus)
+                            : 0.f;
       }
     }
   };
@@ -525,7 +529,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_scan_head_kernel(SSDArgs a
   const uint16_t *dtp = static_cast<const uint16_t *>(a.dt);
   const float A2 = a.A[h] * kLog2e;
   float dtv = 0.f;
-  if (tid < nvalid) dtv = bf_to_f(bf16_bits(dtp[(b * L + t0 + tid) * H + h]));
+  if (tid < nvalid)
+    dtv = step_size(bf_to_f(bf16_bits(dtp[(b * L + t0 + tid) * H + h])), a.dt_bias ? a.dt_bias[h] : 0.f,
+                    a.dt_softplus);
   if (tid < Q) s_dt[tid] = dtv;
   block_inclusive_scan(dtv * A2, s_S, s_wave, Q);
 

@@ -35,7 +35,8 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
   const float4 Av = reinterpret_cast<const float4 *>(a.A + d * N)[q];
   const T *Bt = static_cast<const T *>(a.Bm) + s * N + 4 * q;
   const T *Ct = static_cast<const T *>(a.Cm) + s * N + 4 * q;
-  const float dl = to_f32(static_cast<const T *>(a.delta)[s * D + d]);
+  const float dl = step_size(to_f32(static_cast<const T *>(a.delta)[s * D + d]),
+                             a.delta_bias ? a.delta_bias[d] : 0.f, a.delta_softplus);
   const float xv = to_f32(static_cast<const T *>(a.x)[s * D + d]);
   const float u = dl * xv;
 
@@ -97,6 +98,8 @@ hipError_t launch_dt(const StepArgs &a, hipStream_t st) {
   sa.h0 = a.state;
   sa.y = a.y;
   sa.h_final = a.state;
+  sa.delta_bias = a.delta_bias;
+  sa.delta_softplus = a.delta_softplus;
   return launch_scan_lane(sa, st);
 }
 

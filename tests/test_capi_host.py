@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ssm_scan_fwd", "ssm_scan_fwd_workspace_size", "ssm_state_update", "ssm_ssd_fwd",
               "ssm_ssd_fwd_workspace_size", "ssm_conv1d_fwd", "ssm_conv1d_update",
+              "ssm_scan_fwd_ex", "ssm_state_update_ex", "ssm_ssd_fwd_ex",
               "ssm_status_string", "ssm_version"):
         assert n in names
 
@@ -200,3 +201,19 @@ def test_conv_update_validation(lib):
     assert conv_upd(lib, state=None) == INVALID
     assert conv_upd(lib, y=P[0]) == INVALID              # y on the state
     assert conv_upd(lib, x=P[0]) == INVALID              # x on the state
+
+
+def test_delta_opts_validation(lib):
+    """The step-size options are checked on the host like every argument."""
+    def scan_ex(opts, **over):
+        p = dict(x=P[0], delta=P[1], A=P[2], Bm=P[3], Cm=P[4], D_skip=P[5], z=P[6], h0=P[7], y=P[8],
+                 h_final=P[9])
+        p.update(over)
+        return lib.ssm_scan_fwd_ex(2, 8, 64, 16, F32, p["x"], p["delta"], p["A"], p["Bm"], p["Cm"],
+                                   p["D_skip"], p["z"], p["h0"], p["y"], p["h_final"], None, 0,
+                                   None, ctypes.byref(opts) if opts is not None else None, None)
+    assert scan_ex(ssm.DeltaOpts(None, 2)) == INVALID                 # softplus must be 0/1
+    o = ssm.DeltaOpts(None, 1)
+    o.reserved[1] = 5
+    assert scan_ex(o) == INVALID                                       # reserved must be zero
+    assert scan_ex(ssm.DeltaOpts(P[8].value, 1)) == INVALID           # bias on y
