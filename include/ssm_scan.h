@@ -34,8 +34,10 @@
  * [megatron#6444] "Clean up SSM ops directory structure - #6444": the decode
  *              op selective_state_update, the Mamba-2 state-space-duality
  *              kernels ssd_bmm, ssd_chunk_state, ssd_state_passing,
- *              ssd_chunk_scan, ssd_combined, and the short causal
- *              convolution's causal_conv1d_update.
+ *              ssd_chunk_scan, ssd_combined, the short causal
+ *              convolution's causal_conv1d_update, the slot-indexed state
+ *              gather/scatter (intermediate_extraction) and the
+ *              batch-invariant decode.
  * [fastllm#333] "Tensor-parallel SSM #333": head groups (repeat_interleave of
  *              groups to heads) for Mamba-2.
  * [mixer2-tp]  "Current Implementation of TP in MambaMixer2": the number of
@@ -180,6 +182,33 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
                                const float *A, const void *Bm, const void *Cm,
                                const float *D_skip, const void *z, void *y,
                                const ssm_delta_opts *dopts, void *stream);
+
+/*
+ * ssm_decode_steps -- T decode tokens for each of S sequences whose states
+ * live in a pool of rows (the slot-indexed state gather/scatter of prefix
+ * caching, intermediate_extraction, and the batch-invariant decode of
+ * [megatron#6444]).  Sequence s reads and writes the state row
+ * slot_idx[s] of state_pool IN PLACE; each of its T tokens goes through the
+ * ssm_state_update step in order, so T = 1 is one decode step and T > 1
+ * saves T - 1 launches.  A sequence's results do not depend on which other
+ * sequences share the call.
+ *
+ * state_pool : (pool_rows, D, N) fp32, in/out
+ * slot_idx   : (S) int32 DEVICE array, or NULL for slot s = s (then
+ *              pool_rows >= S).  Slots outside [0, pool_rows) skip the
+ *              sequence (its y rows are not written).  Non-negative slots must
+ *              be distinct: two sequences on one row race.
+ * x, delta, z, y : (S, T, D) dtype `dt`;  Bm, Cm : (S, T, N) dtype `dt`
+ * A : (D, N) fp32;  D_skip : (D) or NULL;  z may be NULL;  dopts as
+ * ssm_scan_fwd_ex.  y must not overlap the inputs or the pool; the pool must
+ * not overlap the inputs.  Sizes as ssm_scan_fwd with L = T.
+ */
+ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtype dt,
+                            float *state_pool, int64_t pool_rows, const int32_t *slot_idx,
+                            const void *x, const void *delta, const float *A,
+                            const void *Bm, const void *Cm, const float *D_skip,
+                            const void *z, void *y, const ssm_delta_opts *dopts,
+                            void *stream);
 
 /*
  * ssm_ssd_fwd -- Mamba-2 state-space-duality (SSD) chunked scan

@@ -76,6 +76,8 @@ def lib():
         L.ssm_state_update_ex.restype = ctypes.c_int
         L.ssm_ssd_fwd_ex.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 10 + [vp, sz, vp, vp]
         L.ssm_ssd_fwd_ex.restype = ctypes.c_int
+        L.ssm_decode_steps.argtypes = [i64] * 4 + [ctypes.c_int, vp, i64, vp] + [vp] * 8 + [vp, vp]
+        L.ssm_decode_steps.restype = ctypes.c_int
         L.ssm_conv1d_fwd.argtypes = [i64] * 4 + [ctypes.c_int] + [vp] * 4 + [ctypes.c_int32, vp, vp, vp]
         L.ssm_conv1d_fwd.restype = ctypes.c_int
         L.ssm_conv1d_update.argtypes = [i64] * 3 + [ctypes.c_int] + [vp] * 4 + [ctypes.c_int32, vp, vp]
@@ -297,4 +299,36 @@ def conv1d_update(state, x, w, bias=None, *, activation="silu", y=None):
     _check("y", y, (S, D), dt, dev)
     _call("ssm_conv1d_update", S, D, K, code, _ptr(state), _ptr(x), _ptr(w), _ptr(bias),
           _act_code(activation), _ptr(y), _stream(dev))
+    return y
+
+
+def decode_steps(state_pool, x, delta, A, Bm, Cm, D_skip=None, z=None, *, slots=None, y=None,
+                 delta_bias=None, delta_softplus=False):
+    """T decode tokens for S sequences whose states are rows of a pool
+    (ssm_decode_steps).  state_pool (P, D, N) float32 is updated in place;
+    x, delta, z: (S, T, D); Bm, Cm: (S, T, N); slots: (S,) int32 device tensor
+    of pool rows (None: row s for sequence s; negative: skip).  Returns y."""
+    if x.dim() != 3:
+        raise ValueError("x must be (S, T, D)")
+    S, T, D = x.shape
+    Pr, Dp, N = state_pool.shape
+    if Dp != D:
+        raise ValueError("state_pool must be (pool_rows, D, N)")
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _check("state_pool", state_pool, (Pr, D, N), torch.float32, dev)
+    for nm, t in (("x", x), ("delta", delta), ("z", z)):
+        _check(nm, t, (S, T, D), dt, dev)
+    _check("Bm", Bm, (S, T, N), dt, dev)
+    _check("Cm", Cm, (S, T, N), dt, dev)
+    _check("A", A, (D, N), torch.float32, dev)
+    _check("D_skip", D_skip, (D,), torch.float32, dev)
+    _check("delta_bias", delta_bias, (D,), torch.float32, dev)
+    _check("slots", slots, (S,), torch.int32, dev)
+    if y is None:
+        y = torch.empty((S, T, D), dtype=dt, device=dev)
+    _check("y", y, (S, T, D), dt, dev)
+    _call("ssm_decode_steps", S, T, D, N, code, _ptr(state_pool), Pr, _ptr(slots), _ptr(x),
+          _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z), _ptr(y),
+          _dopts(delta_bias, delta_softplus), _stream(dev))
     return y

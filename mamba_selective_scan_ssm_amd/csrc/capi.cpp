@@ -269,6 +269,57 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt, fl
   return hip_status(ssm::launch_state_update(a, static_cast<hipStream_t>(stream)));
 }
 
+ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtype dt,
+                            float *state_pool, int64_t pool_rows, const int32_t *slot_idx,
+                            const void *x, const void *delta, const float *A, const void *Bm,
+                            const void *Cm, const float *D_skip, const void *z, void *y,
+                            const ssm_delta_opts *dopts, void *stream) {
+  if (S < 0 || T < 0 || D < 0 || N < 0 || pool_rows < 0 || !valid_dtype(dt) || !dopts_ok(dopts))
+    return SSM_ERR_INVALID_ARG;
+  if (N > SSM_SCAN_MAX_N) return SSM_ERR_UNSUPPORTED;
+  if (S == 0 || D == 0 || T == 0) return SSM_OK;
+  if (S > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  if (slot_idx == nullptr && pool_rows < S) return SSM_ERR_INVALID_ARG;
+  const int64_t es = esize(dt);
+  if ((T + 64) * D * es >= (int64_t(1) << 31) || (T + 64) * N * es >= (int64_t(1) << 31))
+    return SSM_ERR_UNSUPPORTED;
+  if (!x || !delta || !y) return SSM_ERR_INVALID_ARG;
+  if (N > 0 && (!state_pool || !A || !Bm || !Cm)) return SSM_ERR_INVALID_ARG;
+  const int64_t nX = S * T * D, nBC = S * T * N;
+  const Range ins[] = {{x, nX * es},    {delta, nX * es},  {A, D * N * 4}, {Bm, nBC * es},
+                       {Cm, nBC * es},  {D_skip, D * 4},   {z, nX * es},   {slot_idx, S * 4},
+                       {dbias_of(dopts), D * 4}};
+  const Range pool{state_pool, pool_rows * D * N * 4};
+  if (overlaps_any(Range{y, nX * es}, ins) || overlap(Range{y, nX * es}, pool))
+    return SSM_ERR_INVALID_ARG;
+  if (overlaps_any(pool, ins)) return SSM_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 1) {
+    ssm::StepArgs a{};
+    a.S = S; a.D = D; a.N = N;
+    a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
+    a.state = state_pool; a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
+    a.D_skip = D_skip; a.z = z; a.y = y;
+    a.delta_bias = dbias_of(dopts); a.delta_softplus = dsoft_of(dopts);
+    a.slots = slot_idx; a.pool_rows = pool_rows;
+    a.vec_ok = (reinterpret_cast<uintptr_t>(state_pool) % 16 == 0) &&
+               (reinterpret_cast<uintptr_t>(A) % 16 == 0);
+    return hip_status(ssm::launch_state_update(a, s));
+  }
+  // T tokens: the channel-sequential scan with the pool rows as both initial
+  // and final state (each lane reads its state elements before writing them)
+  ssm::ScanArgs a{};
+  a.B = S; a.L = T; a.D = D; a.N = N;
+  a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
+  a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
+  a.D_skip = D_skip; a.z = z; a.h0 = state_pool; a.y = y; a.h_final = state_pool;
+  a.delta_bias = dbias_of(dopts); a.delta_softplus = dsoft_of(dopts);
+  a.slots = slot_idx; a.pool_rows = pool_rows;
+  if (N == 0) return hip_status(ssm::launch_scan_lane(a, s));
+  if (ssm::scan_lanesplit_supported(a)) return hip_status(ssm::launch_scan_lanesplit(a, s));
+  return hip_status(ssm::launch_scan_sequential(a, 0, s));
+}
+
 size_t ssm_ssd_fwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                                   int64_t N, int64_t chunk) {
   if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk <= 0) return 0;

@@ -22,7 +22,22 @@ struct ScanArgs {
   float *h_final;
   const float *delta_bias;  // (D) or null: added to delta
   bool delta_softplus;      // softplus of (delta + bias)
+  // Optional state-row indirection (decode of a slot pool): sequence b reads
+  // h0 and writes h_final at row slots[b] of a pool of pool_rows rows; a slot
+  // outside [0, pool_rows) skips the sequence.  Sequential schedules only.
+  const int32_t *slots;
+  int64_t pool_rows;
 };
+
+// State row of sequence b (false: skip the sequence).
+__device__ __forceinline__ bool scan_state_row(const ScanArgs &a, int64_t b, int64_t &row) {
+  row = b;
+  if (a.slots == nullptr) return true;
+  const int32_t sl = a.slots[b];
+  if (sl < 0 || sl >= a.pool_rows) return false;
+  row = sl;
+  return true;
+}
 
 // Channel-sequential scan: a workgroup per (b, 64 channels), its waves
 // splitting N, one pass over the L tokens.  spl_req = requested states per
@@ -59,6 +74,8 @@ struct StepArgs {
   bool vec_ok;  // state and A rows 16-byte aligned: vectorised lanes allowed
   const float *delta_bias;  // (D) or null
   bool delta_softplus;
+  const int32_t *slots;     // as ScanArgs: state row of sequence s, or null
+  int64_t pool_rows;
 };
 
 hipError_t launch_state_update(const StepArgs &a, hipStream_t s);

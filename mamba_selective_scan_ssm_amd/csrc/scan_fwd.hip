@@ -135,6 +135,8 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_
   const bool active = d_raw < D;
   const int64_t d = active ? d_raw : D - 1;
   const int64_t seg = blockIdx.y, nseg = gridDim.y, b = blockIdx.z;
+  int64_t hrow;  // state row of sequence b
+  if (!scan_state_row(a, b, hrow)) return;  // uniform over the workgroup, before any barrier
   const int64_t t0 = seg * seg_len;
   const int64_t t1 = (t0 + seg_len < L) ? t0 + seg_len : L;
   const int64_t nblk = (t1 - t0 + TB - 1) / TB;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_
     const bool ok = n < N;
     A2[s] = ok ? a.A[d * N + n] * kLog2e : 0.f;
     float v = 0.f;
-    if (ok && MODE == kFull && a.h0 != nullptr) v = a.h0[(b * D + d) * N + n];
+    if (ok && MODE == kFull && a.h0 != nullptr) v = a.h0[(hrow * D + d) * N + n];
     if (ok && MODE == kOutput) v = seg_h[ws_row + n];
     h[s] = v;
   }
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(kWave *W) void scan_split_kernel(ScanArgs a, int64_
   for (int s = 0; s < SPL; ++s) {
     const int n = n0 + s;
     if (n < N) {
-      if (MODE == kFull && a.h_final != nullptr) a.h_final[(b * D + d) * N + n] = h[s];
+      if (MODE == kFull && a.h_final != nullptr) a.h_final[(hrow * D + d) * N + n] = h[s];
       if (MODE == kSummary) {
         seg_a[ws_row + n] = fast_exp2(A2[s] * dsum);
         seg_h[ws_row + n] = h[s];
@@ -408,6 +410,8 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t d0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * kCPW;  // first channel of the wave
   const int64_t b = blockIdx.z;
+  int64_t hrow;  // state row of sequence b
+  if (!scan_state_row(a, b, hrow)) return;
 
   // compute role: channel c, state slice q
   const int c = lane / LPC, q = lane % LPC;
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   float A2[SPL], h[SPL];
   {
     const float *Ap = a.A + dc * kN + q * SPL;
-    const float *hp = a.h0 ? a.h0 + (b * D + dc) * kN + q * SPL : nullptr;
+    const float *hp = a.h0 ? a.h0 + (hrow * D + dc) * kN + q * SPL : nullptr;
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
       A2[s] = Ap[s] * kLog2e;
@@ -627,7 +631,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   if (ncyc > 0) store_cycle(cyc - 1);
 
   if (d0 + c >= D || a.h_final == nullptr) return;
-  float *hf = a.h_final + (b * D + dc) * kN + q * SPL;
+  float *hf = a.h_final + (hrow * D + dc) * kN + q * SPL;
 #pragma unroll
   for (int s = 0; s < SPL; ++s) hf[s] = h[s];
 }
@@ -670,13 +674,15 @@ __global__ __launch_bounds__(kWave) void scan_lane_kernel(ScanArgs a) {
   const bool active = d_raw < D;
   const int64_t d = active ? d_raw : D - 1;
   const int64_t b = blockIdx.z;
+  int64_t hrow;  // state row of sequence b
+  if (!scan_state_row(a, b, hrow)) return;
 
   float A2[NB], h[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     const bool ok = EXACT || n < N;
     A2[n] = ok ? a.A[d * N + n] * kLog2e : 0.f;
-    h[n] = (ok && a.h0 != nullptr) ? a.h0[(b * D + d) * N + n] : 0.f;
+    h[n] = (ok && a.h0 != nullptr) ? a.h0[(hrow * D + d) * N + n] : 0.f;
   }
   // B/C rows are the same for every lane: scalar loads of the raw bits
   using Bits = typename std::conditional<sizeof(T) == 2, uint16_t, float>::type;
@@ -716,7 +722,7 @@ __global__ __launch_bounds__(kWave) void scan_lane_kernel(ScanArgs a) {
   if (!active || a.h_final == nullptr) return;
 #pragma unroll
   for (int n = 0; n < NB; ++n)
-    if (EXACT || n < N) a.h_final[(b * D + d) * N + n] = h[n];
+    if (EXACT || n < N) a.h_final[(hrow * D + d) * N + n] = h[n];
 }
 
 // ---------------------------------------------------------------------------

@@ -27,10 +27,16 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
   const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kCh + threadIdx.x / LPC;
   const int64_t s = blockIdx.y;
   const int64_t D = a.D;
+  int64_t row = s;  // state row of sequence s
+  if (a.slots != nullptr) {
+    const int32_t sl = a.slots[s];
+    if (sl < 0 || sl >= a.pool_rows) return;  // uniform over the block
+    row = sl;
+  }
   const bool active = d_raw < D;
   const int64_t d = active ? d_raw : D - 1;
 
-  float4 *st = reinterpret_cast<float4 *>(a.state + (s * D + d) * N) + q;
+  float4 *st = reinterpret_cast<float4 *>(a.state + (row * D + d) * N) + q;
   const float4 hv = *st;
   const float4 Av = reinterpret_cast<const float4 *>(a.A + d * N)[q];
   const T *Bt = static_cast<const T *>(a.Bm) + s * N + 4 * q;
@@ -100,6 +106,8 @@ hipError_t launch_dt(const StepArgs &a, hipStream_t st) {
   sa.h_final = a.state;
   sa.delta_bias = a.delta_bias;
   sa.delta_softplus = a.delta_softplus;
+  sa.slots = a.slots;
+  sa.pool_rows = a.pool_rows;
   return launch_scan_lane(sa, st);
 }
 

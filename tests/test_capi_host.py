@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ssm_scan_fwd", "ssm_scan_fwd_workspace_size", "ssm_state_update", "ssm_ssd_fwd",
               "ssm_ssd_fwd_workspace_size", "ssm_conv1d_fwd", "ssm_conv1d_update",
-              "ssm_scan_fwd_ex", "ssm_state_update_ex", "ssm_ssd_fwd_ex",
+              "ssm_scan_fwd_ex", "ssm_state_update_ex", "ssm_ssd_fwd_ex", "ssm_decode_steps",
               "ssm_status_string", "ssm_version"):
         assert n in names
 
@@ -217,3 +217,19 @@ def test_delta_opts_validation(lib):
     o.reserved[1] = 5
     assert scan_ex(o) == INVALID                                       # reserved must be zero
     assert scan_ex(ssm.DeltaOpts(P[8].value, 1)) == INVALID           # bias on y
+
+
+def test_decode_steps_validation(lib):
+    def ds(S=4, T=3, D=64, N=16, pool=8, slots=None, **over):
+        p = dict(pool=P[0], x=P[1], delta=P[2], A=P[3], Bm=P[4], Cm=P[5], D_skip=P[6], z=P[7], y=P[8])
+        p.update(over)
+        return lib.ssm_decode_steps(S, T, D, N, F32, p["pool"], pool, slots, p["x"], p["delta"], p["A"],
+                                    p["Bm"], p["Cm"], p["D_skip"], p["z"], p["y"], None, None)
+    assert ds(S=-1) == INVALID
+    assert ds(pool=-1) == INVALID
+    assert ds(N=65) == UNSUPPORTED
+    assert ds(T=0) == OK and ds(S=0) == OK
+    assert ds(pool=2) == INVALID                  # identity slots need pool_rows >= S
+    assert ds(y=P[1]) == INVALID                  # y on x
+    assert ds(pool=8, y=P[0]) == INVALID          # y inside the pool
+    assert ds(x=None) == INVALID
