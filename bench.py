@@ -45,28 +45,43 @@ SCAN_VALU_PER_ELEM, SCAN_TRANS_PER_ELEM, SCAN_FLOPS_PER_ELEM = 4, 1, 6
 SCAN_ELEM_PEAK = 1.0 / (SCAN_VALU_PER_ELEM / VALU_LANE_OPS + SCAN_TRANS_PER_ELEM / TRANS_LANE_OPS)
 
 
-def csrc_hash() -> str:
+# the kernel sources behind each measured entry point: counters taken on
+# other sources are not reported
+_COMMON = ["launch.h", "device_common.h"]
+KERNEL_SOURCES = {
+    "scan_fwd": ["scan_fwd.hip"] + _COMMON,
+    "state_update": ["state_update.hip"] + _COMMON,
+    "ssd_fwd": ["ssd.hip"] + _COMMON,
+    "conv1d_fwd": ["conv1d.hip"] + _COMMON,
+    "conv1d_update": ["conv1d.hip"] + _COMMON,
+    "decode_steps_T1": ["state_update.hip"] + _COMMON,
+    "decode_steps_T4": ["scan_fwd.hip"] + _COMMON,
+}
+
+
+def csrc_hash(entry: str) -> str:
+    """sha256 (first 16 hex digits) over the kernel sources of an entry."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "mamba_selective_scan_ssm_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in sorted(KERNEL_SOURCES[entry]):
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, launch_bytes_alg: float):
-    """HBM bytes per launch from committed rocprofv3 --pmc runs, if they were
-    taken on the current kernel sources; else None."""
+def load_traffic(entry: str, field: str = "bytes_per_launch"):
+    """HBM bytes per launch (or per call) from the committed rocprofv3 --pmc
+    runs, if they were taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         with open(p) as f:
             t = json.load(f)
-        e = t.get(kernel)
-        if not e or e.get("csrc_hash") != csrc_hash():
+        e = t.get(entry)
+        if not e or e.get("csrc_hash") != csrc_hash(entry):
             return None
-        return float(e["bytes_per_launch"])
+        return float(e[field])
     except (OSError, ValueError, KeyError):
         return None
 
@@ -140,11 +155,28 @@ def bench_decode(torch, ssm, gen, steps_meas=128):
 
     mean_ms, min_ms, wall_ms = time_calls(one, steps_meas, 8, torch)
     alg = S * D * N * 4 * 2 + S * D * 2 * 4 + 2 * S * N * 2 + D * N * 4 + D * 4
+    # the 84 MB state fits the 256 MB last-level (Infinity) cache; a model
+    # steps one such state per layer, so also time six states used in turn
+    # (504 MB), as six layers of one decode step would
+    states = [state.clone() for _ in range(6)]
+    it2 = [0]
+
+    def rotated():
+        i = it2[0]
+        it2[0] += 1
+        t = (i // 6) % dec.steps
+        ssm.state_update(states[i % 6], xs[t], ds[t], A, bs[t], cs[t], Ds, zs[t], y=y)
+
+    rot_ms, _, _ = time_calls(rotated, steps_meas, 12, torch)
+    del states
     return {"workload": "decode_256x5120_bf16 (S=256, D=5120, N=16, bf16, fp32 state)",
             "kernel_ms_per_step": mean_ms, "wall_ms_per_step": wall_ms,
             "Gelem_per_s": S * D * N / (mean_ms * 1e-3) / 1e9,
             "alg_bytes_per_step": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
-            "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic_bytes_per_step": load_traffic("state_update"),
+            "six_states_in_turn": {"kernel_ms_per_step": rot_ms, "hbm_GBs": alg / (rot_ms * 1e-3) / 1e9,
+                                   "hbm_frac": alg / (rot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
 def bench_ssd(torch, ssm, gen, steps=10):
@@ -174,7 +206,8 @@ def bench_ssd(torch, ssm, gen, steps=10):
             "alg_bytes": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
             "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "dense_gemm_TFLOPs": flops / (mean_ms * 1e-3) / 1e12,
-            "mfma_frac_bf16": flops / (mean_ms * 1e-3) / 2.5e15, "workspace_bytes": ws_n}
+            "mfma_frac_bf16": flops / (mean_ms * 1e-3) / 2.5e15, "workspace_bytes": ws_n,
+            "traffic_bytes": load_traffic("ssd_fwd", "bytes_per_call")}
 
 
 def bench_conv(torch, ssm, gen, steps=50):
@@ -193,7 +226,8 @@ def bench_conv(torch, ssm, gen, steps=50):
     alg = B * L * D * 2 * 2 + D * K * 4 + D * 4 + 2 * B * D * (K - 1) * 4
     out = {"workload": "conv_mamba2p8b_bf16 (B=8, L=4096, D=5120, K=4, bf16, SiLU)",
            "ms": mean_ms, "alg_bytes": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
-           "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+           "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "traffic_bytes": load_traffic("conv1d_fwd", "bytes_per_call")}
     d = gen.make_workload("conv_decode_256x5120_bf16")
     S, Dd, Kd = d.S, d.D, d.K
     state = upload(d.state0, torch)
@@ -212,7 +246,38 @@ def bench_conv(torch, ssm, gen, steps=50):
     out["decode"] = {"workload": "conv_decode_256x5120_bf16 (S=256, D=5120, K=4)",
                      "kernel_ms_per_step": dm, "wall_ms_per_step": dwall, "alg_bytes_per_step": dalg,
                      "hbm_GBs": dalg / (dm * 1e-3) / 1e9,
-                     "hbm_frac": dalg / (dm * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                     "hbm_frac": dalg / (dm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic_bytes_per_step": load_traffic("conv1d_update", "bytes_per_call")}
+    return out
+
+
+def bench_pool_decode(torch, ssm, gen, steps=128):
+    """Decode from a state pool (ssm_decode_steps): 256 sequences on scattered
+    rows of a 512-row pool; one token per call, then 4 tokens per call."""
+    w = gen.make_workload("pool_decode_256x5120_bf16")
+    tk = w.tokens
+    S, T, D, N = tk.B, tk.L, tk.D, tk.N
+    pool = upload(w.pool, torch)
+    slots = torch.from_numpy(w.slots).cuda()
+    t = {k: upload(getattr(tk, k), torch) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds = upload(tk.A, torch), upload(tk.D_skip, torch)
+    out = {"workload": f"pool_decode_256x5120_bf16 (S={S}, D={D}, N={N}, pool {w.pool.shape[0]} rows, "
+                       "scattered slots, bf16, fp32 state)"}
+    for tt in (1, T):
+        tok = {k: v[:, :tt].contiguous() for k, v in t.items()}
+        y = torch.empty((S, tt, D), dtype=torch.bfloat16, device="cuda")
+
+        def one():
+            ssm.decode_steps(pool, tok["x"], tok["delta"], A, tok["Bm"], tok["Cm"], Ds, tok["z"],
+                             slots=slots, y=y)
+
+        ms, _, wall = time_calls(one, steps, 8, torch)
+        alg = S * D * N * 4 * 2 + S * tt * D * 2 * 4 + 2 * S * tt * N * 2 + D * N * 4 + D * 4 + S * 4
+        out[f"T{tt}"] = {"kernel_ms_per_call": ms, "wall_ms_per_call": wall, "tokens_per_call": S * tt,
+                         "alg_bytes_per_call": alg, "hbm_GBs": alg / (ms * 1e-3) / 1e9,
+                         "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "us_per_token_step": ms * 1e3 / tt,
+                         "traffic_bytes_per_call": load_traffic(f"decode_steps_T{tt}", "bytes_per_call")}
     return out
 
 
@@ -224,7 +289,7 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the decode and SSD rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=8)
-    ap.add_argument("--only", choices=["scan", "decode", "ssd", "conv"], default=None,
+    ap.add_argument("--only", choices=["scan", "decode", "ssd", "conv", "pool"], default=None,
                     help="time one hot-path entry point only (for profiling); prints its row")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) so a "
@@ -252,6 +317,9 @@ def main():
     if args.only == "ssd":
         print(json.dumps({"ssd": bench_ssd(torch, ssm, gen, steps=args.steps)}))
         return
+    if args.only == "pool":
+        print(json.dumps({"pool_decode": bench_pool_decode(torch, ssm, gen, steps=args.steps)}))
+        return
     if args.only == "conv":
         print(json.dumps({"conv": bench_conv(torch, ssm, gen, steps=args.steps)}))
         return
@@ -277,7 +345,7 @@ def main():
     kern_s = mean_ms * 1e-3
     hbm_gbs = alg / kern_s / 1e9
     elem_rate = elems / kern_s
-    traffic = load_traffic("scan_fwd", alg)
+    traffic = load_traffic("scan_fwd")
     roofline = {
         "bound": "alu",
         "achieved": elem_rate * SCAN_FLOPS_PER_ELEM / 1e12,
@@ -306,7 +374,7 @@ def main():
     }
     if not args.no_rows and args.only is None:
         out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen, steps=20),
-                       "conv": bench_conv(torch, ssm, gen)}
+                       "conv": bench_conv(torch, ssm, gen), "pool_decode": bench_pool_decode(torch, ssm, gen)}
     if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
     print(json.dumps(out))

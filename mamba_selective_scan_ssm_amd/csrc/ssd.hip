@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(int64_t B, int64_t 
 // ---------------------------------------------------------------------------
 // 3. chunk outputs
 // ---------------------------------------------------------------------------
-// One workgroup of 8 waves per (chunk, group), looping over the group's
+// One workgroup of 16 waves per (chunk, group), looping over the group's
 // heads.  The chunk's B rows are staged in LDS once (row-major, as the
 // A-operand of CB^T = B C^T needs them) and each wave keeps the C fragments
 // of its row blocks in registers, so CB^T is recomputed per head from
@@ -255,8 +255,10 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(int64_t B, int64_t 
 // and row block I (rows i), one 32-wide p tile:
 //   Y_I = exp(S_i) C_I h_in^T + sum_{J <= I} M_IJ X_J,
 //   M_IJ[i][j] = CB^T[j][i] exp(S_i - S_j) dt_j (j <= i),
-// on the matrix cores with M formed in registers.  With 8 row blocks, wave w
-// takes blocks 7 - w%4 and w%4 of p tile w/4: 9 (I, J) blocks per wave.
+// on the matrix cores with M formed in registers.  Each wave owns one row
+// block and one p tile; with 8 row blocks (Q = 256) the four waves that share
+// a SIMD take blocks s and 7 - s of both p tiles, so every SIMD does the same
+// 18 (I, J) blocks.
 constexpr int kQPad = 256 + 8;
 constexpr int kScanThreads = 1024;
 

@@ -305,7 +305,26 @@ WORKLOADS = {
     # its decode step: 256 sequences, 128 single-token steps
     "conv_decode_256x5120_bf16": dict(kind="conv_decode", S=256, D=5120, K=4, steps=128,
                                       dtype="bf16", seed=1006),
+    # decode from a state pool: 256 sequences on scattered rows of a 512-row
+    # pool, 4 tokens each (prefix-cached serving; T = 1 is one decode step)
+    "pool_decode_256x5120_bf16": dict(kind="pool_decode", S=256, T=4, D=5120, N=16, pool_rows=512,
+                                      dtype="bf16", seed=1007),
 }
+
+
+@dataclasses.dataclass
+class PoolDecodeInputs:
+    tokens: ScanInputs      # (S, T, .) per-sequence tokens; tokens.h0 is None
+    pool: np.ndarray        # fp32 (pool_rows, D, N) state pool
+    slots: np.ndarray       # int32 (S,) distinct pool rows, scattered
+
+
+def make_pool_decode(S, T, D, N, pool_rows, *, dtype="bf16", seed=0) -> PoolDecodeInputs:
+    tok = make_scan(S, T, D, N, dtype=dtype, seed=seed, h0=False)
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(len(_STREAMS) + 1)[-1])
+    pool = _normal(rng, (pool_rows, D, N), std=0.5)
+    slots = rng.permutation(pool_rows)[:S].astype(np.int32)
+    return PoolDecodeInputs(tok, pool, slots)
 
 
 def make_workload(name: str, **overrides):
@@ -323,6 +342,9 @@ def make_workload(name: str, **overrides):
                         dtype=w["dtype"], seed=w["seed"], gate=w["gate"], h0=w.get("h0", True))
     if kind == "conv":
         return make_conv(w["B"], w["L"], w["D"], w["K"], dtype=w["dtype"], seed=w["seed"])
+    if kind == "pool_decode":
+        return make_pool_decode(w["S"], w["T"], w["D"], w["N"], w["pool_rows"], dtype=w["dtype"],
+                                seed=w["seed"])
     if kind == "conv_decode":
         return make_conv_decode(w["S"], w["D"], w["K"], w["steps"], dtype=w["dtype"], seed=w["seed"])
     raise ValueError(kind)

@@ -127,15 +127,18 @@ def test_batch_invariance(T):
 
 
 @pytest.mark.parametrize("T", [1, 4])
-def test_decode_256x5120_pool_sampled(oracle_mod, T):
-    """The decode workload's size (256 sequences, D=5120, N=16, bf16) on a pool
-    of 512 rows with scattered slots; y and the written rows checked on
-    sampled channels, untouched rows checked whole."""
-    S, D, N, P = 256, 5120, 16, 512
-    inp = gen.make_scan(S, T, D, N, dtype="bf16", seed=740 + T)
-    pool_np = _pool(P, D, N, 741)
-    slots = np.random.default_rng(742).permutation(P)[:S].astype(np.int32)
-    _say("decode_steps 256x5120 pool 512", T)
+def test_pool_decode_256x5120_sampled(oracle_mod, T):
+    """The timed pool-decode workload (256 sequences on scattered rows of a
+    512-row pool, D=5120, N=16, bf16) at T = 1 and T = 4 tokens per call; y and
+    the written rows checked on sampled channels, untouched rows whole."""
+    w = gen.make_workload("pool_decode_256x5120_bf16")
+    cut = lambda t: gen.Tensor(np.ascontiguousarray(t.f32[:, :T]),
+                               None if t.bf16 is None else np.ascontiguousarray(t.bf16[:, :T]))
+    inp = dataclasses.replace(w.tokens, L=T, **{k: cut(getattr(w.tokens, k))
+                                                for k in ("x", "delta", "Bm", "Cm", "z")})
+    S, D, P = inp.B, inp.D, w.pool.shape[0]
+    slots, pool_np = w.slots, w.pool
+    _say("pool_decode_256x5120_bf16", T)
     y, pool = _run(inp, pool_np, slots.tolist())
     rng = np.random.default_rng(743)
     ch = np.unique(np.concatenate([rng.integers(0, S * D, 160), [0, D - 1, S * D - 1]]))

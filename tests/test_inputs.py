@@ -50,3 +50,12 @@ def test_workload_shapes():
     assert d.x.shape == (5, 3, 8) and d.Bm.shape == (5, 3, 16) and d.state0.shape == (3, 8, 16)
     q = gen.make_ssd(1, 16, 4, 2, 2, 8, chunk=8)
     assert q.x.shape == (1, 16, 4, 2) and q.dt.shape == (1, 16, 4) and q.Bm.shape == (1, 16, 2, 8)
+
+
+def test_pool_decode_slots_distinct_and_in_range():
+    p = gen.make_pool_decode(6, 3, 8, 4, 10, seed=5)
+    assert p.tokens.x.shape == (6, 3, 8) and p.tokens.h0 is None and p.pool.shape == (10, 8, 4)
+    assert p.slots.dtype == np.int32 and len(set(p.slots.tolist())) == 6
+    assert p.slots.min() >= 0 and p.slots.max() < 10
+    q = gen.make_pool_decode(6, 3, 8, 4, 10, seed=5)
+    assert np.array_equal(p.slots, q.slots) and np.array_equal(p.pool, q.pool)
