@@ -55,7 +55,8 @@ KERNEL_SOURCES = {
     "conv1d_fwd": ["conv1d.hip"] + _COMMON,
     "conv1d_update": ["conv1d.hip"] + _COMMON,
     "decode_steps_T1": ["state_update.hip"] + _COMMON,
-    "decode_steps_T4": ["scan_fwd.hip"] + _COMMON,
+    "decode_steps_T4": ["state_update.hip"] + _COMMON,
+    "decode_steps_T16": ["state_update.hip"] + _COMMON,
 }
 
 
@@ -253,7 +254,7 @@ def bench_conv(torch, ssm, gen, steps=50):
 
 def bench_pool_decode(torch, ssm, gen, steps=128):
     """Decode from a state pool (ssm_decode_steps): 256 sequences on scattered
-    rows of a 512-row pool; one token per call, then 4 tokens per call."""
+    rows of a 512-row pool; 1, 4 and 16 tokens per call."""
     w = gen.make_workload("pool_decode_256x5120_bf16")
     tk = w.tokens
     S, T, D, N = tk.B, tk.L, tk.D, tk.N
@@ -263,7 +264,7 @@ def bench_pool_decode(torch, ssm, gen, steps=128):
     A, Ds = upload(tk.A, torch), upload(tk.D_skip, torch)
     out = {"workload": f"pool_decode_256x5120_bf16 (S={S}, D={D}, N={N}, pool {w.pool.shape[0]} rows, "
                        "scattered slots, bf16, fp32 state)"}
-    for tt in (1, T):
+    for tt in (1, 4, T):
         tok = {k: v[:, :tt].contiguous() for k, v in t.items()}
         y = torch.empty((S, tt, D), dtype=torch.bfloat16, device="cuda")
 

@@ -188,10 +188,13 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
  * live in a pool of rows (the slot-indexed state gather/scatter of prefix
  * caching, intermediate_extraction, and the batch-invariant decode of
  * [megatron#6444]).  Sequence s reads and writes the state row
- * slot_idx[s] of state_pool IN PLACE; each of its T tokens goes through the
- * ssm_state_update step in order, so T = 1 is one decode step and T > 1
- * saves T - 1 launches.  A sequence's results do not depend on which other
- * sequences share the call.
+ * slot_idx[s] of state_pool IN PLACE; its T tokens go through the decode
+ * step in order with the state kept on chip between them, so T = 1 is one
+ * decode step and T > 1 reads and writes the state once for T tokens.  For
+ * T <= 16 the results are bitwise those of T successive ssm_state_update
+ * calls; longer calls run the prefill scan's kernels (bitwise ssm_scan_fwd
+ * with tuning variant 1 and h0 = h_final = the gathered rows).  A sequence's
+ * results do not depend on which other sequences share the call.
  *
  * state_pool : (pool_rows, D, N) fp32, in/out
  * slot_idx   : (S) int32 DEVICE array, or NULL for slot s = s (then

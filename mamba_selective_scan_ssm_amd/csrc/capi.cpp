@@ -257,7 +257,7 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt, fl
   if (overlaps_any(st, ins)) return SSM_ERR_INVALID_ARG;
 
   ssm::StepArgs a{};
-  a.S = S; a.D = D; a.N = N;
+  a.S = S; a.D = D; a.N = N; a.T = 1;
   a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
   a.state = state; a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
   a.D_skip = D_skip; a.z = z; a.y = y;
@@ -268,6 +268,11 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt, fl
   a.vec_ok = aligned;
   return hip_status(ssm::launch_state_update(a, static_cast<hipStream_t>(stream)));
 }
+
+// up to this many tokens per sequence a decode call runs the decode-step
+// kernel; longer calls run the prefill scan kernels (the choice depends on T
+// only, so a sequence's results do not depend on the other sequences)
+constexpr int64_t kDecodeLoopMaxT = 16;
 
 ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtype dt,
                             float *state_pool, int64_t pool_rows, const int32_t *slot_idx,
@@ -294,9 +299,10 @@ ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtyp
     return SSM_ERR_INVALID_ARG;
   if (overlaps_any(pool, ins)) return SSM_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (T == 1) {
+  if (T <= kDecodeLoopMaxT) {
+    // the decode-step kernel, state carried in registers over the T tokens
     ssm::StepArgs a{};
-    a.S = S; a.D = D; a.N = N;
+    a.S = S; a.D = D; a.N = N; a.T = T;
     a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
     a.state = state_pool; a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
     a.D_skip = D_skip; a.z = z; a.y = y;
@@ -306,8 +312,9 @@ ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtyp
                (reinterpret_cast<uintptr_t>(A) % 16 == 0);
     return hip_status(ssm::launch_state_update(a, s));
   }
-  // T tokens: the channel-sequential scan with the pool rows as both initial
-  // and final state (each lane reads its state elements before writing them)
+  // longer runs: the channel-sequential scan with the pool rows as both
+  // initial and final state (each lane reads its state elements before
+  // writing them)
   ssm::ScanArgs a{};
   a.B = S; a.L = T; a.D = D; a.N = N;
   a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;

@@ -63,6 +63,7 @@ hipError_t launch_scan_lane(const ScanArgs &a, hipStream_t s);
 
 struct StepArgs {
   int64_t S, D, N;
+  int64_t T;  // tokens per sequence (>= 1); inputs (S, T, D) and (S, T, N)
   DType dt;
   float *state;
   const void *x, *delta;

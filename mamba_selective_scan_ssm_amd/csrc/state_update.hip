@@ -1,6 +1,7 @@
-// Single-token decode step (selective_state_update in "Clean up SSM ops
-// directory structure - #6444"): the scan body with L = 1 and the state
-// (S, D, N) fp32 read and written in place.
+// Decode step (selective_state_update in "Clean up SSM ops directory
+// structure - #6444"): the scan body for T >= 1 tokens per sequence with the
+// state (S or pool rows, D, N) fp32 read once, carried in registers over the
+// T tokens, and written back in place.
 //
 // The step is HBM-bound on the state (read + write of S*D*N fp32), so the
 // layout is chosen for the state stream: a channel's N states are N/4 lanes
@@ -8,7 +9,7 @@
 // the state tensor contiguously across the wave.  The y contraction over n is
 // finished with a butterfly over those N/4 lanes.  Sizes this layout does not
 // cover (N not a multiple of 4, or a state/A not 16-byte aligned) go to the
-// per-lane scan kernel with L = 1, whose lanes read and then write only their
+// per-lane scan kernel with L = T, whose lanes read and then write only their
 // own state row.
 #include "device_common.h"
 #include "launch.h"
@@ -18,8 +19,9 @@ namespace {
 
 constexpr int kBlock = 256;
 
-// LPC = lanes per channel (N / 4).
-template <typename T, int LPC>
+// LPC = lanes per channel (N / 4).  TT = tokens whose inputs are loaded
+// together before any of them is computed (1 for the single-token step).
+template <typename T, int LPC, int TT>
 __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
   constexpr int N = 4 * LPC;
   constexpr int kCh = kBlock / LPC;  // channels per block
@@ -27,6 +29,7 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
   const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kCh + threadIdx.x / LPC;
   const int64_t s = blockIdx.y;
   const int64_t D = a.D;
+  const int64_t nT = TT == 1 ? 1 : a.T;
   int64_t row = s;  // state row of sequence s
   if (a.slots != nullptr) {
     const int32_t sl = a.slots[s];
@@ -35,44 +38,70 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
   }
   const bool active = d_raw < D;
   const int64_t d = active ? d_raw : D - 1;
+  const T *xp = static_cast<const T *>(a.x);
+  const T *dp = static_cast<const T *>(a.delta);
+  const T *zp = static_cast<const T *>(a.z);
+  const T *Bp = static_cast<const T *>(a.Bm);
+  const T *Cp = static_cast<const T *>(a.Cm);
 
   float4 *st = reinterpret_cast<float4 *>(a.state + (row * D + d) * N) + q;
   const float4 hv = *st;
   const float4 Av = reinterpret_cast<const float4 *>(a.A + d * N)[q];
-  const T *Bt = static_cast<const T *>(a.Bm) + s * N + 4 * q;
-  const T *Ct = static_cast<const T *>(a.Cm) + s * N + 4 * q;
-  const float dl = step_size(to_f32(static_cast<const T *>(a.delta)[s * D + d]),
-                             a.delta_bias ? a.delta_bias[d] : 0.f, a.delta_softplus);
-  const float xv = to_f32(static_cast<const T *>(a.x)[s * D + d]);
-  const float u = dl * xv;
-
+  const float bias = a.delta_bias ? a.delta_bias[d] : 0.f;
   float h[4] = {hv.x, hv.y, hv.z, hv.w};
   const float Ar[4] = {Av.x, Av.y, Av.z, Av.w};
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float dA = fast_exp2(dl * (Ar[j] * kLog2e));
-    h[j] = fmaf(dA, h[j], u * to_f32(Bt[j]));
-    acc = fmaf(to_f32(Ct[j]), h[j], acc);
-  }
-#pragma unroll
-  for (int off = LPC / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPC);
 
+  for (int64_t t0 = 0; t0 < nT; t0 += TT) {
+    // inputs of TT tokens first (indices clamped to the last token, so every
+    // load is in bounds), so their latencies overlap
+    float xv[TT], dv[TT], zv[TT], bv[TT][4], cv[TT][4];
+#pragma unroll
+    for (int k = 0; k < TT; ++k) {
+      const int64_t tok = s * nT + (t0 + k < nT ? t0 + k : nT - 1);  // row of (S, T, .) inputs
+      xv[k] = to_f32(xp[tok * D + d]);
+      dv[k] = to_f32(dp[tok * D + d]);
+      zv[k] = zp ? to_f32(zp[tok * D + d]) : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bv[k][j] = to_f32(Bp[tok * N + 4 * q + j]);
+        cv[k][j] = to_f32(Cp[tok * N + 4 * q + j]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < TT; ++k) {
+      if (t0 + k >= nT) break;
+      const int64_t tok = s * nT + t0 + k;
+      const float dl = step_size(dv[k], bias, a.delta_softplus);
+      const float u = dl * xv[k];
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float dA = fast_exp2(dl * (Ar[j] * kLog2e));
+        h[j] = fmaf(dA, h[j], u * bv[k][j]);
+        acc = fmaf(cv[k][j], h[j], acc);
+      }
+#pragma unroll
+      for (int off = LPC / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPC);
+      if (active && q == 0) {
+        float v = acc;
+        if (a.D_skip) v = fmaf(a.D_skip[d], xv[k], v);
+        if (zp) v *= silu(zv[k]);
+        static_cast<T *>(a.y)[tok * D + d] = from_f32<T>(v);
+      }
+    }
+  }
   if (!active) return;
   *st = make_float4(h[0], h[1], h[2], h[3]);
-  if (q == 0) {
-    float v = acc;
-    if (a.D_skip) v = fmaf(a.D_skip[d], xv, v);
-    if (a.z) v *= silu(to_f32(static_cast<const T *>(a.z)[s * D + d]));
-    static_cast<T *>(a.y)[s * D + d] = from_f32<T>(v);
-  }
 }
 
 template <typename T, int LPC>
 hipError_t launch_t(const StepArgs &a, hipStream_t st) {
   constexpr int kCh = kBlock / LPC;
   dim3 grid(static_cast<unsigned>((a.D + kCh - 1) / kCh), static_cast<unsigned>(a.S));
-  state_update_kernel<T, LPC><<<grid, kBlock, 0, st>>>(a);
+  if (a.T == 1)
+    state_update_kernel<T, LPC, 1><<<grid, kBlock, 0, st>>>(a);
+  else
+    state_update_kernel<T, LPC, 4><<<grid, kBlock, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -86,11 +115,11 @@ hipError_t launch_dt(const StepArgs &a, hipStream_t st) {
     case 64: return launch_t<T, 16>(a, st);
     default: break;
   }
-  // Other N or unaligned rows: the per-lane scan over one token, the state
-  // as both h0 and h_final (each lane reads its row before writing it).
+  // Other N or unaligned rows: the per-lane scan over the T tokens, the
+  // state as both h0 and h_final (each lane reads its row before writing it).
   ScanArgs sa{};
   sa.B = a.S;
-  sa.L = 1;
+  sa.L = a.T;
   sa.D = a.D;
   sa.N = a.N;
   sa.dt = a.dt;

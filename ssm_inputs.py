@@ -306,8 +306,9 @@ WORKLOADS = {
     "conv_decode_256x5120_bf16": dict(kind="conv_decode", S=256, D=5120, K=4, steps=128,
                                       dtype="bf16", seed=1006),
     # decode from a state pool: 256 sequences on scattered rows of a 512-row
-    # pool, 4 tokens each (prefix-cached serving; T = 1 is one decode step)
-    "pool_decode_256x5120_bf16": dict(kind="pool_decode", S=256, T=4, D=5120, N=16, pool_rows=512,
+    # pool, up to 16 tokens each (prefix-cached serving; the first token
+    # alone is one decode step)
+    "pool_decode_256x5120_bf16": dict(kind="pool_decode", S=256, T=16, D=5120, N=16, pool_rows=512,
                                       dtype="bf16", seed=1007),
 }
 

@@ -56,7 +56,7 @@ def _check_against_oracle(oracle_mod, inp, pool_np, slots, y, pool, dtype, **kw)
     assert np.array_equal(pn[untouched], pool_np[untouched].astype(np.float64)), "unnamed pool rows changed"
 
 
-@pytest.mark.parametrize("T", [1, 5, 16])
+@pytest.mark.parametrize("T", [1, 5, 16, 40])   # 40: the prefill kernels' path
 @pytest.mark.parametrize("N,dtype", [(16, "bf16"), (16, "f32"), (5, "f32"), (64, "bf16")])
 def test_slots_permuted_subset(oracle_mod, T, N, dtype):
     S, D, P = 6, 130, 10
@@ -83,32 +83,33 @@ def test_slots_with_delta_transform(oracle_mod, T):
                           delta_softplus=True)
 
 
-@pytest.mark.parametrize("T", [1, 12])
-def test_identity_slots_match_single_call_kernels(T):
-    """slot_idx = NULL is the plain state-update / scan: results are bitwise
-    those of ssm_state_update (T = 1) and ssm_scan_fwd with h0 = h_final = the
-    state (T > 1)."""
+@pytest.mark.parametrize("T,N", [(1, 16), (12, 16), (16, 5), (40, 16), (40, 5)])
+def test_identity_slots_match_single_call_kernels(T, N):
+    """slot_idx = NULL: up to 16 tokens the results are bitwise those of T
+    successive ssm_state_update calls; longer calls bitwise ssm_scan_fwd
+    (variant 1) with h0 = h_final = the state."""
     import mamba_selective_scan_ssm_amd as ssm
-    S, D, N = 5, 320, 16
-    inp = gen.make_scan(S, T, D, N, dtype="bf16", seed=720 + T)
+    S, D = 5, 320
+    inp = gen.make_scan(S, T, D, N, dtype="bf16", seed=720 + T + N)
     pool_np = _pool(S, D, N, 721)
-    _say("decode_steps identity vs single-call kernels", T)
+    _say("decode_steps identity vs single-call kernels", T, N)
     y, pool = _run(inp, pool_np, None)
     st = to_dev(pool_np)
-    if T == 1:
-        ry = ssm.state_update(st, to_dev(inp.x)[:, 0], to_dev(inp.delta)[:, 0], to_dev(inp.A),
-                              to_dev(inp.Bm)[:, 0], to_dev(inp.Cm)[:, 0], to_dev(inp.D_skip),
-                              to_dev(inp.z)[:, 0]).unsqueeze(1)
+    x, dl, Bm, Cm, z = (to_dev(getattr(inp, k)) for k in ("x", "delta", "Bm", "Cm", "z"))
+    A, Ds = to_dev(inp.A), to_dev(inp.D_skip)
+    if T <= 16:
+        ry = torch.stack([ssm.state_update(st, x[:, t].contiguous(), dl[:, t].contiguous(), A,
+                                           Bm[:, t].contiguous(), Cm[:, t].contiguous(), Ds,
+                                           z[:, t].contiguous()) for t in range(T)], 1)
         rh = st
     else:
-        ry, rh = ssm.scan_fwd(to_dev(inp.x), to_dev(inp.delta), to_dev(inp.A), to_dev(inp.Bm),
-                              to_dev(inp.Cm), to_dev(inp.D_skip), to_dev(inp.z), st, variant=1)
+        ry, rh = ssm.scan_fwd(x, dl, A, Bm, Cm, Ds, z, st, variant=1)
     torch.cuda.synchronize()
     assert torch.equal(y, ry)
     assert torch.equal(pool, rh)
 
 
-@pytest.mark.parametrize("T", [1, 6])
+@pytest.mark.parametrize("T", [1, 6, 24])
 def test_batch_invariance(T):
     """A sequence's y and state do not depend on which other sequences share
     the call: run it alone, then among 7 others on other slots."""
@@ -126,10 +127,10 @@ def test_batch_invariance(T):
         assert torch.equal(pool1[slots[s]], pool_all[slots[s]])
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 4, 16])
 def test_pool_decode_256x5120_sampled(oracle_mod, T):
     """The timed pool-decode workload (256 sequences on scattered rows of a
-    512-row pool, D=5120, N=16, bf16) at T = 1 and T = 4 tokens per call; y and
+    512-row pool, D=5120, N=16, bf16) at T = 1, 4 and 16 tokens per call; y and
     the written rows checked on sampled channels, untouched rows whole."""
     w = gen.make_workload("pool_decode_256x5120_bf16")
     cut = lambda t: gen.Tensor(np.ascontiguousarray(t.f32[:, :T]),
