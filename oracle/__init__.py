@@ -47,6 +47,8 @@ def _load():
         i64, fp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
         lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [fp] * 8 + [fp, i64, dp, dp, fp, ctypes.c_int]
         lib.oracle_scan.restype = None
+        lib.oracle_scan_bwd.argtypes = [i64] * 4 + [fp] * 10 + [fp, ctypes.c_int, fp, i64] + [dp] * 9
+        lib.oracle_scan_bwd.restype = None
         lib.oracle_state_update.argtypes = [i64, i64, i64, dp] + [fp] * 7 + [dp, fp, ctypes.c_int]
         lib.oracle_state_update.restype = None
         lib.oracle_ssd.argtypes = [i64] * 6 + [fp] * 8 + [fp, i64, dp, dp, fp, ctypes.c_int]
@@ -126,6 +128,63 @@ def scan(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, channels=None, threa
     if full:
         return y.reshape(B, D, L).transpose(0, 2, 1).copy(), h.reshape(B, D, N)
     return y, h
+
+
+def scan_bwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, dy=None, dh_final=None,
+             delta_bias=None, delta_softplus=False, channels=None, threads=None):
+    """Gradients of ``scan`` for the output gradient dy (B, L, D) and the
+    final-state gradient dh_final (B, D, N) (None = zero).
+
+    Returns a dict of fp64 arrays: dx, ddelta, dz -- (B, L, D), or (k, L) for
+    the k requested ``channels`` (flat b*D + d) -- and dh0 -- (B, D, N) or
+    (k, N); dA (D, N), dD (D,), dbias (D,), dB and dC (B, L, N) summed over
+    the requested channels only (all channels when ``channels`` is None).
+    dz is None without a gate, dD None without D_skip.
+    """
+    lib = _load()
+    x, delta, A, Bm, Cm, dy = map(_f32, (x, delta, A, Bm, Cm, dy))
+    D_skip, z, h0, dh_final, delta_bias = map(_f32, (D_skip, z, h0, dh_final, delta_bias))
+    B, L, D = x.shape
+    N = A.shape[1]
+    full = channels is None
+    ch = np.arange(B * D, dtype=np.int64) if full else np.ascontiguousarray(channels, dtype=np.int64)
+    n = len(ch)
+    threads = max(1, min(threads or default_threads(), max(n, 1)))
+    dx = np.zeros((n, L))
+    ddl = np.zeros((n, L))
+    dz = np.zeros((n, L))
+    dh0 = np.zeros((n, N))
+    bounds = np.linspace(0, n, threads + 1).astype(np.int64)
+    acc = [dict(dA=np.zeros((D, N)), dD=np.zeros(D), dbias=np.zeros(D), dB=np.zeros((B, L, N)),
+                dC=np.zeros((B, L, N))) for _ in range(threads)]
+
+    def work(i):
+        a, b = bounds[i], bounds[i + 1]
+        if b <= a:
+            return
+        c = ch[a:b]
+        r = acc[i]
+        lib.oracle_scan_bwd(B, L, D, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                            _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final),
+                            _ptr(delta_bias), int(bool(delta_softplus)), c.ctypes.data, len(c),
+                            dx[a:b].ctypes.data, ddl[a:b].ctypes.data, dz[a:b].ctypes.data,
+                            dh0[a:b].ctypes.data, r["dA"].ctypes.data, r["dD"].ctypes.data,
+                            r["dbias"].ctypes.data, r["dB"].ctypes.data, r["dC"].ctypes.data)
+
+    if threads == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, range(threads)))
+    out = {k: sum(r[k] for r in acc) for k in ("dA", "dD", "dbias", "dB", "dC")}
+    if full:
+        tr = lambda v: v.reshape(B, D, L).transpose(0, 2, 1).copy()
+        out.update(dx=tr(dx), ddelta=tr(ddl), dz=tr(dz) if z is not None else None, dh0=dh0.reshape(B, D, N))
+    else:
+        out.update(dx=dx, ddelta=ddl, dz=dz if z is not None else None, dh0=dh0)
+    if D_skip is None:
+        out["dD"] = None
+    return out
 
 
 def state_update(state, x, delta, A, Bm, Cm, D_skip=None, z=None, delta_bias=None,

@@ -37,6 +37,11 @@
  *   then softplus(v) = log(1 + e^v): the fused dt-bias/softplus input
  *   transform of Mamba's scan (the bias is a model tensor on the llama.cpp
  *   page); off by default.
+ * - Backward (gradients of the scan): the mamba page's replies on the
+ *   backward kernel -- states recomputed by a forward scan, gradients of the
+ *   states carried by a reverse scan over dy * C, the gradient of the initial
+ *   state dh * exp(delta_0 * A).  The remaining gradients are the chain rule
+ *   through the same recurrence (see oracle_scan_bwd).
  * - Decode (single-token state update, Megatron's selective_state_update in
  *   "Clean up SSM ops directory structure - #6444"): the same step with L = 1,
  *   state updated in place.
@@ -127,6 +132,111 @@ void oracle_scan(int64_t B, int64_t L, int64_t D, int64_t N,
             y_out[k * L + t] = v;
         }
     }
+}
+
+/*
+ * Gradients of oracle_scan (the backward of the mamba page's middle replies:
+ * the forward states are recomputed, then a reverse-time pass carries the
+ * adjoint of the state -- fed by dy * C at every token and decayed by
+ * exp(delta * A) from one token to the one before -- and the gradient of h0
+ * is exp(delta_0 * A) times the adjoint at the first token).
+ *
+ * With u_t = delta_t x_t, a_t = exp(delta_t A), h_t = a_t h_{t-1} + u_t B_t,
+ * q_t = sum_n C_t h_t + D x_t and y_t = q_t silu(z_t), and g_t = dy_t
+ * silu(z_t) the gradient reaching q_t, the adjoint of the state is
+ *   lam_t = g_t C_t + a_{t+1} lam_{t+1},  lam_{L-1} = g C + dh_final,
+ * and per token
+ *   ddelta_t = sum_n lam_t (A a_t h_{t-1} + B_t x_t)   (times the softplus
+ *              slope sigmoid(delta + bias) when softplus is on)
+ *   dx_t     = sum_n lam_t delta_t B_t + D g_t
+ *   dz_t     = dy_t q_t silu'(z_t)
+ *   dB_t    += lam_t delta_t x_t,   dC_t += g_t h_t   (summed over channels)
+ *   dA      += lam_t delta_t a_t h_{t-1},  dD += g_t x_t,  dbias += ddelta_t
+ *   dh0      = a_0 lam_0.
+ * Inputs as oracle_scan, plus dy (B, L, D) and dh_final (B, D, N) (NULL =
+ * zero).  Per requested channel k: dx, ddelta, dz rows at [k * L + t] and
+ * dh0 at [k * N + n] (overwritten); dA (D, N), dD (D), dbias (D), dB and dC
+ * (B, L, N) are ADDED TO (the caller zeroes them), with the contributions of
+ * the requested channels only.  z NULL: no gate and dz untouched.
+ */
+void oracle_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N,
+                     const float *x, const float *delta, const float *A,
+                     const float *Bm, const float *Cm, const float *D_skip,
+                     const float *z, const float *h0,
+                     const float *dy, const float *dh_final,
+                     const float *delta_bias, int delta_softplus,
+                     const int64_t *channels, int64_t n_channels,
+                     double *dx, double *ddelta, double *dz, double *dh0,
+                     double *dA, double *dD, double *dbias, double *dB, double *dC)
+{
+    (void)B;
+    double *h = (double *)malloc((size_t)((L + 1) * N > 0 ? (L + 1) * N : 1) * sizeof(double));
+    double *lam = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    for (int64_t k = 0; k < n_channels; ++k) {
+        const int64_t b = channels[k] / D;
+        const int64_t d = channels[k] % D;
+        /* forward: h[(t + 1) * N + n] is the state after token t */
+        for (int64_t n = 0; n < N; ++n)
+            h[n] = h0 ? (double)h0[(b * D + d) * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t row = b * L + t;
+            const double dl = step_size(delta[row * D + d], delta_bias, d, delta_softplus);
+            const double xv = x[row * D + d];
+            for (int64_t n = 0; n < N; ++n) {
+                const double a = exp(dl * (double)A[d * N + n]);
+                h[(t + 1) * N + n] = a * h[t * N + n] + dl * (double)Bm[row * N + n] * xv;
+            }
+        }
+        /* reverse */
+        for (int64_t n = 0; n < N; ++n)
+            lam[n] = dh_final ? (double)dh_final[(b * D + d) * N + n] : 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+            const int64_t row = b * L + t;
+            const double raw = delta[row * D + d];
+            const double dl = step_size(raw, delta_bias, d, delta_softplus);
+            const double xv = x[row * D + d];
+            const double dyv = dy[row * D + d];
+            double q = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                q += (double)Cm[row * N + n] * h[(t + 1) * N + n];
+            if (D_skip) q += (double)D_skip[d] * xv;
+            double g = dyv;
+            if (z) {
+                const double zv = z[row * D + d];
+                const double sg = 1.0 / (1.0 + exp(-zv));
+                g = dyv * zv * sg;
+                dz[k * L + t] = dyv * q * sg * (1.0 + zv * (1.0 - sg));
+            }
+            double ddl = 0.0, dxv = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double An = A[d * N + n];
+                const double Bn = Bm[row * N + n];
+                const double a = exp(dl * An);
+                lam[n] += g * (double)Cm[row * N + n];
+                dC[row * N + n] += g * h[(t + 1) * N + n];
+                dB[row * N + n] += lam[n] * dl * xv;
+                ddl += lam[n] * (An * a * h[t * N + n] + Bn * xv);
+                dA[d * N + n] += lam[n] * dl * a * h[t * N + n];
+                dxv += lam[n] * dl * Bn;
+                lam[n] *= a;
+            }
+            if (D_skip) {
+                dxv += (double)D_skip[d] * g;
+                dD[d] += g * xv;
+            }
+            if (delta_softplus) {
+                const double v = raw + (delta_bias ? (double)delta_bias[d] : 0.0);
+                ddl *= 1.0 / (1.0 + exp(-v));
+            }
+            dx[k * L + t] = dxv;
+            ddelta[k * L + t] = ddl;
+            dbias[d] += ddl;
+        }
+        for (int64_t n = 0; n < N; ++n)
+            dh0[k * N + n] = lam[n];
+    }
+    free(lam);
+    free(h);
 }
 
 /*
