@@ -184,6 +184,46 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
                                const ssm_delta_opts *dopts, void *stream);
 
 /*
+ * ssm_scan_bwd -- gradients of ssm_scan_fwd_ex (training).
+ *
+ * The backward of [mamba#285] (replies on the backward kernel): the states
+ * are recomputed forward, the gradient of the state is carried backwards by
+ * a reverse scan fed with dy * C and decayed by exp(delta * A) from token to
+ * token, and the gradient of the initial state is exp(delta_0 * A) times the
+ * carried gradient at the first token.  With y the gated output of
+ * ssm_scan_fwd_ex and h_final its final state, for the loss gradients dy
+ * (B, L, D) and dh_final (B, D, N) (NULL = zero) this returns
+ *   dx, ddelta, dz : (B, L, D) dtype `dt` (ddelta is the gradient of the
+ *                    delta INPUT, i.e. through bias and softplus when dopts
+ *                    asks for them; dz only with z, else must be NULL)
+ *   dA             : (D, N) fp32;   dB, dC : (B, L, N) fp32
+ *   dD             : (D) fp32, written when D_skip and dD are both non-NULL
+ *   dh0            : (B, D, N) fp32 or NULL (not returned)
+ *   d_delta_bias   : (D) fp32 or NULL (not returned): the sum of ddelta
+ * Every output is overwritten (not accumulated).  Sums over channels and
+ * over tokens are taken in a fixed order: results are run-to-run
+ * reproducible.  Inputs as ssm_scan_fwd_ex (dy in dtype `dt`); A, h0,
+ * dh_final, dh0 and the workspace 16-byte aligned.  N in {4, 8, 16, 32, 64}
+ * (else SSM_ERR_UNSUPPORTED).  Outputs must not overlap inputs, the
+ * workspace or each other.
+ * workspace : at least ssm_scan_bwd_workspace_size() bytes: the states
+ *             entering every 16-token segment (B * ceil(L/16) * D * N fp32,
+ *             671 MB at B=8, L=4096, D=5120, N=16) plus per-channel-tile
+ *             partial sums; contents on entry are ignored.
+ */
+ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                        const void *x, const void *delta, const float *A,
+                        const void *Bm, const void *Cm, const float *D_skip,
+                        const void *z, const float *h0, const void *dy,
+                        const float *dh_final, void *dx, void *ddelta, void *dz,
+                        float *dA, float *dB, float *dC, float *dD, float *dh0,
+                        float *d_delta_bias, const ssm_delta_opts *dopts,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device workspace ssm_scan_bwd needs (bytes; 0 for unsupported N). */
+size_t ssm_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N);
+
+/*
  * ssm_decode_steps -- T decode tokens for each of S sequences whose states
  * live in a pool of rows (the slot-indexed state gather/scatter of prefix
  * caching, intermediate_extraction, and the batch-invariant decode of

@@ -76,6 +76,10 @@ def lib():
         L.ssm_state_update_ex.restype = ctypes.c_int
         L.ssm_ssd_fwd_ex.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 10 + [vp, sz, vp, vp]
         L.ssm_ssd_fwd_ex.restype = ctypes.c_int
+        L.ssm_scan_bwd.argtypes = [i64] * 4 + [ctypes.c_int] + [vp] * 20 + [vp, sz, vp]
+        L.ssm_scan_bwd.restype = ctypes.c_int
+        L.ssm_scan_bwd_workspace_size.argtypes = [i64] * 4
+        L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_decode_steps.argtypes = [i64] * 4 + [ctypes.c_int, vp, i64, vp] + [vp] * 8 + [vp, vp]
         L.ssm_decode_steps.restype = ctypes.c_int
         L.ssm_conv1d_fwd.argtypes = [i64] * 4 + [ctypes.c_int] + [vp] * 4 + [ctypes.c_int32, vp, vp, vp]
@@ -332,3 +336,50 @@ def decode_steps(state_pool, x, delta, A, Bm, Cm, D_skip=None, z=None, *, slots=
           _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D_skip), _ptr(z), _ptr(y),
           _dopts(delta_bias, delta_softplus), _stream(dev))
     return y
+
+
+def scan_bwd_workspace_size(B, L, D, N) -> int:
+    return int(lib().ssm_scan_bwd_workspace_size(B, L, D, N))
+
+
+def scan_bwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, dy=None, dh_final=None, *,
+             delta_bias=None, delta_softplus=False, want_dh0=True, want_dbias=False, workspace=None):
+    """Gradients of scan_fwd (ssm_scan_bwd) for the output gradient dy and
+    the final-state gradient dh_final (None = zero).  Returns a dict: dx,
+    ddelta, dz (input dtype; dz None without z), dA, dB, dC (float32), dD
+    (None without D_skip), dh0 (None unless want_dh0), dbias (None unless
+    want_dbias)."""
+    B, L, D = x.shape
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    for nm, t in (("x", x), ("delta", delta), ("z", z), ("dy", dy)):
+        _check(nm, t, (B, L, D), dt, dev)
+    if dy is None:
+        raise ValueError("dy is required")
+    _check("Bm", Bm, (B, L, N), dt, dev)
+    _check("Cm", Cm, (B, L, N), dt, dev)
+    _check("A", A, (D, N), torch.float32, dev)
+    _check("D_skip", D_skip, (D,), torch.float32, dev)
+    _check("h0", h0, (B, D, N), torch.float32, dev)
+    _check("dh_final", dh_final, (B, D, N), torch.float32, dev)
+    _check("delta_bias", delta_bias, (D,), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty((B, L, D), dtype=dt, device=dev),
+           "ddelta": torch.empty((B, L, D), dtype=dt, device=dev),
+           "dz": torch.empty((B, L, D), dtype=dt, device=dev) if z is not None else None,
+           "dA": torch.empty((D, N), **f32), "dB": torch.empty((B, L, N), **f32),
+           "dC": torch.empty((B, L, N), **f32),
+           "dD": torch.empty((D,), **f32) if D_skip is not None else None,
+           "dh0": torch.empty((B, D, N), **f32) if want_dh0 else None,
+           "dbias": torch.empty((D,), **f32) if want_dbias else None}
+    need = scan_bwd_workspace_size(B, L, D, N)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("ssm_scan_bwd", B, L, D, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+          _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]),
+          _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+          _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(out["dbias"]), _dopts(delta_bias, delta_softplus),
+          _ptr(workspace), wsb, _stream(dev))
+    return out

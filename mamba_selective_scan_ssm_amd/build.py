@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssmscan.so")
 ARCH = "gfx950"
-SOURCES = ["capi.cpp", "scan_fwd.hip", "state_update.hip", "ssd.hip", "conv1d.hip"]
+SOURCES = ["capi.cpp", "scan_fwd.hip", "state_update.hip", "ssd.hip", "conv1d.hip", "scan_bwd.hip"]
 # Packed-FP32 VALU forms are disabled for all device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -7,6 +7,7 @@
 
 #include <cstdint>
 
+#include "bwd.h"
 #include "launch.h"
 
 namespace {
@@ -325,6 +326,57 @@ ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtyp
   if (N == 0) return hip_status(ssm::launch_scan_lane(a, s));
   if (ssm::scan_lanesplit_supported(a)) return hip_status(ssm::launch_scan_lanesplit(a, s));
   return hip_status(ssm::launch_scan_sequential(a, 0, s));
+}
+
+size_t ssm_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N) {
+  if (B < 0 || L < 0 || D < 0 || N < 0 || !ssm::scan_bwd_supported_n(N)) return 0;
+  return static_cast<size_t>(ssm::scan_bwd_ws_floats(B, L, D, N)) * sizeof(float);
+}
+
+ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                        const void *x, const void *delta, const float *A, const void *Bm,
+                        const void *Cm, const float *D_skip, const void *z, const float *h0,
+                        const void *dy, const float *dh_final, void *dx, void *ddelta, void *dz,
+                        float *dA, float *dB, float *dC, float *dD, float *dh0,
+                        float *d_delta_bias, const ssm_delta_opts *dopts, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  if (B < 0 || L < 0 || D < 0 || N < 0 || !valid_dtype(dt) || !dopts_ok(dopts))
+    return SSM_ERR_INVALID_ARG;
+  if (!ssm::scan_bwd_supported_n(N)) return SSM_ERR_UNSUPPORTED;
+  if (B > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  const int64_t es = esize(dt);
+  const int64_t nX = B * L * D, nBC = B * L * N, nS = B * D * N;
+  if (nX > 0 && (!x || !delta || !dy || !dx || !ddelta || (z && !dz))) return SSM_ERR_INVALID_ARG;
+  if (nBC > 0 && (!Bm || !Cm || !dB || !dC)) return SSM_ERR_INVALID_ARG;
+  if (D * N > 0 && (!A || !dA)) return SSM_ERR_INVALID_ARG;
+  if (!z && dz) return SSM_ERR_INVALID_ARG;
+  auto a16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  if (!a16(A) || !a16(h0) || !a16(dh_final) || !a16(dh0)) return SSM_ERR_UNSUPPORTED;
+  const size_t need = ssm_scan_bwd_workspace_size(B, L, D, N);
+  if (need > 0 && (!workspace || workspace_bytes < need || !a16(workspace))) return SSM_ERR_WORKSPACE;
+  const Range ins[] = {{x, nX * es},     {delta, nX * es},    {A, D * N * 4},
+                       {Bm, nBC * es},   {Cm, nBC * es},      {D_skip, D * 4},
+                       {z, nX * es},     {h0, nS * 4},        {dy, nX * es},
+                       {dh_final, nS * 4}, {dbias_of(dopts), D * 4}, {workspace, static_cast<int64_t>(need)}};
+  const Range outs[] = {{dx, nX * es},  {ddelta, nX * es}, {dz, nX * es}, {dA, D * N * 4},
+                        {dB, nBC * 4},  {dC, nBC * 4},     {dD, D * 4},   {dh0, nS * 4},
+                        {d_delta_bias, D * 4}};
+  for (const Range &o : outs) {
+    if (overlaps_any(o, ins)) return SSM_ERR_INVALID_ARG;
+    int same = 0;
+    for (const Range &o2 : outs) same += overlap(o, o2) ? 1 : 0;
+    if (same > 1) return SSM_ERR_INVALID_ARG;  // overlaps another output
+  }
+  ssm::BwdArgs a{};
+  a.B = B; a.L = L; a.D = D; a.N = N;
+  a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
+  a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.D_skip = D_skip; a.z = z;
+  a.h0 = h0; a.dy = dy; a.dh_final = dh_final;
+  a.delta_bias = dbias_of(dopts); a.delta_softplus = dsoft_of(dopts);
+  a.dx = dx; a.ddelta = ddelta; a.dz = dz; a.dA = dA; a.dB = dB; a.dC = dC;
+  a.dD = dD; a.dbias = d_delta_bias; a.dh0 = dh0;
+  a.ws = static_cast<float *>(workspace);
+  return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t ssm_ssd_fwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,

@@ -313,6 +313,22 @@ WORKLOADS = {
 }
 
 
+_GRAD_STREAMS = ("grad_dy", "grad_dh")
+
+
+@dataclasses.dataclass
+class GradInputs:
+    dy: Tensor               # (B, L, D) gradient of the scan output, storage dtype
+    dh_final: np.ndarray     # fp32 (B, D, N) gradient of the final state
+
+
+def make_grads(B, L, D, N, *, dtype="bf16", seed=0) -> GradInputs:
+    """Loss gradients for the scan backward: dy ~ N(0, 1), dh_final ~ N(0, 0.5)."""
+    kids = np.random.SeedSequence(seed).spawn(len(_STREAMS) + len(_CONV_STREAMS) + len(_GRAD_STREAMS))
+    r = {n: np.random.default_rng(k) for n, k in zip(_GRAD_STREAMS, kids[-len(_GRAD_STREAMS):])}
+    return GradInputs(_store(_normal(r["grad_dy"], (B, L, D)), dtype), _normal(r["grad_dh"], (B, D, N), std=0.5))
+
+
 @dataclasses.dataclass
 class PoolDecodeInputs:
     tokens: ScanInputs      # (S, T, .) per-sequence tokens; tokens.h0 is None

@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
     for n in ("ssm_scan_fwd", "ssm_scan_fwd_workspace_size", "ssm_state_update", "ssm_ssd_fwd",
               "ssm_ssd_fwd_workspace_size", "ssm_conv1d_fwd", "ssm_conv1d_update",
               "ssm_scan_fwd_ex", "ssm_state_update_ex", "ssm_ssd_fwd_ex", "ssm_decode_steps",
+              "ssm_scan_bwd", "ssm_scan_bwd_workspace_size",
               "ssm_status_string", "ssm_version"):
         assert n in names
 
@@ -233,3 +234,52 @@ def test_decode_steps_validation(lib):
     assert ds(y=P[1]) == INVALID                  # y on x
     assert ds(pool=8, y=P[0]) == INVALID          # y inside the pool
     assert ds(x=None) == INVALID
+
+
+Q = [ctypes.c_void_p(0x4000000 * (i + 1)) for i in range(24)]  # 64 MiB apart
+
+
+_DEFAULT = object()
+
+
+def bwd(lib, B=2, L=8, D=64, N=16, dt=F32, ws=_DEFAULT, ws_len=None, **over):
+    """Every call below must be rejected on the host: none may reach a launch."""
+    names = ["x", "delta", "A", "Bm", "Cm", "D_skip", "z", "h0", "dy", "dh_final", "dx", "ddelta", "dz",
+             "dA", "dB", "dC", "dD", "dh0", "dbias"]
+    p = {k: Q[i] for i, k in enumerate(names)}
+    p.update(over)
+    if ws is _DEFAULT:
+        ws = Q[20]
+    if ws_len is None:
+        ws_len = lib.ssm_scan_bwd_workspace_size(B, L, D, N)
+    return lib.ssm_scan_bwd(B, L, D, N, dt, *(p[k] for k in names), None, ws, ws_len, None)
+
+
+def test_scan_bwd_workspace_size(lib):
+    assert lib.ssm_scan_bwd_workspace_size(2, 8, 64, 12) == 0
+    # entering states (1 segment) + dB|dC partials (1 tile) + dA partials + dD, dbias partials
+    want = (2 * 1 * 64 * 16 + 2 * 8 * 1 * 32 + 2 * 64 * 16 + 2 * 2 * 64) * 4
+    assert lib.ssm_scan_bwd_workspace_size(2, 8, 64, 16) == want
+    # 16-token segments, 64-channel tiles at N = 16
+    assert lib.ssm_scan_bwd_workspace_size(1, 17, 65, 16) == (2 * 65 * 16 + 17 * 2 * 32 + 65 * 16 + 2 * 65) * 4
+
+
+def test_scan_bwd_validation(lib):
+    assert bwd(lib, B=-1) == INVALID
+    assert bwd(lib, dt=7) == INVALID
+    assert bwd(lib, N=12) == UNSUPPORTED
+    assert bwd(lib, N=128) == UNSUPPORTED
+    assert bwd(lib, B=70000) == UNSUPPORTED
+    assert bwd(lib, dy=None) == INVALID
+    assert bwd(lib, dx=None) == INVALID
+    assert bwd(lib, dz=None) == INVALID                       # gate given, its gradient not
+    assert bwd(lib, z=None) == INVALID                        # dz given without a gate
+    assert bwd(lib, dB=None) == INVALID
+    assert bwd(lib, A=ctypes.c_void_p(Q[2].value + 4)) == UNSUPPORTED
+    assert bwd(lib, dh0=ctypes.c_void_p(Q[17].value + 8)) == UNSUPPORTED
+    assert bwd(lib, ws=None) == WORKSPACE
+    assert bwd(lib, ws_len=64) == WORKSPACE
+    assert bwd(lib, ws=ctypes.c_void_p(Q[20].value + 4)) == WORKSPACE
+    assert bwd(lib, dx=Q[0]) == INVALID                       # output on an input
+    assert bwd(lib, dC=Q[14]) == INVALID                      # two outputs on one buffer
+    assert bwd(lib, dA=Q[20]) == INVALID                      # output on the workspace

@@ -1,0 +1,148 @@
+"""GPU parity of ssm_scan_bwd (gradients of the selective scan) against the
+oracle's backward, on the same seeded inputs and loss gradients.
+
+Small cases are compared whole (ragged L across 16-token segments, D across
+channel tiles, every supported N, gate / skip / h0 / dh_final / step-size
+transform on and off); the 2.8B-shaped case, at the size the bench times,
+on sampled channels, with dB/dC checked whole for one sequence and dA/dD on
+sampled channels over every sequence.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import ssm_inputs as gen
+from tests.helpers import assert_close, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _run(inp, gr, dtype, gate=True, d_skip=True, h0=True, dhf=True, bias=None, softplus=False, **kw):
+    import mamba_selective_scan_ssm_amd as ssm
+    out = ssm.scan_bwd(to_dev(inp.x), to_dev(inp.delta), to_dev(inp.A), to_dev(inp.Bm), to_dev(inp.Cm),
+                       to_dev(inp.D_skip) if d_skip else None, to_dev(inp.z) if gate else None,
+                       to_dev(inp.h0) if h0 else None, to_dev(gr.dy), to_dev(gr.dh_final) if dhf else None,
+                       delta_bias=None if bias is None else to_dev(bias), delta_softplus=softplus,
+                       want_dh0=True, want_dbias=True, **kw)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else to_np(v)) for k, v in out.items()}
+
+
+def _oracle(oracle_mod, inp, gr, gate=True, d_skip=True, h0=True, dhf=True, bias=None, softplus=False,
+            channels=None):
+    return oracle_mod.scan_bwd(inp.x.f32, inp.delta.f32, inp.A, inp.Bm.f32, inp.Cm.f32,
+                               inp.D_skip if d_skip else None, inp.z.f32 if gate else None,
+                               inp.h0 if h0 else None, gr.dy.f32, gr.dh_final if dhf else None,
+                               delta_bias=bias, delta_softplus=softplus, channels=channels)
+
+
+def _compare(g, r, dtype, keys=("dx", "ddelta", "dz", "dA", "dB", "dC", "dD", "dh0", "dbias")):
+    for k in keys:
+        if r.get(k) is None:
+            continue
+        assert_close(g[k], r[k], dtype, k)
+
+
+@pytest.mark.parametrize("B,L,D,N,dtype", [
+    (2, 37, 70, 16, "f32"),     # ragged segment and channel tile
+    (1, 64, 64, 16, "bf16"),
+    (2, 50, 33, 4, "f32"),
+    (1, 33, 40, 8, "bf16"),
+    (2, 20, 48, 32, "f32"),
+    (1, 17, 20, 64, "bf16"),
+    (3, 5, 130, 16, "f32"),     # shorter than one segment
+])
+def test_bwd_shapes(oracle_mod, B, L, D, N, dtype):
+    inp = gen.make_scan(B, L, D, N, dtype=dtype, seed=800 + L + N)
+    gr = gen.make_grads(B, L, D, N, dtype=dtype, seed=801 + L)
+    _say("scan_bwd", B, L, D, N, dtype)
+    _compare(_run(inp, gr, dtype), _oracle(oracle_mod, inp, gr), dtype)
+
+
+@pytest.mark.parametrize("gate,d_skip,h0,dhf", [
+    (False, True, True, True), (True, False, True, True), (True, True, False, False), (False, False, False, True),
+])
+def test_bwd_optional_terms(oracle_mod, gate, d_skip, h0, dhf):
+    inp = gen.make_scan(2, 40, 96, 16, dtype="f32", seed=820)
+    gr = gen.make_grads(2, 40, 96, 16, dtype="f32", seed=821)
+    _say("scan_bwd optional terms", gate, d_skip, h0, dhf)
+    opts = dict(gate=gate, d_skip=d_skip, h0=h0, dhf=dhf)
+    g = _run(inp, gr, "f32", **opts)
+    r = _oracle(oracle_mod, inp, gr, **opts)
+    _compare(g, r, "f32")
+    if not gate:
+        assert g["dz"] is None
+    if not d_skip:
+        assert g["dD"] is None
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_delta_transform(oracle_mod, dtype):
+    inp = gen.make_scan(2, 45, 64, 16, dtype=dtype, seed=830)
+    inp.delta = gen._store((inp.delta.f32 * 6.0 - 3.0).astype(np.float32), dtype)
+    bias = np.random.default_rng(831).normal(0.0, 1.0, 64).astype(np.float32)
+    gr = gen.make_grads(2, 45, 64, 16, dtype=dtype, seed=832)
+    _say("scan_bwd softplus", dtype)
+    _compare(_run(inp, gr, dtype, bias=bias, softplus=True),
+             _oracle(oracle_mod, inp, gr, bias=bias, softplus=True), dtype)
+
+
+def test_bwd_empty_sequence_and_no_channels(oracle_mod):
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(2, 0, 64, 16, dtype="f32", seed=840)
+    gr = gen.make_grads(2, 0, 64, 16, dtype="f32", seed=841)
+    _say("scan_bwd L=0")
+    g = _run(inp, gr, "f32")
+    assert np.array_equal(g["dh0"], gr.dh_final.astype(np.float64))
+    assert not g["dA"].any() and not g["dD"].any() and not g["dbias"].any()
+    assert g["dx"].shape == (2, 0, 64) and g["dB"].shape == (2, 0, 16)
+    inp = gen.make_scan(2, 10, 0, 16, dtype="f32", seed=842)
+    _say("scan_bwd D=0")
+    out = ssm.scan_bwd(to_dev(inp.x), to_dev(inp.delta), to_dev(inp.A), to_dev(inp.Bm), to_dev(inp.Cm),
+                       None, None, None, to_dev(inp.x))
+    torch.cuda.synchronize()
+    assert not out["dB"].any() and not out["dC"].any()
+
+
+def test_bwd_reproducible():
+    """Sums are taken in a fixed order: two calls agree bit for bit."""
+    inp = gen.make_scan(2, 70, 200, 16, dtype="bf16", seed=850)
+    gr = gen.make_grads(2, 70, 200, 16, dtype="bf16", seed=851)
+    _say("scan_bwd reproducible")
+    a = _run(inp, gr, "bf16")
+    b = _run(inp, gr, "bf16")
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k]), k
+
+
+def test_bwd_mamba2p8b_sampled(oracle_mod):
+    """The 2.8B-shaped prefill (B=8, L=4096, D=5120, N=16, bf16) as the bench
+    times it: dx/ddelta/dz/dh0 on sampled channels, dA/dD/dbias on sampled
+    channels (all sequences), dB/dC whole for one sequence."""
+    inp = gen.make_workload("mamba2p8b_prefill_bf16")
+    B, L, D, N = inp.B, inp.L, inp.D, inp.N
+    gr = gen.make_grads(B, L, D, N, dtype="bf16", seed=1008)
+    _say("scan_bwd mamba2p8b full size")
+    g = _run(inp, gr, "bf16")
+    rng = np.random.default_rng(860)
+    ds = np.unique(np.concatenate([rng.integers(0, D, 6), [0, D - 1]]))
+    ch = np.concatenate([b * D + ds for b in range(B)])
+    r = _oracle(oracle_mod, inp, gr, channels=ch)
+    bb, dd = ch // D, ch % D
+    assert_close(g["dx"][bb, :, dd], r["dx"], "bf16", "dx")
+    assert_close(g["ddelta"][bb, :, dd], r["ddelta"], "bf16", "ddelta")
+    assert_close(g["dz"][bb, :, dd], r["dz"], "bf16", "dz")
+    assert_close(g["dh0"][bb, dd], r["dh0"], "bf16", "dh0")
+    assert_close(g["dA"][ds], r["dA"][ds], "bf16", "dA")
+    assert_close(g["dD"][ds], r["dD"][ds], "bf16", "dD")
+    assert_close(g["dbias"][ds], r["dbias"][ds], "bf16", "dbias")
+    b1 = 5
+    r1 = _oracle(oracle_mod, inp, gr, channels=b1 * D + np.arange(D))
+    assert_close(g["dB"][b1], r1["dB"][b1], "bf16", "dB")
+    assert_close(g["dC"][b1], r1["dC"][b1], "bf16", "dC")
