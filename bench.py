@@ -43,6 +43,12 @@ TRANS_LANE_OPS = VALU_LANE_OPS / 4
 # h = dA*h + u*B -> 1 fma; y += C*h -> 1 fma.  6 flops + 1 transcendental.
 SCAN_VALU_PER_ELEM, SCAN_TRANS_PER_ELEM, SCAN_FLOPS_PER_ELEM = 4, 1, 6
 SCAN_ELEM_PEAK = 1.0 / (SCAN_VALU_PER_ELEM / VALU_LANE_OPS + SCAN_TRANS_PER_ELEM / TRANS_LANE_OPS)
+# backward, per element at least: the forward recurrence again (3 VALU) and
+# one exp(delta A); the adjoint g*C + lam (1), lam*u for dB (1), g*h for dC
+# (1), C*h for q (1), p = a*h_prev (1), ddelta += lam (A p + B x) (3),
+# dA += (lam delta) p (2), dx += lam B (1), lam *= a (1): 15 VALU + 1 exp
+BWD_VALU_PER_ELEM, BWD_TRANS_PER_ELEM = 15, 1
+BWD_ELEM_PEAK = 1.0 / (BWD_VALU_PER_ELEM / VALU_LANE_OPS + BWD_TRANS_PER_ELEM / TRANS_LANE_OPS)
 
 
 # the kernel sources behind each measured entry point: counters taken on
@@ -57,6 +63,7 @@ KERNEL_SOURCES = {
     "decode_steps_T1": ["state_update.hip"] + _COMMON,
     "decode_steps_T4": ["state_update.hip"] + _COMMON,
     "decode_steps_T16": ["state_update.hip"] + _COMMON,
+    "scan_bwd": ["scan_bwd.hip", "bwd.h"] + _COMMON,
 }
 
 
@@ -252,6 +259,32 @@ def bench_conv(torch, ssm, gen, steps=50):
     return out
 
 
+def bench_bwd(torch, ssm, gen, steps=10):
+    """Backward of the 2.8B-shaped prefill scan (ssm_scan_bwd): all gradients
+    (dx, ddelta, dz, dA, dB, dC, dD, dh0) for dy and dh_final."""
+    inp = gen.make_workload("mamba2p8b_prefill_bf16")
+    B, L, D, N = inp.B, inp.L, inp.D, inp.N
+    gr = gen.make_grads(B, L, D, N, dtype="bf16", seed=1008)
+    t = {k: upload(getattr(inp, k), torch) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds, h0 = upload(inp.A, torch), upload(inp.D_skip, torch), upload(inp.h0, torch)
+    dy, dhf = upload(gr.dy, torch), upload(gr.dh_final, torch)
+    ws = torch.empty(ssm.scan_bwd_workspace_size(B, L, D, N), dtype=torch.uint8, device="cuda")
+    del inp, gr
+
+    def one():
+        ssm.scan_bwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, dy, dhf, workspace=ws)
+
+    ms, min_ms, wall = time_calls(one, steps, 3, torch)
+    elems = B * L * D * N
+    io = B * L * D * 2 * 7 + B * L * N * (2 * 2 + 4 * 2) + D * N * 4 * 2 + D * 4 * 2 + B * D * N * 4 * 3
+    rate = elems / (ms * 1e-3)
+    return {"workload": "mamba2p8b_prefill_bf16 backward (B=8, L=4096, D=5120, N=16, bf16, all gradients)",
+            "ms": ms, "ms_min": min_ms, "Gelem_per_s": rate / 1e9, "alg_bytes": io,
+            "hbm_GBs": io / (ms * 1e-3) / 1e9, "hbm_frac": io / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alu_frac": rate / BWD_ELEM_PEAK, "alu_peak_Telem_s": BWD_ELEM_PEAK / 1e12,
+            "workspace_bytes": ws.numel(), "traffic_bytes": load_traffic("scan_bwd", "bytes_per_call")}
+
+
 def bench_pool_decode(torch, ssm, gen, steps=128):
     """Decode from a state pool (ssm_decode_steps): 256 sequences on scattered
     rows of a 512-row pool; 1, 4 and 16 tokens per call."""
@@ -290,7 +323,7 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the decode and SSD rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=8)
-    ap.add_argument("--only", choices=["scan", "decode", "ssd", "conv", "pool"], default=None,
+    ap.add_argument("--only", choices=["scan", "decode", "ssd", "conv", "pool", "bwd"], default=None,
                     help="time one hot-path entry point only (for profiling); prints its row")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) so a "
@@ -317,6 +350,9 @@ def main():
         return
     if args.only == "ssd":
         print(json.dumps({"ssd": bench_ssd(torch, ssm, gen, steps=args.steps)}))
+        return
+    if args.only == "bwd":
+        print(json.dumps({"bwd": bench_bwd(torch, ssm, gen, steps=args.steps)}))
         return
     if args.only == "pool":
         print(json.dumps({"pool_decode": bench_pool_decode(torch, ssm, gen, steps=args.steps)}))
@@ -375,7 +411,8 @@ def main():
     }
     if not args.no_rows and args.only is None:
         out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen, steps=20),
-                       "conv": bench_conv(torch, ssm, gen), "pool_decode": bench_pool_decode(torch, ssm, gen)}
+                       "conv": bench_conv(torch, ssm, gen), "pool_decode": bench_pool_decode(torch, ssm, gen),
+                       "bwd": bench_bwd(torch, ssm, gen)}
     if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
     print(json.dumps(out))

@@ -207,8 +207,8 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
  * (else SSM_ERR_UNSUPPORTED).  Outputs must not overlap inputs, the
  * workspace or each other.
  * workspace : at least ssm_scan_bwd_workspace_size() bytes: the states
- *             entering every 16-token segment (B * ceil(L/16) * D * N fp32,
- *             671 MB at B=8, L=4096, D=5120, N=16) plus per-channel-tile
+ *             entering every 8-token segment (B * ceil(L/8) * D * N fp32,
+ *             1.34 GB at B=8, L=4096, D=5120, N=16) plus per-channel-tile
  *             partial sums; contents on entry are ignored.
  */
 ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,

@@ -18,15 +18,18 @@
 // Schedule.  A lane holds 4 consecutive states of a channel (N/4 lanes per
 // channel, as in the decode step) and a workgroup 1024/N channels of one
 // sequence.  Pass 1 runs the recurrence forward and writes the state that
-// enters every 16-token segment to the workspace.  Pass 2 walks the
-// segments backwards: it reloads a segment's entering state, recomputes the
-// segment's 16 states into registers, then runs the reverse recurrence over
-// them.  Per token each wave sums its channels' dB and dC contributions with
-// a butterfly that leaves every (B|C, n) sum in one lane, the four waves add
-// theirs through LDS, and the workgroup writes one partial per (token, n).
-// Two small kernels then add the partials of the channel tiles (dB, dC) and
-// of the sequences (dA, dD, dbias) in a fixed order, so the result does not
-// depend on timing (no atomics).
+// enters every 8-token segment to the workspace.  Pass 2 walks the segments
+// backwards: it reloads a segment's entering state, recomputes the
+// segment's 8 states into registers, then runs the reverse recurrence over
+// them.  A segment's inputs are loaded by the whole workgroup one segment
+// ahead (coalesced over channels), converted once, and staged in LDS with
+// the gate and step-size factors already applied; its per-token outputs go
+// back through LDS to coalesced stores.  Sums across lanes use DPP: over a
+// channel's lanes, and over half the channels of a row of 16 lanes for dB
+// and dC, whose partials meet in LDS; the workgroup writes one partial per
+// (token, n).  Two small kernels then add the partials of the channel tiles
+// (dB, dC) and of the sequences (dA, dD, dbias) in a fixed order, so the
+// result does not depend on timing (no atomics).
 #include "bwd.h"
 #include "device_common.h"
 
@@ -34,53 +37,123 @@ namespace ssm {
 namespace {
 
 constexpr int kBwdThreads = 256;
-constexpr int kSeg = 16;  // tokens per checkpointed segment
+constexpr int kSeg = 8;  // tokens per checkpointed segment
 
 __device__ __forceinline__ float sigmoid_f(float v) {
   return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e));
 }
 
-// sum over the LPC adjacent lanes of a channel
+// Cross-lane moves on the VALU (DPP): quad permutations, row rotations and
+// mirrors stay inside a row of 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15 - i of the row
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7 - i of the half row
+constexpr int kRowRor = 0x120;        // + m: rotate the row right by m lanes
+
+// sum over the LPC adjacent lanes of a channel (all of them get it)
 template <int LPC>
 __device__ __forceinline__ float channel_sum(float v) {
-#pragma unroll
-  for (int off = LPC / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, LPC);
+  if constexpr (LPC >= 2) v += dpp_f<kQuadXor1>(v);
+  if constexpr (LPC >= 4) v += dpp_f<kQuadXor2>(v);
+  if constexpr (LPC >= 8) v += dpp_f<kRowHalfMirror>(v);
+  if constexpr (LPC >= 16) v += dpp_f<kRowMirror>(v);
   return v;
 }
 
-template <typename T>
-__device__ __forceinline__ void load4(const T *p, float *v) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = to_f32(p[j]);
+// Partial sum over the channels of a row of 16 lanes for each state slice q
+// (lanes LPC apart hold the same q): rotations by LPC, 2 LPC, ... add up a
+// cyclic window of half the row's channels, so the lanes of channels 0 and
+// R/2 (R = 16 / LPC channels per row) hold two sums that together cover the
+// row.  With one channel per row the value is returned as is.
+template <int LPC, int M = LPC>
+__device__ __forceinline__ float row_half_sum(float v) {
+  if constexpr (2 * M < 16) return row_half_sum<LPC, 2 * M>(v + dpp_f<kRowRor + M>(v));
+  else return v;
 }
 
 __host__ __device__ constexpr int64_t bwd_nseg(int64_t L) { return (L + kSeg - 1) / kSeg; }
 __host__ __device__ constexpr int64_t bwd_channels_per_block(int64_t N) { return 4 * kBwdThreads / N; }
 
+// Raw inputs of one segment for the workgroup, loaded into registers one
+// segment ahead.  Thread tid stages channel tid % kCh of the tile at tokens
+// tid / kCh + e * LPC (e < kE), and B/C entries tid + e * 256 of the
+// segment's (16, N) rows.  Indices past the sequence or the channel range
+// are clamped (their values are never used).
+template <typename T, int LPC, bool kFull>
+struct SegRegs {
+  static constexpr int N = 4 * LPC;
+  static constexpr int kCh = kBwdThreads / LPC;
+  static constexpr int kE = (kSeg * kCh + kBwdThreads - 1) / kBwdThreads;
+  static constexpr int kEB = (kSeg * N + kBwdThreads - 1) / kBwdThreads;
+  float d[kE], x[kE], z[kFull ? kE : 1], g[kFull ? kE : 1], bb[kEB], cc[kFull ? kEB : 1];
+
+  __device__ __forceinline__ void load(const BwdArgs &a, int64_t b, int64_t t0, int64_t dst, int tid) {
+    const T *xp = static_cast<const T *>(a.x), *dp = static_cast<const T *>(a.delta);
+    const T *zp = static_cast<const T *>(a.z), *gp = static_cast<const T *>(a.dy);
+    const T *Bp = static_cast<const T *>(a.Bm), *Cp = static_cast<const T *>(a.Cm);
+    const int64_t L = a.L, D = a.D;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int64_t t = t0 + tid / kCh + e * LPC;
+      const int64_t i = (b * L + (t < L ? t : L - 1)) * D + dst;
+      d[e] = to_f32(dp[i]);
+      x[e] = to_f32(xp[i]);
+      if constexpr (kFull) {
+        z[e] = zp ? to_f32(zp[i]) : 0.f;
+        g[e] = to_f32(gp[i]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kEB; ++e) {
+      const int idx = (tid + e * kBwdThreads) % (kSeg * N);
+      const int64_t t = t0 + idx / N;
+      const int64_t i = (b * L + (t < L ? t : L - 1)) * N + idx % N;
+      bb[e] = to_f32(Bp[i]);
+      if constexpr (kFull) cc[e] = to_f32(Cp[i]);
+    }
+  }
+};
+
 template <typename T, int LPC>
 __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
   constexpr int N = 4 * LPC;
   constexpr int kCh = kBwdThreads / LPC;        // channels per workgroup
-  constexpr int kLq = LPC == 1 ? 0 : LPC == 2 ? 1 : LPC == 4 ? 2 : LPC == 8 ? 3 : 4;
-  constexpr int kCB = 6 - kLq;                   // lane bits that select the channel
-  constexpr int kHalv = kCB < 3 ? kCB : 3;       // halving steps of the butterfly
-  constexpr int kFull = kCB - kHalv;             // remaining summing steps
-  constexpr int kCnt = 8 >> kHalv;               // sums each lane ends with
-  __shared__ float s_red[4][kSeg][2 * N];        // per wave: [token][B sums | C sums]
+  constexpr int kE = (kSeg * kCh + kBwdThreads - 1) / kBwdThreads;  // staged entries per thread
+  constexpr int kEB = (kSeg * N + kBwdThreads - 1) / kBwdThreads;
+  static_assert(kBwdThreads % kCh == 0, "a staging thread keeps one channel");
+  // staged segment: step size, x, gradient reaching q (dy silu(z)); B, C rows
+  __shared__ float s_dl[kSeg][kCh], s_x[kSeg][kCh], s_g[kSeg][kCh];
+  __shared__ __attribute__((aligned(16))) float s_B[kSeg][N], s_C[kSeg][N];
+  // per (token, channel): dx, ddelta before the softplus slope, q
+  __shared__ float s_o[3][kSeg][kCh];
+  constexpr int kRowCh = 16 / LPC;                // channels per row of 16 lanes
+  constexpr int kSPR = kRowCh >= 2 ? 2 : 1;       // partial sums per row
+  constexpr int kSlots = 16 * kSPR;               // per workgroup
+  __shared__ float s_red[kSlots][kSeg][2 * N];    // [slot][token][B sums | C sums]
+  __shared__ float s_db[kBwdThreads];
 
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64, q = tid % LPC;
   const int64_t tile = blockIdx.x, ntile = gridDim.x, b = blockIdx.y;
   const int64_t B = a.B, L = a.L, D = a.D;
-  const int64_t d_raw = tile * kCh + tid / LPC;
+  // compute role: channel c of the tile, states 4q..4q+3
+  const int c = tid / LPC;
+  const int64_t d_raw = tile * kCh + c;
   const bool active = d_raw < D;
   const int64_t d = active ? d_raw : D - 1;
+  // staging role: channel cs of the tile, tokens k0 + e * LPC
+  const int cs = tid % kCh, k0 = tid / kCh;
+  const int64_t ds_raw = tile * kCh + cs;
+  const bool s_active = ds_raw < D;
+  const int64_t dst = s_active ? ds_raw : D - 1;
+  const float bias_s = a.delta_bias ? a.delta_bias[dst] : 0.f;
+  const bool has_z = a.z != nullptr;
+
   const int64_t nseg = bwd_nseg(L);
-  const T *xp = static_cast<const T *>(a.x);
-  const T *dp = static_cast<const T *>(a.delta);
-  const T *zp = static_cast<const T *>(a.z);
-  const T *gp = static_cast<const T *>(a.dy);
-  const T *Bp = static_cast<const T *>(a.Bm);
-  const T *Cp = static_cast<const T *>(a.Cm);
   float *ck = a.ws;                      // (B, nseg, D, N) entering states
   float *P = ck + B * nseg * D * N;      // (B, L, ntile, 2N) dB|dC partials
   float *PA = P + B * L * ntile * 2 * N; // (B, D, N) dA partials
@@ -92,7 +165,6 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
   float A2[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) A2[j] = An[j] * kLog2e;
-  const float bias = a.delta_bias ? a.delta_bias[d] : 0.f;
   const float Dd = a.D_skip ? a.D_skip[d] : 0.f;
 
   // ---- pass 1: forward, keeping the state that enters every segment ----
@@ -101,20 +173,42 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
     const float4 v = reinterpret_cast<const float4 *>(a.h0 + (b * D + d) * N)[q];
     h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
   }
-  for (int64_t s = 0; s < nseg; ++s) {
-    if (active)
-      reinterpret_cast<float4 *>(ck + ((b * nseg + s) * D + d) * N)[q] =
-          make_float4(h[0], h[1], h[2], h[3]);
-    const int64_t t0 = s * kSeg;
-    const int nt = static_cast<int>(L - t0 < kSeg ? L - t0 : kSeg);
-    for (int k = 0; k < nt; ++k) {
-      const int64_t row = b * L + t0 + k;
-      const float dl = step_size(to_f32(dp[row * D + d]), bias, a.delta_softplus);
-      const float u = dl * to_f32(xp[row * D + d]);
-      float Bv[4];
-      load4(Bp + row * N + 4 * q, Bv);
+  {
+    SegRegs<T, LPC, false> r;
+    if (nseg > 0) r.load(a, b, 0, dst, tid);
+    for (int64_t s = 0; s < nseg; ++s) {
+      const int64_t t0 = s * kSeg;
+      const int nt = static_cast<int>(L - t0 < kSeg ? L - t0 : kSeg);
+      if (active)
+        reinterpret_cast<float4 *>(ck + ((b * nseg + s) * D + d) * N)[q] =
+            make_float4(h[0], h[1], h[2], h[3]);
+      __syncthreads();  // the previous segment's LDS reads are done
 #pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = fmaf(fast_exp2(dl * A2[j]), h[j], u * Bv[j]);
+      for (int e = 0; e < kE; ++e) {
+        const int k = k0 + e * LPC;
+        if (k < kSeg) {
+          s_dl[k][cs] = step_size(r.d[e], bias_s, a.delta_softplus);
+          s_x[k][cs] = r.x[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kEB; ++e) {
+        const int idx = tid + e * kBwdThreads;
+        if (idx < kSeg * N) s_B[idx / N][idx % N] = r.bb[e];
+      }
+      if (s + 1 < nseg) r.load(a, b, t0 + kSeg, dst, tid);
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kSeg; ++k) {
+        if (k < nt) {
+          const float dl = s_dl[k][c];
+          const float u = dl * s_x[k][c];
+          const float4 Bv = *reinterpret_cast<const float4 *>(&s_B[k][4 * q]);
+          const float bv[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) h[j] = fmaf(fast_exp2(dl * A2[j]), h[j], u * bv[j]);
+        }
+      }
     }
   }
 
@@ -126,128 +220,152 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
   }
   float dAacc[4] = {0.f, 0.f, 0.f, 0.f};
   float dDacc = 0.f, dbacc = 0.f;
+  SegRegs<T, LPC, true> r;
+  float4 hck = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (nseg > 0) {
+    r.load(a, b, (nseg - 1) * kSeg, dst, tid);
+    if (active) hck = reinterpret_cast<const float4 *>(ck + ((b * nseg + nseg - 1) * D + d) * N)[q];
+  }
   for (int64_t s = nseg - 1; s >= 0; --s) {
     const int64_t t0 = s * kSeg;
     const int nt = static_cast<int>(L - t0 < kSeg ? L - t0 : kSeg);
-    float H[kSeg + 1][4];  // H[k] = state before token t0 + k
-    {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (active) v = reinterpret_cast<const float4 *>(ck + ((b * nseg + s) * D + d) * N)[q];
-      H[0][0] = v.x; H[0][1] = v.y; H[0][2] = v.z; H[0][3] = v.w;
+    float slope[kE], wz[kE];  // softplus slope and dz / q of the staged entries
+    __syncthreads();  // the previous segment's LDS reads are done
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int k = k0 + e * LPC;
+      const float raw = r.d[e];
+      slope[e] = a.delta_softplus ? sigmoid_f(raw + bias_s) : 1.f;
+      float gq = r.g[e], w = 0.f;
+      if (has_z) {
+        const float zv = r.z[e];
+        const float sg = sigmoid_f(zv);
+        gq = r.g[e] * zv * sg;
+        w = r.g[e] * sg * fmaf(zv, 1.f - sg, 1.f);
+      }
+      wz[e] = w;
+      if (k < kSeg) {
+        s_dl[k][cs] = step_size(raw, bias_s, a.delta_softplus);
+        s_x[k][cs] = r.x[e];
+        s_g[k][cs] = s_active ? gq : 0.f;  // channels past D: no gradient flows
+      }
     }
+#pragma unroll
+    for (int e = 0; e < kEB; ++e) {
+      const int idx = tid + e * kBwdThreads;
+      if (idx < kSeg * N) {
+        s_B[idx / N][idx % N] = r.bb[e];
+        s_C[idx / N][idx % N] = r.cc[e];
+      }
+    }
+    float H[kSeg + 1][4];  // H[k] = state before token t0 + k
+    float aS[kSeg][4];     // exp(delta A) of token t0 + k
+    H[0][0] = hck.x; H[0][1] = hck.y; H[0][2] = hck.z; H[0][3] = hck.w;
+    if (s > 0) {
+      r.load(a, b, t0 - kSeg, dst, tid);
+      if (active) hck = reinterpret_cast<const float4 *>(ck + ((b * nseg + s - 1) * D + d) * N)[q];
+    }
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < kSeg; ++k) {
       if (k < nt) {
-        const int64_t row = b * L + t0 + k;
-        const float dl = step_size(to_f32(dp[row * D + d]), bias, a.delta_softplus);
-        const float u = dl * to_f32(xp[row * D + d]);
-        float Bv[4];
-        load4(Bp + row * N + 4 * q, Bv);
+        const float dl = s_dl[k][c];
+        const float u = dl * s_x[k][c];
+        const float4 Bv = *reinterpret_cast<const float4 *>(&s_B[k][4 * q]);
+        const float bv[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) H[k + 1][j] = fmaf(fast_exp2(dl * A2[j]), H[k][j], u * Bv[j]);
+        for (int j = 0; j < 4; ++j) {
+          aS[k][j] = fast_exp2(dl * A2[j]);
+          H[k + 1][j] = fmaf(aS[k][j], H[k][j], u * bv[j]);
+        }
       }
     }
 #pragma unroll
     for (int k = kSeg - 1; k >= 0; --k) {
       if (k < nt) {
-        const int64_t row = b * L + t0 + k;
-        const float raw = to_f32(dp[row * D + d]);
-        const float dl = step_size(raw, bias, a.delta_softplus);
-        const float xv = to_f32(xp[row * D + d]);
-        const float dyv = to_f32(gp[row * D + d]);
-        float Bv[4], Cv[4];
-        load4(Bp + row * N + 4 * q, Bv);
-        load4(Cp + row * N + 4 * q, Cv);
+        const float dl = s_dl[k][c];
+        const float xv = s_x[k][c];
+        const float g = s_g[k][c];
+        const float4 Bq = *reinterpret_cast<const float4 *>(&s_B[k][4 * q]);
+        const float4 Cq = *reinterpret_cast<const float4 *>(&s_C[k][4 * q]);
+        const float Bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w};
+        const float Cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
         float qp = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) qp = fmaf(Cv[j], H[k + 1][j], qp);
         const float qs = fmaf(Dd, xv, channel_sum<LPC>(qp));
-        float g = dyv, dzv = 0.f;
-        if (zp != nullptr) {
-          const float zv = to_f32(zp[row * D + d]);
-          const float sg = sigmoid_f(zv);
-          g = dyv * zv * sg;
-          dzv = dyv * qs * sg * fmaf(zv, 1.f - sg, 1.f);
-        }
         const float u = dl * xv;
         float v[8];
-        float ddl = 0.f, dxp = 0.f;
+        // ddelta = sum_n lam A a h_prev + x sum_n lam B; the second sum is dx's
+        float dda = 0.f, dxp = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float aj = fast_exp2(dl * A2[j]);
           lam[j] = fmaf(g, Cv[j], lam[j]);
           v[j] = lam[j] * u;
           v[4 + j] = g * H[k + 1][j];
-          const float p = aj * H[k][j];
-          ddl = fmaf(lam[j], fmaf(An[j], p, Bv[j] * xv), ddl);
-          dAacc[j] = fmaf(lam[j] * dl, p, dAacc[j]);
+          const float w = lam[j] * (aS[k][j] * H[k][j]);
+          dda = fmaf(An[j], w, dda);
+          dAacc[j] = fmaf(w, dl, dAacc[j]);
           dxp = fmaf(lam[j], Bv[j], dxp);
-          lam[j] *= aj;
+          lam[j] *= aS[k][j];
         }
-        ddl = channel_sum<LPC>(ddl);
         dxp = channel_sum<LPC>(dxp);
-        if (a.delta_softplus) ddl *= sigmoid_f(raw + bias);
-        if (active && q == 0) {
-          static_cast<T *>(a.dx)[row * D + d] = from_f32<T>(fmaf(dl, dxp, Dd * g));
-          static_cast<T *>(a.ddelta)[row * D + d] = from_f32<T>(ddl);
-          if (zp != nullptr) static_cast<T *>(a.dz)[row * D + d] = from_f32<T>(dzv);
+        const float ddl = fmaf(xv, dxp, channel_sum<LPC>(dda));
+        if (q == 0) {
+          s_o[0][k][c] = fmaf(dl, dxp, Dd * g);
+          s_o[1][k][c] = ddl;
+          s_o[2][k][c] = qs;
         }
         dDacc = fmaf(g, xv, dDacc);
-        dbacc += ddl;
-        if (!active) {
+        // dB / dC: partial sums over the row's channels, written by the
+        // lanes of the row's channels 0 and R/2
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = 0.f;
-        }
-        // butterfly over the channel bits of the lane: halving steps leave
-        // each lane with the sums of kCnt of the 8 values (indices base..),
-        // the remaining steps add the rest of the wave's channels
-        int base = 0;
-#pragma unroll
-        for (int st = 0; st < kHalv; ++st) {
-          const int m = 1 << (5 - st);
-          const int half = 4 >> st;
-          const bool hi = (lane & m) != 0;
-#pragma unroll
-          for (int i = 0; i < half; ++i) {
-            const float keep = hi ? v[half + i] : v[i];
-            const float send = hi ? v[i] : v[half + i];
-            v[i] = keep + __shfl_xor(send, m);
-          }
-          base += hi ? half : 0;
-        }
-        bool writer = true;
-#pragma unroll
-        for (int st = 0; st < kFull; ++st) {
-          const int m = 1 << (5 - kHalv - st);
-          v[0] += __shfl_xor(v[0], m);
-          writer = writer && (lane & m) == 0;
-        }
-        if (writer) {
-#pragma unroll
-          for (int i = 0; i < kCnt; ++i) {
-            const int idx = base + i;
-            s_red[wave][k][(idx / 4) * N + 4 * q + idx % 4] = v[i];
-          }
+        for (int i = 0; i < 8; ++i) v[i] = row_half_sum<LPC>(v[i]);
+        const int rc = (lane % 16) / LPC;  // channel within the row
+        if (rc % (kRowCh / kSPR) == 0) {
+          float *dst = &s_red[(wave * 4 + lane / 16) * kSPR + rc / (kRowCh / kSPR)][k][4 * q];
+          *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<float4 *>(dst + N) = make_float4(v[4], v[5], v[6], v[7]);
         }
       }
     }
     __syncthreads();
     for (int e = tid; e < nt * 2 * N; e += kBwdThreads) {
       const int k = e / (2 * N), j = e % (2 * N);
-      P[((b * L + t0 + k) * ntile + tile) * 2 * N + j] =
-          s_red[0][k][j] + s_red[1][k][j] + s_red[2][k][j] + s_red[3][k][j];
+      float v = 0.f;
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r) v += s_red[r][k][j];
+      P[((b * L + t0 + k) * ntile + tile) * 2 * N + j] = v;
     }
-    __syncthreads();
+    // per-token outputs, stored by the staging role (coalesced over channels)
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int k = k0 + e * LPC;
+      if (k < nt && s_active) {
+        const int64_t i = (b * L + t0 + k) * D + ds_raw;
+        const float ddl = s_o[1][k][cs] * slope[e];
+        static_cast<T *>(a.dx)[i] = from_f32<T>(s_o[0][k][cs]);
+        static_cast<T *>(a.ddelta)[i] = from_f32<T>(ddl);
+        if (has_z) static_cast<T *>(a.dz)[i] = from_f32<T>(s_o[2][k][cs] * wz[e]);
+        dbacc += ddl;
+      }
+    }
   }
 
+  // dbias partial of channel cs: the LPC staging threads of a channel add up
+  s_db[tid] = dbacc;
+  __syncthreads();
+  if (tid < kCh && s_active) {
+    float v = 0.f;
+#pragma unroll
+    for (int m = 0; m < LPC; ++m) v += s_db[tid + m * kCh];
+    PB[b * D + ds_raw] = v;
+  }
   if (!active) return;
   if (a.dh0 != nullptr)
     reinterpret_cast<float4 *>(a.dh0 + (b * D + d) * N)[q] = make_float4(lam[0], lam[1], lam[2], lam[3]);
   reinterpret_cast<float4 *>(PA + (b * D + d) * N)[q] = make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
-  if (q == 0) {
-    PD[b * D + d] = dDacc;
-    PB[b * D + d] = dbacc;
-  }
+  if (q == 0) PD[b * D + d] = dDacc;
 }
 
 // dB, dC: sum of the channel tiles' partials, tiles in order

@@ -260,8 +260,8 @@ def test_scan_bwd_workspace_size(lib):
     # entering states (1 segment) + dB|dC partials (1 tile) + dA partials + dD, dbias partials
     want = (2 * 1 * 64 * 16 + 2 * 8 * 1 * 32 + 2 * 64 * 16 + 2 * 2 * 64) * 4
     assert lib.ssm_scan_bwd_workspace_size(2, 8, 64, 16) == want
-    # 16-token segments, 64-channel tiles at N = 16
-    assert lib.ssm_scan_bwd_workspace_size(1, 17, 65, 16) == (2 * 65 * 16 + 17 * 2 * 32 + 65 * 16 + 2 * 65) * 4
+    # 8-token segments, 64-channel tiles at N = 16
+    assert lib.ssm_scan_bwd_workspace_size(1, 17, 65, 16) == (3 * 2 * 65 * 16 // 2 + 17 * 2 * 32 + 65 * 16 + 2 * 65) * 4
 
 
 def test_scan_bwd_validation(lib):
