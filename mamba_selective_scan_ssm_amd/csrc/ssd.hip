@@ -122,6 +122,40 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(SSDArgs a, fl
   __shared__ __attribute__((aligned(16))) uint16_t s_xlo[kP * kSlicePad];
   __shared__ __attribute__((aligned(16))) uint16_t s_bt[N * kSlicePad];
 
+  const uint16_t *xp = static_cast<const uint16_t *>(a.x);
+  const uint16_t *Bp = static_cast<const uint16_t *>(a.Bm);
+  // Raw x and B of one 64-token slice, loaded into registers one slice
+  // ahead so their latency overlaps the previous slice's MFMAs.  Unit u:
+  // token pair jp = u % 32 and an 8-wide column chunk u / 32, so that the
+  // transposed LDS writes of the 64 lanes of a wave fall in distinct banks
+  // (a token pair is one 32-bit word of a transposed row).
+  constexpr int kXU = (kSlice / 2) * (kP / 8);                      // x units per slice
+  constexpr int kXPer = (kXU + kThreads - 1) / kThreads;
+  constexpr int kBU = (kSlice / 2) * (N / 8);                       // B units per slice
+  constexpr int kBPer = (kBU + kThreads - 1) / kThreads;
+  uint4 xr[kXPer][2], br[kBPer][2];
+  auto load_slice = [&](int js) {
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int u = tid + i * kThreads;
+      const int jp = u % (kSlice / 2), pc = u / (kSlice / 2);
+      const int j0 = js + 2 * jp;
+      const int64_t base = ((b * L + t0 + j0) * H + h) * kP + pc * 8;
+      xr[i][0] = load8_raw(xp + base, u < kXU && j0 < nvalid);
+      xr[i][1] = load8_raw(xp + base + H * kP, u < kXU && j0 + 1 < nvalid);
+    }
+#pragma unroll
+    for (int i = 0; i < kBPer; ++i) {
+      const int u = tid + i * kThreads;
+      const int jp = u % (kSlice / 2), nc8 = u / (kSlice / 2);
+      const int j0 = js + 2 * jp;
+      const int64_t base = ((b * L + t0 + j0) * a.G + g) * N + nc8 * 8;
+      br[i][0] = load8_raw(Bp + base, u < kBU && j0 < nvalid);
+      br[i][1] = load8_raw(Bp + base + a.G * N, u < kBU && j0 + 1 < nvalid);
+    }
+  };
+  load_slice(0);
+
   const uint16_t *dtp = static_cast<const uint16_t *>(a.dt);
   const float A2 = a.A[h] * kLog2e;
   float dtv = 0.f;
@@ -140,44 +174,42 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(SSDArgs a, fl
 #pragma unroll
   for (int q = 0; q < TPW; ++q) acc[q][0] = acc[q][1] = f32x16{};
 
-  const uint16_t *xp = static_cast<const uint16_t *>(a.x);
-  const uint16_t *Bp = static_cast<const uint16_t *>(a.Bm);
-
   for (int js = 0; js < Q; js += kSlice) {
     // stage x (scaled, split) and B for tokens [js, js+64), transposed
-    // unit = (token pair jp, 8-wide column chunk)
-    for (int u = tid; u < (kSlice / 2) * (kP / 8); u += kThreads) {
-      const int jp = u / (kP / 8), pc = u % (kP / 8);
-      const int j0 = js + 2 * jp;
-      const int64_t base = ((b * L + t0 + j0) * H + h) * kP + pc * 8;
-      const uint4 r0 = load8_raw(xp + base, j0 < nvalid);
-      const uint4 r1 = load8_raw(xp + base + H * kP, j0 + 1 < nvalid);
-      const float w0 = s_w[j0], w1 = s_w[j0 + 1];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 h0v, l0v, h1v, l1v;
-        split_bf16(elem_f32(r0, e) * w0, h0v, l0v);
-        split_bf16(elem_f32(r1, e) * w1, h1v, l1v);
-        const int off = (pc * 8 + e) * kSlicePad + 2 * jp;
-        *reinterpret_cast<uint32_t *>(&s_xhi[off]) =
-            pack2(__builtin_bit_cast(uint16_t, h0v), __builtin_bit_cast(uint16_t, h1v));
-        *reinterpret_cast<uint32_t *>(&s_xlo[off]) =
-            pack2(__builtin_bit_cast(uint16_t, l0v), __builtin_bit_cast(uint16_t, l1v));
+    for (int i = 0; i < kXPer; ++i) {
+      const int u = tid + i * kThreads;
+      if (u < kXU) {
+        const int jp = u % (kSlice / 2), pc = u / (kSlice / 2);
+        const int j0 = js + 2 * jp;
+        const float w0 = s_w[j0], w1 = s_w[j0 + 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __bf16 h0v, l0v, h1v, l1v;
+          split_bf16(elem_f32(xr[i][0], e) * w0, h0v, l0v);
+          split_bf16(elem_f32(xr[i][1], e) * w1, h1v, l1v);
+          const int off = (pc * 8 + e) * kSlicePad + 2 * jp;
+          *reinterpret_cast<uint32_t *>(&s_xhi[off]) =
+              pack2(__builtin_bit_cast(uint16_t, h0v), __builtin_bit_cast(uint16_t, h1v));
+          *reinterpret_cast<uint32_t *>(&s_xlo[off]) =
+              pack2(__builtin_bit_cast(uint16_t, l0v), __builtin_bit_cast(uint16_t, l1v));
+        }
       }
     }
-    for (int u = tid; u < (kSlice / 2) * (N / 8); u += kThreads) {
-      const int jp = u / (N / 8), nc8 = u % (N / 8);
-      const int j0 = js + 2 * jp;
-      const int64_t base = ((b * L + t0 + j0) * a.G + g) * N + nc8 * 8;
-      const uint4 r0 = load8_raw(Bp + base, j0 < nvalid);
-      const uint4 r1 = load8_raw(Bp + base + a.G * N, j0 + 1 < nvalid);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int off = (nc8 * 8 + e) * kSlicePad + 2 * jp;
-        *reinterpret_cast<uint32_t *>(&s_bt[off]) = pack2(elem16(r0, e), elem16(r1, e));
+    for (int i = 0; i < kBPer; ++i) {
+      const int u = tid + i * kThreads;
+      if (u < kBU) {
+        const int jp = u % (kSlice / 2), nc8 = u / (kSlice / 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int off = (nc8 * 8 + e) * kSlicePad + 2 * jp;
+          *reinterpret_cast<uint32_t *>(&s_bt[off]) = pack2(elem16(br[i][0], e), elem16(br[i][1], e));
+        }
       }
     }
     __syncthreads();
+    if (js + kSlice < Q) load_slice(js + kSlice);
 #pragma unroll
     for (int ks = 0; ks < kSlice / 16; ++ks) {
       const int jo = ks * 16 + 8 * lg;
