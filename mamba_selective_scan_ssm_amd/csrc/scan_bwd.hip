@@ -79,17 +79,17 @@ __device__ __forceinline__ float row_half_sum(float v) {
 __host__ __device__ constexpr int64_t bwd_nseg(int64_t L) { return (L + kSeg - 1) / kSeg; }
 __host__ __device__ constexpr int64_t bwd_channels_per_block(int64_t N) { return 4 * kBwdThreads / N; }
 
-// Raw inputs of one segment for the workgroup, loaded into registers one
-// segment ahead.  Thread tid stages channel tid % kCh of the tile at tokens
+// Raw inputs of kTok tokens for the workgroup, loaded into registers one
+// block ahead.  Thread tid stages channel tid % kCh of the tile at tokens
 // tid / kCh + e * LPC (e < kE), and B/C entries tid + e * 256 of the
-// segment's (16, N) rows.  Indices past the sequence or the channel range
+// block's (kTok, N) rows.  Indices past the sequence or the channel range
 // are clamped (their values are never used).
-template <typename T, int LPC, bool kFull>
+template <typename T, int LPC, bool kFull, int kTok = kSeg>
 struct SegRegs {
   static constexpr int N = 4 * LPC;
   static constexpr int kCh = kBwdThreads / LPC;
-  static constexpr int kE = (kSeg * kCh + kBwdThreads - 1) / kBwdThreads;
-  static constexpr int kEB = (kSeg * N + kBwdThreads - 1) / kBwdThreads;
+  static constexpr int kE = (kTok * kCh + kBwdThreads - 1) / kBwdThreads;
+  static constexpr int kEB = (kTok * N + kBwdThreads - 1) / kBwdThreads;
   float d[kE], x[kE], z[kFull ? kE : 1], g[kFull ? kE : 1], bb[kEB], cc[kFull ? kEB : 1];
 
   __device__ __forceinline__ void load(const BwdArgs &a, int64_t b, int64_t t0, int64_t dst, int tid) {
@@ -110,7 +110,7 @@ struct SegRegs {
     }
 #pragma unroll
     for (int e = 0; e < kEB; ++e) {
-      const int idx = (tid + e * kBwdThreads) % (kSeg * N);
+      const int idx = (tid + e * kBwdThreads) % (kTok * N);
       const int64_t t = t0 + idx / N;
       const int64_t i = (b * L + (t < L ? t : L - 1)) * N + idx % N;
       bb[e] = to_f32(Bp[i]);
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
   constexpr int kRowCh = 16 / LPC;                // channels per row of 16 lanes
   constexpr int kSPR = kRowCh >= 2 ? 2 : 1;       // partial sums per row
   constexpr int kSlots = 16 * kSPR;               // per workgroup
-  __shared__ float s_red[kSlots][kSeg][2 * N];    // [slot][token][B sums | C sums]
+  __shared__ __attribute__((aligned(16))) float s_red[kSlots][kSeg][2 * N];  // [slot][token][B | C sums]
   __shared__ float s_db[kBwdThreads];
 
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64, q = tid % LPC;
@@ -174,36 +174,45 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
     h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
   }
   {
-    SegRegs<T, LPC, false> r;
-    if (nseg > 0) r.load(a, b, 0, dst, tid);
-    for (int64_t s = 0; s < nseg; ++s) {
-      const int64_t t0 = s * kSeg;
-      const int nt = static_cast<int>(L - t0 < kSeg ? L - t0 : kSeg);
-      if (active)
-        reinterpret_cast<float4 *>(ck + ((b * nseg + s) * D + d) * N)[q] =
-            make_float4(h[0], h[1], h[2], h[3]);
-      __syncthreads();  // the previous segment's LDS reads are done
+    // blocks of kP1 tokens (kM segments) per staging step where the staged
+    // block fits in the LDS of the pass-2 partial sums, which pass 1 does
+    // not use
+    constexpr int kM = (2 * 4 * kSeg * kCh + 4 * kSeg * N) <= kSlots * kSeg * 2 * N ? 4 : 1;
+    constexpr int kP1 = kM * kSeg;
+    float (*p_dl)[kCh] = kM > 1 ? reinterpret_cast<float (*)[kCh]>(&s_red[0][0][0]) : s_dl;
+    float (*p_x)[kCh] = kM > 1 ? p_dl + kP1 : s_x;
+    float (*p_B)[N] = kM > 1 ? reinterpret_cast<float (*)[N]>(p_x + kP1) : s_B;
+    const int64_t nblk = (L + kP1 - 1) / kP1;
+    SegRegs<T, LPC, false, kP1> r;
+    if (nblk > 0) r.load(a, b, 0, dst, tid);
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+      const int64_t t0 = blk * kP1;
+      const int nt = static_cast<int>(L - t0 < kP1 ? L - t0 : kP1);
+      __syncthreads();  // the previous block's LDS reads are done
 #pragma unroll
-      for (int e = 0; e < kE; ++e) {
+      for (int e = 0; e < SegRegs<T, LPC, false, kP1>::kE; ++e) {
         const int k = k0 + e * LPC;
-        if (k < kSeg) {
-          s_dl[k][cs] = step_size(r.d[e], bias_s, a.delta_softplus);
-          s_x[k][cs] = r.x[e];
+        if (k < kP1) {
+          p_dl[k][cs] = step_size(r.d[e], bias_s, a.delta_softplus);
+          p_x[k][cs] = r.x[e];
         }
       }
 #pragma unroll
-      for (int e = 0; e < kEB; ++e) {
+      for (int e = 0; e < SegRegs<T, LPC, false, kP1>::kEB; ++e) {
         const int idx = tid + e * kBwdThreads;
-        if (idx < kSeg * N) s_B[idx / N][idx % N] = r.bb[e];
+        if (idx < kP1 * N) p_B[idx / N][idx % N] = r.bb[e];
       }
-      if (s + 1 < nseg) r.load(a, b, t0 + kSeg, dst, tid);
+      if (blk + 1 < nblk) r.load(a, b, t0 + kP1, dst, tid);
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < kSeg; ++k) {
+      for (int k = 0; k < kP1; ++k) {
         if (k < nt) {
-          const float dl = s_dl[k][c];
-          const float u = dl * s_x[k][c];
-          const float4 Bv = *reinterpret_cast<const float4 *>(&s_B[k][4 * q]);
+          if (k % kSeg == 0 && active)  // the state entering segment (t0 + k) / kSeg
+            reinterpret_cast<float4 *>(ck + ((b * nseg + (t0 + k) / kSeg) * D + d) * N)[q] =
+                make_float4(h[0], h[1], h[2], h[3]);
+          const float dl = p_dl[k][c];
+          const float u = dl * p_x[k][c];
+          const float4 Bv = *reinterpret_cast<const float4 *>(&p_B[k][4 * q]);
           const float bv[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) h[j] = fmaf(fast_exp2(dl * A2[j]), h[j], u * bv[j]);
