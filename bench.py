@@ -278,11 +278,28 @@ def bench_bwd(torch, ssm, gen, steps=10):
     elems = B * L * D * N
     io = B * L * D * 2 * 7 + B * L * N * (2 * 2 + 4 * 2) + D * N * 4 * 2 + D * 4 * 2 + B * D * N * 4 * 3
     rate = elems / (ms * 1e-3)
+    # a training step's pair: the forward saving the 8-token segment states,
+    # then the backward reading them instead of recomputing them
+    saved = {}
+
+    def fwd_train():
+        saved["ck"] = ssm.scan_fwd_train(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0)[2]
+
+    fms, _, _ = time_calls(fwd_train, steps, 3, torch)
+    ck = saved["ck"]
+
+    def bwd_saved():
+        ssm.scan_bwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, dy, dhf, workspace=ws, h_ckpt=ck)
+
+    bms, _, _ = time_calls(bwd_saved, steps, 3, torch)
     return {"workload": "mamba2p8b_prefill_bf16 backward (B=8, L=4096, D=5120, N=16, bf16, all gradients)",
             "ms": ms, "ms_min": min_ms, "Gelem_per_s": rate / 1e9, "alg_bytes": io,
             "hbm_GBs": io / (ms * 1e-3) / 1e9, "hbm_frac": io / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "alu_frac": rate / BWD_ELEM_PEAK, "alu_peak_Telem_s": BWD_ELEM_PEAK / 1e12,
-            "workspace_bytes": ws.numel(), "traffic_bytes": load_traffic("scan_bwd", "bytes_per_call")}
+            "workspace_bytes": ws.numel(), "traffic_bytes": load_traffic("scan_bwd", "bytes_per_call"),
+            "with_saved_states": {"fwd_train_ms": fms, "bwd_ms": bms, "step_ms": fms + bms,
+                                  "bwd_alu_frac": elems / (bms * 1e-3) / BWD_ELEM_PEAK,
+                                  "saved_state_bytes": ck.numel() * 4}}
 
 
 def bench_pool_decode(torch, ssm, gen, steps=128):

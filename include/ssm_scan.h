@@ -156,6 +156,23 @@ ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype
                            const ssm_tuning *tuning, const ssm_delta_opts *dopts,
                            void *stream);
 
+/*
+ * ssm_scan_fwd_train -- ssm_scan_fwd_ex for a training step: also writes
+ * h_ckpt (B, ceil(L/8), D, N) fp32, the state entering every 8-token segment
+ * (segment 0: h0), which ssm_scan_bwd then reads instead of recomputing
+ * them (the mamba page's backward recomputes the forward states; here the
+ * forward keeps them at segment boundaries).  Always the lane-split
+ * schedule: N in {4, 8, 16, 32, 64}, Bm and Cm 16-byte aligned, x, delta, z,
+ * y aligned to two elements, D even, h_ckpt 16-byte aligned (else
+ * SSM_ERR_UNSUPPORTED).  y and h_final are bitwise those of ssm_scan_fwd_ex
+ * with tuning variant 3.  h_ckpt must not overlap any other argument.
+ */
+ssm_status ssm_scan_fwd_train(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                              const void *x, const void *delta, const float *A,
+                              const void *Bm, const void *Cm, const float *D_skip,
+                              const void *z, const float *h0, void *y, float *h_final,
+                              float *h_ckpt, const ssm_delta_opts *dopts, void *stream);
+
 /* Device workspace ssm_scan_fwd needs for these sizes and tuning (bytes). */
 size_t ssm_scan_fwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N,
                                    const ssm_tuning *tuning);
@@ -192,7 +209,9 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
  * token, and the gradient of the initial state is exp(delta_0 * A) times the
  * carried gradient at the first token.  With y the gated output of
  * ssm_scan_fwd_ex and h_final its final state, for the loss gradients dy
- * (B, L, D) and dh_final (B, D, N) (NULL = zero) this returns
+ * (B, L, D) and dh_final (B, D, N) (NULL = zero) this returns the outputs
+ * below.  h_ckpt: the segment states ssm_scan_fwd_train wrote for the same
+ * inputs (16-byte aligned), or NULL to recompute them here.
  *   dx, ddelta, dz : (B, L, D) dtype `dt` (ddelta is the gradient of the
  *                    delta INPUT, i.e. through bias and softplus when dopts
  *                    asks for them; dz only with z, else must be NULL)
@@ -215,7 +234,8 @@ ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
                         const void *x, const void *delta, const float *A,
                         const void *Bm, const void *Cm, const float *D_skip,
                         const void *z, const float *h0, const void *dy,
-                        const float *dh_final, void *dx, void *ddelta, void *dz,
+                        const float *dh_final, const float *h_ckpt, void *dx,
+                        void *ddelta, void *dz,
                         float *dA, float *dB, float *dC, float *dD, float *dh0,
                         float *d_delta_bias, const ssm_delta_opts *dopts,
                         void *workspace, size_t workspace_bytes, void *stream);

@@ -76,7 +76,9 @@ def lib():
         L.ssm_state_update_ex.restype = ctypes.c_int
         L.ssm_ssd_fwd_ex.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 10 + [vp, sz, vp, vp]
         L.ssm_ssd_fwd_ex.restype = ctypes.c_int
-        L.ssm_scan_bwd.argtypes = [i64] * 4 + [ctypes.c_int] + [vp] * 20 + [vp, sz, vp]
+        L.ssm_scan_bwd.argtypes = [i64] * 4 + [ctypes.c_int] + [vp] * 21 + [vp, sz, vp]
+        L.ssm_scan_fwd_train.argtypes = [i64] * 4 + [ctypes.c_int] + [vp] * 12 + [vp]
+        L.ssm_scan_fwd_train.restype = ctypes.c_int
         L.ssm_scan_bwd.restype = ctypes.c_int
         L.ssm_scan_bwd_workspace_size.argtypes = [i64] * 4
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
@@ -342,8 +344,35 @@ def scan_bwd_workspace_size(B, L, D, N) -> int:
     return int(lib().ssm_scan_bwd_workspace_size(B, L, D, N))
 
 
+def scan_fwd_train(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, delta_bias=None,
+                   delta_softplus=False):
+    """scan_fwd for a training step (ssm_scan_fwd_train): returns y, h_final
+    and h_ckpt (B, ceil(L/8), D, N), the state entering every 8-token
+    segment, for scan_bwd(..., h_ckpt=h_ckpt)."""
+    B, L, D = x.shape
+    N = A.shape[1]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    for nm, t in (("x", x), ("delta", delta), ("z", z)):
+        _check(nm, t, (B, L, D), dt, dev)
+    _check("Bm", Bm, (B, L, N), dt, dev)
+    _check("Cm", Cm, (B, L, N), dt, dev)
+    _check("A", A, (D, N), torch.float32, dev)
+    _check("D_skip", D_skip, (D,), torch.float32, dev)
+    _check("h0", h0, (B, D, N), torch.float32, dev)
+    _check("delta_bias", delta_bias, (D,), torch.float32, dev)
+    y = torch.empty((B, L, D), dtype=dt, device=dev)
+    hf = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+    ck = torch.empty((B, (L + 7) // 8, D, N), dtype=torch.float32, device=dev)
+    _call("ssm_scan_fwd_train", B, L, D, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+          _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(y), _ptr(hf), _ptr(ck), _dopts(delta_bias, delta_softplus),
+          _stream(dev))
+    return y, hf, ck
+
+
 def scan_bwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, dy=None, dh_final=None, *,
-             delta_bias=None, delta_softplus=False, want_dh0=True, want_dbias=False, workspace=None):
+             delta_bias=None, delta_softplus=False, want_dh0=True, want_dbias=False, workspace=None,
+             h_ckpt=None):
     """Gradients of scan_fwd (ssm_scan_bwd) for the output gradient dy and
     the final-state gradient dh_final (None = zero).  Returns a dict: dx,
     ddelta, dz (input dtype; dz None without z), dA, dB, dC (float32), dD
@@ -364,6 +393,7 @@ def scan_bwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, dy=None, dh_fina
     _check("h0", h0, (B, D, N), torch.float32, dev)
     _check("dh_final", dh_final, (B, D, N), torch.float32, dev)
     _check("delta_bias", delta_bias, (D,), torch.float32, dev)
+    _check("h_ckpt", h_ckpt, (B, (L + 7) // 8, D, N), torch.float32, dev)
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dx": torch.empty((B, L, D), dtype=dt, device=dev),
            "ddelta": torch.empty((B, L, D), dtype=dt, device=dev),
@@ -378,7 +408,7 @@ def scan_bwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, dy=None, dh_fina
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("ssm_scan_bwd", B, L, D, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
-          _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]),
+          _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(h_ckpt), _ptr(out["dx"]),
           _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
           _ptr(out["dD"]), _ptr(out["dh0"]), _ptr(out["dbias"]), _dopts(delta_bias, delta_softplus),
           _ptr(workspace), wsb, _stream(dev))

@@ -17,6 +17,8 @@ struct BwdArgs {
   const float *h0;           // (B, D, N) or null
   const void *dy;            // (B, L, D): gradient of the output y
   const float *dh_final;     // (B, D, N) or null: gradient of h_final
+  const float *h_ckpt;       // (B, ceil(L/8), D, N) states entering each 8-token
+                             // segment, saved by the forward; null: recomputed
   const float *delta_bias;   // (D) or null
   bool delta_softplus;
   void *dx, *ddelta, *dz;    // (B, L, D) in the input dtype (dz null without z)

@@ -231,6 +231,43 @@ ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype
   return hip_status(ssm::launch_scan_sequential(a, spl_of(tuning), s));
 }
 
+ssm_status ssm_scan_fwd_train(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                              const void *x, const void *delta, const float *A, const void *Bm,
+                              const void *Cm, const float *D_skip, const void *z, const float *h0,
+                              void *y, float *h_final, float *h_ckpt, const ssm_delta_opts *dopts,
+                              void *stream) {
+  if (B < 0 || L < 0 || D < 0 || N < 0 || !valid_dtype(dt) || !dopts_ok(dopts))
+    return SSM_ERR_INVALID_ARG;
+  if (N > SSM_SCAN_MAX_N) return SSM_ERR_UNSUPPORTED;
+  if (B == 0 || D == 0 || L == 0)  // no segment states to write
+    return ssm_scan_fwd_ex(B, L, D, N, dt, x, delta, A, Bm, Cm, D_skip, z, h0, y, h_final, nullptr, 0,
+                           nullptr, dopts, stream);
+  if (!h_ckpt) return SSM_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(h_ckpt) % 16 != 0) return SSM_ERR_UNSUPPORTED;
+  if (B > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
+  const int64_t es = esize(dt);
+  if ((L + 64) * D * es >= (int64_t(1) << 31) || (L + 64) * N * es >= (int64_t(1) << 31))
+    return SSM_ERR_UNSUPPORTED;
+  const int64_t nBLD = B * L * D, nBLN = B * L * N, nBDN = B * D * N;
+  const int64_t nCk = B * ((L + 7) / 8) * D * N;
+  if (!x || !delta || !y || (N > 0 && (!Bm || !Cm || !A))) return SSM_ERR_INVALID_ARG;
+  const Range ins[] = {{x, nBLD * es},   {delta, nBLD * es}, {A, D * N * 4}, {Bm, nBLN * es},
+                       {Cm, nBLN * es},  {D_skip, D * 4},    {z, nBLD * es}, {h0, nBDN * 4},
+                       {dbias_of(dopts), D * 4}};
+  const Range ry{y, nBLD * es}, rh{h_final, nBDN * 4}, rc{h_ckpt, nCk * 4};
+  if (overlaps_any(ry, ins) || overlaps_any(rh, ins) || overlaps_any(rc, ins)) return SSM_ERR_INVALID_ARG;
+  if (overlap(ry, rh) || overlap(ry, rc) || overlap(rh, rc)) return SSM_ERR_INVALID_ARG;
+  ssm::ScanArgs a{};
+  a.B = B; a.L = L; a.D = D; a.N = N;
+  a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
+  a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm;
+  a.D_skip = D_skip; a.z = z; a.h0 = h0; a.y = y; a.h_final = h_final;
+  a.delta_bias = dbias_of(dopts); a.delta_softplus = dsoft_of(dopts);
+  a.h_ckpt = h_ckpt;
+  if (!ssm::scan_lanesplit_supported(a)) return SSM_ERR_UNSUPPORTED;
+  return hip_status(ssm::launch_scan_lanesplit(a, static_cast<hipStream_t>(stream)));
+}
+
 ssm_status ssm_state_update(int64_t S, int64_t D, int64_t N, ssm_dtype dt, float *state,
                             const void *x, const void *delta, const float *A, const void *Bm,
                             const void *Cm, const float *D_skip, const void *z, void *y,
@@ -336,7 +373,8 @@ size_t ssm_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N) {
 ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
                         const void *x, const void *delta, const float *A, const void *Bm,
                         const void *Cm, const float *D_skip, const void *z, const float *h0,
-                        const void *dy, const float *dh_final, void *dx, void *ddelta, void *dz,
+                        const void *dy, const float *dh_final, const float *h_ckpt, void *dx,
+                        void *ddelta, void *dz,
                         float *dA, float *dB, float *dC, float *dD, float *dh0,
                         float *d_delta_bias, const ssm_delta_opts *dopts, void *workspace,
                         size_t workspace_bytes, void *stream) {
@@ -351,13 +389,14 @@ ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
   if (D * N > 0 && (!A || !dA)) return SSM_ERR_INVALID_ARG;
   if (!z && dz) return SSM_ERR_INVALID_ARG;
   auto a16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-  if (!a16(A) || !a16(h0) || !a16(dh_final) || !a16(dh0)) return SSM_ERR_UNSUPPORTED;
+  if (!a16(A) || !a16(h0) || !a16(dh_final) || !a16(dh0) || !a16(h_ckpt)) return SSM_ERR_UNSUPPORTED;
   const size_t need = ssm_scan_bwd_workspace_size(B, L, D, N);
   if (need > 0 && (!workspace || workspace_bytes < need || !a16(workspace))) return SSM_ERR_WORKSPACE;
   const Range ins[] = {{x, nX * es},     {delta, nX * es},    {A, D * N * 4},
                        {Bm, nBC * es},   {Cm, nBC * es},      {D_skip, D * 4},
                        {z, nX * es},     {h0, nS * 4},        {dy, nX * es},
-                       {dh_final, nS * 4}, {dbias_of(dopts), D * 4}, {workspace, static_cast<int64_t>(need)}};
+                       {dh_final, nS * 4}, {dbias_of(dopts), D * 4}, {workspace, static_cast<int64_t>(need)},
+                       {h_ckpt, B * ((L + 7) / 8) * D * N * 4}};
   const Range outs[] = {{dx, nX * es},  {ddelta, nX * es}, {dz, nX * es}, {dA, D * N * 4},
                         {dB, nBC * 4},  {dC, nBC * 4},     {dD, D * 4},   {dh0, nS * 4},
                         {d_delta_bias, D * 4}};
@@ -371,7 +410,7 @@ ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
   a.B = B; a.L = L; a.D = D; a.N = N;
   a.dt = dt == SSM_BF16 ? DType::BF16 : DType::F32;
   a.x = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.D_skip = D_skip; a.z = z;
-  a.h0 = h0; a.dy = dy; a.dh_final = dh_final;
+  a.h0 = h0; a.dy = dy; a.dh_final = dh_final; a.h_ckpt = h_ckpt;
   a.delta_bias = dbias_of(dopts); a.delta_softplus = dsoft_of(dopts);
   a.dx = dx; a.ddelta = ddelta; a.dz = dz; a.dA = dA; a.dB = dB; a.dC = dC;
   a.dD = dD; a.dbias = d_delta_bias; a.dh0 = dh0;

@@ -27,6 +27,9 @@ struct ScanArgs {
   // outside [0, pool_rows) skips the sequence.  Sequential schedules only.
   const int32_t *slots;
   int64_t pool_rows;
+  // Optional (lane-split schedule only): the state entering every 8-token
+  // segment of sequence b, at ((b * ceil(L/8) + s) * D + d) * N + n.
+  float *h_ckpt;
 };
 
 // State row of sequence b (false: skip the sequence).

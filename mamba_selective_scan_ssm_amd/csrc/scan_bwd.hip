@@ -18,7 +18,8 @@
 // Schedule.  A lane holds 4 consecutive states of a channel (N/4 lanes per
 // channel, as in the decode step) and a workgroup 1024/N channels of one
 // sequence.  Pass 1 runs the recurrence forward and writes the state that
-// enters every 8-token segment to the workspace.  Pass 2 walks the segments
+// enters every 8-token segment to the workspace (skipped when the forward
+// saved those states).  Pass 2 walks the segments
 // backwards: it reloads a segment's entering state, recomputes the
 // segment's 8 states into registers, then runs the reverse recurrence over
 // them.  A segment's inputs are loaded by the whole workgroup one segment
@@ -156,6 +157,8 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
   const int64_t nseg = bwd_nseg(L);
   float *ck = a.ws;                      // (B, nseg, D, N) entering states
   float *P = ck + B * nseg * D * N;      // (B, L, ntile, 2N) dB|dC partials
+  // the entering states: from the forward when it saved them, else pass 1
+  const float *ckr = a.h_ckpt ? a.h_ckpt : ck;
   float *PA = P + B * L * ntile * 2 * N; // (B, D, N) dA partials
   float *PD = PA + B * D * N;            // (B, D) dD partials
   float *PB = PD + B * D;                // (B, D) dbias partials
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
     const float4 v = reinterpret_cast<const float4 *>(a.h0 + (b * D + d) * N)[q];
     h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
   }
-  {
+  if (a.h_ckpt == nullptr) {
     // blocks of kP1 tokens (kM segments) per staging step where the staged
     // block fits in the LDS of the pass-2 partial sums, which pass 1 does
     // not use
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
   float4 hck = make_float4(0.f, 0.f, 0.f, 0.f);
   if (nseg > 0) {
     r.load(a, b, (nseg - 1) * kSeg, dst, tid);
-    if (active) hck = reinterpret_cast<const float4 *>(ck + ((b * nseg + nseg - 1) * D + d) * N)[q];
+    if (active) hck = reinterpret_cast<const float4 *>(ckr + ((b * nseg + nseg - 1) * D + d) * N)[q];
   }
   for (int64_t s = nseg - 1; s >= 0; --s) {
     const int64_t t0 = s * kSeg;
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
     H[0][0] = hck.x; H[0][1] = hck.y; H[0][2] = hck.z; H[0][3] = hck.w;
     if (s > 0) {
       r.load(a, b, t0 - kSeg, dst, tid);
-      if (active) hck = reinterpret_cast<const float4 *>(ck + ((b * nseg + s - 1) * D + d) * N)[q];
+      if (active) hck = reinterpret_cast<const float4 *>(ckr + ((b * nseg + s - 1) * D + d) * N)[q];
     }
     __syncthreads();
 #pragma unroll

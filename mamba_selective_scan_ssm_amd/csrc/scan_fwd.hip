@@ -380,7 +380,10 @@ __device__ __forceinline__ float word_elem(const uint32_t *w, int e) {
 #define SSM_LS_CYCLE 4
 #endif
 
-template <typename T, int LPC, int SPL, bool HAS_Z>
+// CK: also write the state entering every 8-token segment to a.h_ckpt
+// (B, ceil(L/8), D, N) -- what a training step's backward recomputes
+// otherwise.  A block of this kernel is exactly one such segment.
+template <typename T, int LPC, int SPL, bool HAS_Z, bool CK>
 __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   constexpr int TB = 8;                 // tokens per block
   constexpr int kCPW = kWave / LPC;     // channels per wave
@@ -478,6 +481,24 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   const int64_t nblk = (L + TB - 1) / TB;
   const int64_t ncyc = (nblk + kCyc - 1) / kCyc;
 
+  // segment states: the state after each block of a cycle, stored with the
+  // cycle's y (the state entering segment 0 is h0, stored here)
+  const bool ck_on = CK && d0 + c < D;
+  float *ckp = CK ? a.h_ckpt + (b * nblk * D + dc) * kN + q * SPL : nullptr;
+  float hk[CK ? kCyc : 1][SPL];
+  auto store_ckpt = [&](int64_t seg, const float *v) {
+    if constexpr (SPL % 4 == 0) {
+#pragma unroll
+      for (int s4 = 0; s4 < SPL / 4; ++s4)
+        reinterpret_cast<float4 *>(ckp + seg * D * kN)[s4] =
+            make_float4(v[4 * s4], v[4 * s4 + 1], v[4 * s4 + 2], v[4 * s4 + 3]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) ckp[seg * D * kN + s] = v[s];
+    }
+  };
+  if (CK && ck_on && nblk > 0) store_ckpt(0, h);
+
   // Raw inputs of one cycle of kCyc blocks.  Two sets alternate: while one
   // cycle is computed, the next one's loads are in flight.
   struct Raw {
@@ -553,6 +574,10 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
       }
       s_y[wave][j][c * LPC + q] = acc;
     }
+    if constexpr (CK) {
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) hk[u][s] = h[s];
+    }
   };
 
   // y of the slots of a block, packed as stored
@@ -594,6 +619,10 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
           const u32x2 pv = {yv[u][m][0], yv[u][m][1]};
           __builtin_amdgcn_raw_buffer_store_b64(pv, ry, vov, sov, 0);
         }
+      }
+      if constexpr (CK) {
+        const int64_t seg = cyc * kCyc + u + 1;  // entered after block cyc * kCyc + u
+        if (ck_on && seg < nblk) store_ckpt(seg, hk[u]);
       }
     }
   };
@@ -801,10 +830,17 @@ template <typename T, int LPC, int SPL>
 hipError_t launch_lanesplit_t(const ScanArgs &a, hipStream_t s) {
   constexpr int kChPerWG = 4 * (kWave / LPC);
   dim3 grid(static_cast<unsigned>((a.D + kChPerWG - 1) / kChPerWG), 1, static_cast<unsigned>(a.B));
-  if (a.z)
-    scan_lanesplit_kernel<T, LPC, SPL, true><<<grid, kWave * 4, 0, s>>>(a);
-  else
-    scan_lanesplit_kernel<T, LPC, SPL, false><<<grid, kWave * 4, 0, s>>>(a);
+  if (a.h_ckpt) {
+    if (a.z)
+      scan_lanesplit_kernel<T, LPC, SPL, true, true><<<grid, kWave * 4, 0, s>>>(a);
+    else
+      scan_lanesplit_kernel<T, LPC, SPL, false, true><<<grid, kWave * 4, 0, s>>>(a);
+  } else {
+    if (a.z)
+      scan_lanesplit_kernel<T, LPC, SPL, true, false><<<grid, kWave * 4, 0, s>>>(a);
+    else
+      scan_lanesplit_kernel<T, LPC, SPL, false, false><<<grid, kWave * 4, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

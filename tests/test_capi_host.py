@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     for n in ("ssm_scan_fwd", "ssm_scan_fwd_workspace_size", "ssm_state_update", "ssm_ssd_fwd",
               "ssm_ssd_fwd_workspace_size", "ssm_conv1d_fwd", "ssm_conv1d_update",
               "ssm_scan_fwd_ex", "ssm_state_update_ex", "ssm_ssd_fwd_ex", "ssm_decode_steps",
-              "ssm_scan_bwd", "ssm_scan_bwd_workspace_size",
+              "ssm_scan_bwd", "ssm_scan_bwd_workspace_size", "ssm_scan_fwd_train",
               "ssm_status_string", "ssm_version"):
         assert n in names
 
@@ -244,12 +244,13 @@ _DEFAULT = object()
 
 def bwd(lib, B=2, L=8, D=64, N=16, dt=F32, ws=_DEFAULT, ws_len=None, **over):
     """Every call below must be rejected on the host: none may reach a launch."""
-    names = ["x", "delta", "A", "Bm", "Cm", "D_skip", "z", "h0", "dy", "dh_final", "dx", "ddelta", "dz",
-             "dA", "dB", "dC", "dD", "dh0", "dbias"]
+    names = ["x", "delta", "A", "Bm", "Cm", "D_skip", "z", "h0", "dy", "dh_final", "h_ckpt", "dx", "ddelta",
+             "dz", "dA", "dB", "dC", "dD", "dh0", "dbias"]
     p = {k: Q[i] for i, k in enumerate(names)}
+    p["h_ckpt"] = None
     p.update(over)
     if ws is _DEFAULT:
-        ws = Q[20]
+        ws = Q[21]
     if ws_len is None:
         ws_len = lib.ssm_scan_bwd_workspace_size(B, L, D, N)
     return lib.ssm_scan_bwd(B, L, D, N, dt, *(p[k] for k in names), None, ws, ws_len, None)
@@ -276,10 +277,28 @@ def test_scan_bwd_validation(lib):
     assert bwd(lib, z=None) == INVALID                        # dz given without a gate
     assert bwd(lib, dB=None) == INVALID
     assert bwd(lib, A=ctypes.c_void_p(Q[2].value + 4)) == UNSUPPORTED
-    assert bwd(lib, dh0=ctypes.c_void_p(Q[17].value + 8)) == UNSUPPORTED
+    assert bwd(lib, dh0=ctypes.c_void_p(Q[18].value + 8)) == UNSUPPORTED
+    assert bwd(lib, h_ckpt=ctypes.c_void_p(Q[10].value + 8)) == UNSUPPORTED
     assert bwd(lib, ws=None) == WORKSPACE
     assert bwd(lib, ws_len=64) == WORKSPACE
-    assert bwd(lib, ws=ctypes.c_void_p(Q[20].value + 4)) == WORKSPACE
+    assert bwd(lib, ws=ctypes.c_void_p(Q[21].value + 4)) == WORKSPACE
     assert bwd(lib, dx=Q[0]) == INVALID                       # output on an input
-    assert bwd(lib, dC=Q[14]) == INVALID                      # two outputs on one buffer
-    assert bwd(lib, dA=Q[20]) == INVALID                      # output on the workspace
+    assert bwd(lib, dC=Q[15]) == INVALID                      # two outputs on one buffer
+    assert bwd(lib, dA=Q[21]) == INVALID                      # output on the workspace
+    assert bwd(lib, dB=Q[10], h_ckpt=Q[10]) == INVALID        # output on the saved states
+
+
+def test_scan_fwd_train_validation(lib):
+    def tr(B=2, L=16, D=64, N=16, dt=F32, **over):
+        names = ["x", "delta", "A", "Bm", "Cm", "D_skip", "z", "h0", "y", "h_final", "h_ckpt"]
+        p = {k: Q[i] for i, k in enumerate(names)}
+        p.update(over)
+        return lib.ssm_scan_fwd_train(B, L, D, N, dt, *(p[k] for k in names), None, None)
+    assert tr(B=-1) == INVALID
+    assert tr(h_ckpt=None) == INVALID
+    assert tr(h_ckpt=ctypes.c_void_p(Q[10].value + 4)) == UNSUPPORTED
+    assert tr(N=12) == UNSUPPORTED                            # lane-split schedule only
+    assert tr(D=63) == UNSUPPORTED                            # odd D
+    assert tr(h_ckpt=Q[9]) == INVALID                         # on h_final
+    assert tr(y=Q[0]) == INVALID
+    assert tr(N=65) == UNSUPPORTED

@@ -1,7 +1,7 @@
 """GPU parity of ssm_scan_bwd (gradients of the selective scan) against the
 oracle's backward, on the same seeded inputs and loss gradients.
 
-Small cases are compared whole (ragged L across 16-token segments, D across
+Small cases are compared whole (ragged L across 8-token segments, D across
 channel tiles, every supported N, gate / skip / h0 / dh_final / step-size
 transform on and off); the 2.8B-shaped case, at the size the bench times,
 on sampled channels, with dB/dC checked whole for one sequence and dA/dD on
@@ -146,3 +146,47 @@ def test_bwd_mamba2p8b_sampled(oracle_mod):
     r1 = _oracle(oracle_mod, inp, gr, channels=b1 * D + np.arange(D))
     assert_close(g["dB"][b1], r1["dB"][b1], "bf16", "dB")
     assert_close(g["dC"][b1], r1["dC"][b1], "bf16", "dC")
+    # the training pair the bench also times: forward saving the segment
+    # states, backward reading them -- bitwise the backward above
+    import mamba_selective_scan_ssm_amd as ssm
+    dev = [to_dev(v) for v in (inp.x, inp.delta, inp.A, inp.Bm, inp.Cm, inp.D_skip, inp.z, inp.h0)]
+    _, _, ck = ssm.scan_fwd_train(*dev)
+    g2 = ssm.scan_bwd(*dev, to_dev(gr.dy), to_dev(gr.dh_final), want_dbias=True, h_ckpt=ck)
+    torch.cuda.synchronize()
+    for k, v in g2.items():
+        if v is not None:
+            assert np.array_equal(to_np(v), g[k]), k
+
+
+@pytest.mark.parametrize("L,N,dtype", [(37, 16, "f32"), (64, 16, "bf16"), (20, 32, "f32"), (9, 4, "bf16"),
+                                       (16, 64, "f32")])
+def test_saved_segment_states(oracle_mod, L, N, dtype):
+    """ssm_scan_fwd_train: y and h_final bitwise those of the lane-split
+    forward; its segment states equal the oracle's state after 8s tokens; the
+    backward reading them is bitwise the backward that recomputes them."""
+    import mamba_selective_scan_ssm_amd as ssm
+    B, D = 2, 96
+    inp = gen.make_scan(B, L, D, N, dtype=dtype, seed=870 + L + N)
+    gr = gen.make_grads(B, L, D, N, dtype=dtype, seed=871 + L)
+    dev = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "A", "Bm", "Cm", "D_skip", "z", "h0")}
+    args = (dev["x"], dev["delta"], dev["A"], dev["Bm"], dev["Cm"], dev["D_skip"], dev["z"], dev["h0"])
+    _say("scan_fwd_train", L, N, dtype)
+    y, hf, ck = ssm.scan_fwd_train(*args)
+    y3, hf3 = ssm.scan_fwd(*args, variant=3)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y3) and torch.equal(hf, hf3)
+    nseg = (L + 7) // 8
+    assert ck.shape == (B, nseg, D, N)
+    ckn = to_np(ck)
+    assert np.array_equal(ckn[:, 0], inp.h0.astype(np.float64))
+    for sg in sorted({1, nseg // 2, nseg - 1} - {0}):
+        cut = lambda t: np.ascontiguousarray(t.f32[:, :8 * sg])
+        _, hs = oracle_mod.scan(cut(inp.x), cut(inp.delta), inp.A, cut(inp.Bm), cut(inp.Cm), inp.D_skip,
+                                cut(inp.z), inp.h0)
+        assert_close(ckn[:, sg], hs, dtype, f"segment state {sg}")
+    g0 = ssm.scan_bwd(*args, to_dev(gr.dy), to_dev(gr.dh_final), want_dbias=True)
+    g1 = ssm.scan_bwd(*args, to_dev(gr.dy), to_dev(gr.dh_final), want_dbias=True, h_ckpt=ck)
+    torch.cuda.synchronize()
+    for k in g0:
+        if g0[k] is not None:
+            assert torch.equal(g0[k], g1[k]), k
