@@ -94,13 +94,86 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
   *st = make_float4(h[0], h[1], h[2], h[3]);
 }
 
+// Single-token step with CPT channels per thread: every load of the CPT
+// channels (and the sequence's B/C slice, shared by them) is issued before
+// any of them is used, so a wave keeps CPT times the state bytes in flight.
+template <typename T, int LPC, int CPT>
+__global__ __launch_bounds__(kBlock) void state_step_kernel(StepArgs a) {
+  constexpr int N = 4 * LPC;
+  constexpr int kCh = kBlock / LPC;  // channels per pass of the block
+  const int q = threadIdx.x % LPC;
+  const int64_t s = blockIdx.y;
+  const int64_t D = a.D;
+  int64_t row = s;
+  if (a.slots != nullptr) {
+    const int32_t sl = a.slots[s];
+    if (sl < 0 || sl >= a.pool_rows) return;  // uniform over the block
+    row = sl;
+  }
+  const T *xp = static_cast<const T *>(a.x);
+  const T *dp = static_cast<const T *>(a.delta);
+  const T *zp = static_cast<const T *>(a.z);
+  float Bv[4], Cv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    Bv[j] = to_f32(static_cast<const T *>(a.Bm)[s * N + 4 * q + j]);
+    Cv[j] = to_f32(static_cast<const T *>(a.Cm)[s * N + 4 * q + j]);
+  }
+  int64_t d[CPT];
+  bool act[CPT];
+  float4 hv[CPT], Av[CPT];
+  float xv[CPT], dv[CPT], zv[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int64_t dr = (static_cast<int64_t>(blockIdx.x) * CPT + k) * kCh + threadIdx.x / LPC;
+    act[k] = dr < D;
+    d[k] = act[k] ? dr : D - 1;
+    hv[k] = reinterpret_cast<const float4 *>(a.state + (row * D + d[k]) * N)[q];
+    Av[k] = reinterpret_cast<const float4 *>(a.A + d[k] * N)[q];
+    xv[k] = to_f32(xp[s * D + d[k]]);
+    dv[k] = to_f32(dp[s * D + d[k]]);
+    zv[k] = zp ? to_f32(zp[s * D + d[k]]) : 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const float dl = step_size(dv[k], a.delta_bias ? a.delta_bias[d[k]] : 0.f, a.delta_softplus);
+    const float u = dl * xv[k];
+    float h[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
+    const float Ar[4] = {Av[k].x, Av[k].y, Av[k].z, Av[k].w};
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float dA = fast_exp2(dl * (Ar[j] * kLog2e));
+      h[j] = fmaf(dA, h[j], u * Bv[j]);
+      acc = fmaf(Cv[j], h[j], acc);
+    }
+#pragma unroll
+    for (int off = LPC / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPC);
+    hv[k] = make_float4(h[0], h[1], h[2], h[3]);
+    if (act[k] && q == 0) {
+      float v = acc;
+      if (a.D_skip) v = fmaf(a.D_skip[d[k]], xv[k], v);
+      if (zp) v *= silu(zv[k]);
+      static_cast<T *>(a.y)[s * D + d[k]] = from_f32<T>(v);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k)
+    if (act[k]) reinterpret_cast<float4 *>(a.state + (row * D + d[k]) * N)[q] = hv[k];
+}
+
 template <typename T, int LPC>
 hipError_t launch_t(const StepArgs &a, hipStream_t st) {
   constexpr int kCh = kBlock / LPC;
   dim3 grid(static_cast<unsigned>((a.D + kCh - 1) / kCh), static_cast<unsigned>(a.S));
-  if (a.T == 1)
-    state_update_kernel<T, LPC, 1><<<grid, kBlock, 0, st>>>(a);
-  else
+  if (a.T == 1) {
+#ifndef SSM_STEP_CPT
+#define SSM_STEP_CPT 2
+#endif
+    constexpr int kCPT = SSM_STEP_CPT;
+    dim3 g1(static_cast<unsigned>((a.D + kCPT * kCh - 1) / (kCPT * kCh)), static_cast<unsigned>(a.S));
+    state_step_kernel<T, LPC, kCPT><<<g1, kBlock, 0, st>>>(a);
+  } else
     state_update_kernel<T, LPC, 4><<<grid, kBlock, 0, st>>>(a);
   return hipGetLastError();
 }
