@@ -87,16 +87,17 @@ def test_conv_split_sequence_bitwise():
     assert torch.equal(torch.cat([y1, y2], 1), y) and torch.equal(s2, st)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_conv_decode_matches_oracle_and_prefill(oracle_mod, dtype):
-    """128 single-token steps (256 x 5120 at bf16; smaller at fp32) against
-    the oracle's convolution over the same tokens, and bitwise against the
-    GPU prefill of the whole sequence."""
+@pytest.mark.parametrize("dtype,D", [("f32", 600), ("bf16", 0), ("f32", 602), ("bf16", 302)])
+def test_conv_decode_matches_oracle_and_prefill(oracle_mod, dtype, D):
+    """Single-token steps (128 at 256 x 5120 bf16 -- D = 0 here -- fewer at
+    the other sizes; D not a multiple of 4 takes the one-channel-per-thread
+    kernel) against the oracle's convolution over the same tokens, and
+    bitwise against the GPU prefill of the whole sequence."""
     import mamba_selective_scan_ssm_amd as ssm
-    if dtype == "bf16":
+    if D == 0:
         d = gen.make_workload("conv_decode_256x5120_bf16")
     else:
-        d = gen.make_conv_decode(16, 600, 4, 40, dtype="f32", seed=512)
+        d = gen.make_conv_decode(16, D, 4, 40, dtype=dtype, seed=512 + D)
     _say("conv decode", dtype, d.S, d.D, d.steps)
     state = to_dev(d.state0)
     w, b = to_dev(d.w), to_dev(d.bias)
@@ -107,7 +108,7 @@ def test_conv_decode_matches_oracle_and_prefill(oracle_mod, dtype):
     x_seq = xs.transpose(0, 1).contiguous()        # (S, steps, D)
     y_pre, s_pre = ssm.conv1d_fwd(x_seq, w, b, to_dev(d.state0))
     assert torch.equal(y_dec, y_pre) and torch.equal(state, s_pre)
-    S = d.S if dtype == "f32" else 8               # oracle on a subset of sequences
+    S = d.S if D else 8                            # oracle on a subset of sequences
     ry, rs = oracle_mod.conv1d(d.x.f32.transpose(1, 0, 2)[:S], d.w, d.bias, d.state0[:S], act=True)
     assert_close(to_np(y_dec[:S]), ry, dtype, "y")
     np.testing.assert_array_equal(to_np(state[:S]), rs)
