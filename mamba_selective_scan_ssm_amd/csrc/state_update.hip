@@ -7,7 +7,11 @@
 // layout is chosen for the state stream: a channel's N states are N/4 lanes
 // holding four consecutive states each, so one 16-byte load per lane covers
 // the state tensor contiguously across the wave.  The y contraction over n is
-// finished with a butterfly over those N/4 lanes.  Sizes this layout does not
+// finished with a butterfly over those N/4 lanes.  The single-token step
+// gives each thread two channels whose loads are all issued before either is
+// used, so a wave keeps twice the state bytes in flight (the step is bound by
+// how many bytes are in flight, not by the instruction stream).  Sizes this
+// layout does not
 // cover (N not a multiple of 4, or a state/A not 16-byte aligned) go to the
 // per-lane scan kernel with L = T, whose lanes read and then write only their
 // own state row.
