@@ -78,16 +78,41 @@ __device__ __forceinline__ float row_half_sum(float v) {
 }
 
 __host__ __device__ constexpr int64_t bwd_nseg(int64_t L) { return (L + kSeg - 1) / kSeg; }
-__host__ __device__ constexpr int64_t bwd_channels_per_block(int64_t N) { return 4 * kBwdThreads / N; }
+// states per lane.  Two per lane at N = 16 doubles the waves but needs 127
+// VGPRs and 40 KB of LDS, so only 4 waves per SIMD fit and the 5 per SIMD of
+// the 2.8B shape run in two rounds (5.2 ms against 4.1 ms): 4 per lane.
+__host__ __device__ constexpr int64_t bwd_spl(int64_t) { return 4; }
+__host__ __device__ constexpr int64_t bwd_channels_per_block(int64_t N) {
+  return bwd_spl(N) * kBwdThreads / N;
+}
+
+// SPL consecutive floats (16- or 8-byte aligned)
+template <int SPL>
+__device__ __forceinline__ void ld_spl(const float *p, float *v) {
+  if constexpr (SPL == 4) {
+    const float4 r = *reinterpret_cast<const float4 *>(p);
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+  } else {
+    const float2 r = *reinterpret_cast<const float2 *>(p);
+    v[0] = r.x; v[1] = r.y;
+  }
+}
+template <int SPL>
+__device__ __forceinline__ void st_spl(float *p, const float *v) {
+  if constexpr (SPL == 4)
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  else
+    *reinterpret_cast<float2 *>(p) = make_float2(v[0], v[1]);
+}
 
 // Raw inputs of kTok tokens for the workgroup, loaded into registers one
 // block ahead.  Thread tid stages channel tid % kCh of the tile at tokens
 // tid / kCh + e * LPC (e < kE), and B/C entries tid + e * 256 of the
 // block's (kTok, N) rows.  Indices past the sequence or the channel range
 // are clamped (their values are never used).
-template <typename T, int LPC, bool kFull, int kTok = kSeg>
+template <typename T, int LPC, int SPL, bool kFull, int kTok = kSeg>
 struct SegRegs {
-  static constexpr int N = 4 * LPC;
+  static constexpr int N = SPL * LPC;
   static constexpr int kCh = kBwdThreads / LPC;
   static constexpr int kE = (kTok * kCh + kBwdThreads - 1) / kBwdThreads;
   static constexpr int kEB = (kTok * N + kBwdThreads - 1) / kBwdThreads;
@@ -120,9 +145,9 @@ struct SegRegs {
   }
 };
 
-template <typename T, int LPC>
+template <typename T, int LPC, int SPL>
 __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
-  constexpr int N = 4 * LPC;
+  constexpr int N = SPL * LPC;
   constexpr int kCh = kBwdThreads / LPC;        // channels per workgroup
   constexpr int kE = (kSeg * kCh + kBwdThreads - 1) / kBwdThreads;  // staged entries per thread
   constexpr int kEB = (kSeg * N + kBwdThreads - 1) / kBwdThreads;
@@ -163,19 +188,15 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
   float *PD = PA + B * D * N;            // (B, D) dD partials
   float *PB = PD + B * D;                // (B, D) dbias partials
 
-  const float4 Av = reinterpret_cast<const float4 *>(a.A + d * N)[q];
-  const float An[4] = {Av.x, Av.y, Av.z, Av.w};
-  float A2[4];
+  float An[SPL], A2[SPL];
+  ld_spl<SPL>(a.A + d * N + SPL * q, An);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) A2[j] = An[j] * kLog2e;
+  for (int j = 0; j < SPL; ++j) A2[j] = An[j] * kLog2e;
   const float Dd = a.D_skip ? a.D_skip[d] : 0.f;
 
   // ---- pass 1: forward, keeping the state that enters every segment ----
-  float h[4] = {0.f, 0.f, 0.f, 0.f};
-  if (a.h0 != nullptr && active) {
-    const float4 v = reinterpret_cast<const float4 *>(a.h0 + (b * D + d) * N)[q];
-    h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
-  }
+  float h[SPL] = {};
+  if (a.h0 != nullptr && active) ld_spl<SPL>(a.h0 + (b * D + d) * N + SPL * q, h);
   if (a.h_ckpt == nullptr) {
     // blocks of kP1 tokens (kM segments) per staging step where the staged
     // block fits in the LDS of the pass-2 partial sums, which pass 1 does
@@ -186,14 +207,14 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
     float (*p_x)[kCh] = kM > 1 ? p_dl + kP1 : s_x;
     float (*p_B)[N] = kM > 1 ? reinterpret_cast<float (*)[N]>(p_x + kP1) : s_B;
     const int64_t nblk = (L + kP1 - 1) / kP1;
-    SegRegs<T, LPC, false, kP1> r;
+    SegRegs<T, LPC, SPL, false, kP1> r;
     if (nblk > 0) r.load(a, b, 0, dst, tid);
     for (int64_t blk = 0; blk < nblk; ++blk) {
       const int64_t t0 = blk * kP1;
       const int nt = static_cast<int>(L - t0 < kP1 ? L - t0 : kP1);
       __syncthreads();  // the previous block's LDS reads are done
 #pragma unroll
-      for (int e = 0; e < SegRegs<T, LPC, false, kP1>::kE; ++e) {
+      for (int e = 0; e < SegRegs<T, LPC, SPL, false, kP1>::kE; ++e) {
         const int k = k0 + e * LPC;
         if (k < kP1) {
           p_dl[k][cs] = step_size(r.d[e], bias_s, a.delta_softplus);
@@ -201,7 +222,7 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int e = 0; e < SegRegs<T, LPC, false, kP1>::kEB; ++e) {
+      for (int e = 0; e < SegRegs<T, LPC, SPL, false, kP1>::kEB; ++e) {
         const int idx = tid + e * kBwdThreads;
         if (idx < kP1 * N) p_B[idx / N][idx % N] = r.bb[e];
       }
@@ -211,32 +232,28 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
       for (int k = 0; k < kP1; ++k) {
         if (k < nt) {
           if (k % kSeg == 0 && active)  // the state entering segment (t0 + k) / kSeg
-            reinterpret_cast<float4 *>(ck + ((b * nseg + (t0 + k) / kSeg) * D + d) * N)[q] =
-                make_float4(h[0], h[1], h[2], h[3]);
+            st_spl<SPL>(ck + ((b * nseg + (t0 + k) / kSeg) * D + d) * N + SPL * q, h);
           const float dl = p_dl[k][c];
           const float u = dl * p_x[k][c];
-          const float4 Bv = *reinterpret_cast<const float4 *>(&p_B[k][4 * q]);
-          const float bv[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+          float bv[SPL];
+          ld_spl<SPL>(&p_B[k][SPL * q], bv);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) h[j] = fmaf(fast_exp2(dl * A2[j]), h[j], u * bv[j]);
+          for (int j = 0; j < SPL; ++j) h[j] = fmaf(fast_exp2(dl * A2[j]), h[j], u * bv[j]);
         }
       }
     }
   }
 
   // ---- pass 2: segments in reverse ----
-  float lam[4] = {0.f, 0.f, 0.f, 0.f};
-  if (a.dh_final != nullptr && active) {
-    const float4 v = reinterpret_cast<const float4 *>(a.dh_final + (b * D + d) * N)[q];
-    lam[0] = v.x; lam[1] = v.y; lam[2] = v.z; lam[3] = v.w;
-  }
-  float dAacc[4] = {0.f, 0.f, 0.f, 0.f};
+  float lam[SPL] = {};
+  if (a.dh_final != nullptr && active) ld_spl<SPL>(a.dh_final + (b * D + d) * N + SPL * q, lam);
+  float dAacc[SPL] = {};
   float dDacc = 0.f, dbacc = 0.f;
-  SegRegs<T, LPC, true> r;
-  float4 hck = make_float4(0.f, 0.f, 0.f, 0.f);
+  SegRegs<T, LPC, SPL, true> r;
+  float hck[SPL] = {};
   if (nseg > 0) {
     r.load(a, b, (nseg - 1) * kSeg, dst, tid);
-    if (active) hck = reinterpret_cast<const float4 *>(ckr + ((b * nseg + nseg - 1) * D + d) * N)[q];
+    if (active) ld_spl<SPL>(ckr + ((b * nseg + nseg - 1) * D + d) * N + SPL * q, hck);
   }
   for (int64_t s = nseg - 1; s >= 0; --s) {
     const int64_t t0 = s * kSeg;
@@ -270,12 +287,13 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
         s_C[idx / N][idx % N] = r.cc[e];
       }
     }
-    float H[kSeg + 1][4];  // H[k] = state before token t0 + k
-    float aS[kSeg][4];     // exp(delta A) of token t0 + k
-    H[0][0] = hck.x; H[0][1] = hck.y; H[0][2] = hck.z; H[0][3] = hck.w;
+    float H[kSeg + 1][SPL];  // H[k] = state before token t0 + k
+    float aS[kSeg][SPL];     // exp(delta A) of token t0 + k
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) H[0][j] = hck[j];
     if (s > 0) {
       r.load(a, b, t0 - kSeg, dst, tid);
-      if (active) hck = reinterpret_cast<const float4 *>(ckr + ((b * nseg + s - 1) * D + d) * N)[q];
+      if (active) ld_spl<SPL>(ckr + ((b * nseg + s - 1) * D + d) * N + SPL * q, hck);
     }
     __syncthreads();
 #pragma unroll
@@ -283,10 +301,10 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
       if (k < nt) {
         const float dl = s_dl[k][c];
         const float u = dl * s_x[k][c];
-        const float4 Bv = *reinterpret_cast<const float4 *>(&s_B[k][4 * q]);
-        const float bv[4] = {Bv.x, Bv.y, Bv.z, Bv.w};
+        float bv[SPL];
+        ld_spl<SPL>(&s_B[k][SPL * q], bv);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < SPL; ++j) {
           aS[k][j] = fast_exp2(dl * A2[j]);
           H[k + 1][j] = fmaf(aS[k][j], H[k][j], u * bv[j]);
         }
@@ -298,23 +316,22 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
         const float dl = s_dl[k][c];
         const float xv = s_x[k][c];
         const float g = s_g[k][c];
-        const float4 Bq = *reinterpret_cast<const float4 *>(&s_B[k][4 * q]);
-        const float4 Cq = *reinterpret_cast<const float4 *>(&s_C[k][4 * q]);
-        const float Bv[4] = {Bq.x, Bq.y, Bq.z, Bq.w};
-        const float Cv[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
+        float Bv[SPL], Cv[SPL];
+        ld_spl<SPL>(&s_B[k][SPL * q], Bv);
+        ld_spl<SPL>(&s_C[k][SPL * q], Cv);
         float qp = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qp = fmaf(Cv[j], H[k + 1][j], qp);
+        for (int j = 0; j < SPL; ++j) qp = fmaf(Cv[j], H[k + 1][j], qp);
         const float qs = fmaf(Dd, xv, channel_sum<LPC>(qp));
         const float u = dl * xv;
-        float v[8];
+        float v[2 * SPL];  // dB then dC contributions of the lane's states
         // ddelta = sum_n lam A a h_prev + x sum_n lam B; the second sum is dx's
         float dda = 0.f, dxp = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < SPL; ++j) {
           lam[j] = fmaf(g, Cv[j], lam[j]);
           v[j] = lam[j] * u;
-          v[4 + j] = g * H[k + 1][j];
+          v[SPL + j] = g * H[k + 1][j];
           const float w = lam[j] * (aS[k][j] * H[k][j]);
           dda = fmaf(An[j], w, dda);
           dAacc[j] = fmaf(w, dl, dAacc[j]);
@@ -332,12 +349,12 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
         // dB / dC: partial sums over the row's channels, written by the
         // lanes of the row's channels 0 and R/2
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = row_half_sum<LPC>(v[i]);
+        for (int i = 0; i < 2 * SPL; ++i) v[i] = row_half_sum<LPC>(v[i]);
         const int rc = (lane % 16) / LPC;  // channel within the row
         if (rc % (kRowCh / kSPR) == 0) {
-          float *dst = &s_red[(wave * 4 + lane / 16) * kSPR + rc / (kRowCh / kSPR)][k][4 * q];
-          *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-          *reinterpret_cast<float4 *>(dst + N) = make_float4(v[4], v[5], v[6], v[7]);
+          float *dst = &s_red[(wave * 4 + lane / 16) * kSPR + rc / (kRowCh / kSPR)][k][SPL * q];
+          st_spl<SPL>(dst, v);
+          st_spl<SPL>(dst + N, v + SPL);
         }
       }
     }
@@ -375,8 +392,8 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
   }
   if (!active) return;
   if (a.dh0 != nullptr)
-    reinterpret_cast<float4 *>(a.dh0 + (b * D + d) * N)[q] = make_float4(lam[0], lam[1], lam[2], lam[3]);
-  reinterpret_cast<float4 *>(PA + (b * D + d) * N)[q] = make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
+    st_spl<SPL>(a.dh0 + (b * D + d) * N + SPL * q, lam);
+  st_spl<SPL>(PA + (b * D + d) * N + SPL * q, dAacc);
   if (q == 0) PD[b * D + d] = dDacc;
 }
 
@@ -419,8 +436,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_param_kernel(int64_t B, int64_
   dst[c] = v;
 }
 
-template <typename T, int LPC>
+template <typename T, int LPC, int SPL>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
+  static_assert(LPC * SPL > 0, "");
   const int64_t kCh = bwd_channels_per_block(a.N);
   const int64_t ntile = (a.D + kCh - 1) / kCh;
   const int64_t nseg = bwd_nseg(a.L);
@@ -430,7 +448,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
   float *PB = PD + a.B * a.D;
   if (ntile > 0 && a.B > 0) {
     dim3 grid(static_cast<unsigned>(ntile), static_cast<unsigned>(a.B));
-    scan_bwd_kernel<T, LPC><<<grid, kBwdThreads, 0, s>>>(a);
+    scan_bwd_kernel<T, LPC, SPL><<<grid, kBwdThreads, 0, s>>>(a);
   }
   const int64_t nbc = a.B * a.L * 2 * a.N;
   if (nbc > 0)
@@ -446,11 +464,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
 template <typename T>
 hipError_t launch_bwd_dt(const BwdArgs &a, hipStream_t s) {
   switch (a.N) {
-    case 4: return launch_bwd_t<T, 1>(a, s);
-    case 8: return launch_bwd_t<T, 2>(a, s);
-    case 16: return launch_bwd_t<T, 4>(a, s);
-    case 32: return launch_bwd_t<T, 8>(a, s);
-    case 64: return launch_bwd_t<T, 16>(a, s);
+    case 4: return launch_bwd_t<T, 1, 4>(a, s);
+    case 8: return launch_bwd_t<T, 2, 4>(a, s);
+    case 16: return launch_bwd_t<T, 4, 4>(a, s);
+    case 32: return launch_bwd_t<T, 8, 4>(a, s);
+    case 64: return launch_bwd_t<T, 16, 4>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
