@@ -122,3 +122,29 @@ def test_random_conv(oracle_mod, case):
     ry, rs = oracle_mod.conv1d(cv.x.f32, cv.w, cv.bias, cv.state0, act=True)
     assert_close(to_np(y), ry, c["dtype"], "y")
     assert np.array_equal(to_np(st), rs)
+
+
+def _ssd_case(i):
+    G = int(RNG.choice([1, 2]))
+    return dict(B=int(RNG.integers(1, 3)), L=int(RNG.choice([1, 63, 64, 65, 200, 300])), G=G,
+                H=G * int(RNG.integers(1, 4)), N=int(RNG.choice([32, 64, 96, 128, 160, 256])),
+                chunk=int(RNG.choice([64, 128, 256])), gate=bool(RNG.integers(0, 2)), seed=3400 + i)
+
+
+SSD_CASES = [_ssd_case(i) for i in range(10)]
+
+
+@pytest.mark.parametrize("case", SSD_CASES, ids=lambda c: "B{B}L{L}H{H}G{G}N{N}c{chunk}".format(**c))
+def test_random_ssd(oracle_mod, case):
+    import mamba_selective_scan_ssm_amd as ssm
+    c = case
+    w = gen.make_ssd(c["B"], c["L"], c["H"], 64, c["G"], c["N"], chunk=c["chunk"], dtype="bf16",
+                     seed=c["seed"], gate=c["gate"])
+    _say("random ssd", c)
+    y, hf = ssm.ssd_fwd(to_dev(w.x), to_dev(w.dt), to_dev(w.A), to_dev(w.Bm), to_dev(w.Cm), to_dev(w.D_skip),
+                        to_dev(w.z), to_dev(w.h0), chunk=c["chunk"])
+    torch.cuda.synchronize()
+    ry, rh = oracle_mod.ssd(w.x.f32, w.dt.f32, w.A, w.Bm.f32, w.Cm.f32, w.D_skip,
+                            None if w.z is None else w.z.f32, w.h0)
+    assert_close(to_np(y), ry, "bf16", "y")
+    assert_close(to_np(hf), rh, "bf16", "h_final")
