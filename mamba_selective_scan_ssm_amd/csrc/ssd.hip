@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(int64_t B, int64_t 
 // ---------------------------------------------------------------------------
 // 3. chunk outputs
 // ---------------------------------------------------------------------------
-// One workgroup of 16 waves per (chunk, group), looping over the group's
+// One workgroup of 8 waves per (chunk, group), looping over the group's
 // heads.  The chunk's B rows are staged in LDS once (row-major, as the
 // A-operand of CB^T = B C^T needs them) and each wave keeps the C fragments
 // of its row blocks in registers, so CB^T is recomputed per head from
@@ -287,12 +287,12 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(int64_t B, int64_t 
 // and row block I (rows i), one 32-wide p tile:
 //   Y_I = exp(S_i) C_I h_in^T + sum_{J <= I} M_IJ X_J,
 //   M_IJ[i][j] = CB^T[j][i] exp(S_i - S_j) dt_j (j <= i),
-// on the matrix cores with M formed in registers.  Each wave owns one row
-// block and one p tile; with 8 row blocks (Q = 256) the four waves that share
-// a SIMD take blocks s and 7 - s of both p tiles, so every SIMD does the same
-// 18 (I, J) blocks.
+// on the matrix cores with M formed in registers.  With 8 row blocks (Q =
+// 256) each wave owns one row block and both p tiles, and the two waves that
+// share a SIMD take blocks s and 7 - s, so every SIMD does the same 9 (I, J)
+// blocks and each block's M is formed once for both tiles.
 constexpr int kQPad = 256 + 8;
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 512;
 
 template <int N>
 __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs a, const float *ws_states) {
@@ -325,23 +325,24 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
   const uint16_t *zp = static_cast<const uint16_t *>(a.z);
   const int nIB = Q / 32;
 
-  // this wave's row block IA (IA < 0: none; IB is never used) and p tile.
-  // Wave k runs on SIMD k % 4; with 8 row blocks the four waves of a SIMD
-  // take blocks s and 7 - s of both p tiles, 18 (I, J) blocks per SIMD.
-  int IA, IB = -1, pt;
+  // this wave's row block IA (IA < 0: none) and its p tiles pt0 .. pt0 +
+  // npt - 1.  Wave k runs on SIMD k % 4; with 8 row blocks the two waves of
+  // a SIMD take blocks s and 7 - s, each with both p tiles, so a block's
+  // C B^T and decayed scores are formed once for both tiles and every SIMD
+  // does the same 9 (I, J) blocks.
+  int IA, pt0, npt;
   {
     const int sm = wave % 4, m = wave / 4;
     if (nIB == 8) {
-      IA = (m % 2 == 0) ? sm : 7 - sm; pt = m / 2;
+      IA = (m == 0) ? sm : 7 - sm; pt0 = 0; npt = 2;
     } else if (nIB == 4) {
-      IA = wave < 8 ? wave % 4 : -1; pt = (wave / 4) % 2;
+      IA = sm; pt0 = m; npt = 1;
     } else {
-      IA = wave < 4 ? wave % 2 : -1; pt = (wave / 2) % 2;
+      IA = wave < 4 ? wave % 2 : -1; pt0 = (wave / 2) % 2; npt = 1;
     }
   }
   const bool active = IA >= 0;
   const int iA = (active ? IA : 0) * 32 + l32;  // C row of this lane
-  const int p_lane = pt * 32 + l32;
 
   // stage the chunk's B rows (zeros past the end)
   for (int u = tid; u < 256 * (N / 8); u += kScanThreads) {
@@ -472,17 +473,26 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
         const_cast<uint16_t *>(zp ? zp + head0 : yp + head0), 0, yz_bytes, 0x00020000);
     auto row_block = [&](int I, const bf16x8 *cf) {
       const int i_lane = I * 32 + l32;
-      f32x16 acc = f32x16{};
+      f32x16 acc[2] = {f32x16{}, f32x16{}};  // p tiles pt0, pt0 + 1
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = p_lane * kNPad + ks * 16 + 8 * lg;
-        const bf16x8 vh = *reinterpret_cast<const bf16x8 *>(&s_hh[off]);
-        const bf16x8 vl = *reinterpret_cast<const bf16x8 *>(&s_hl[off]);
-        acc = mfma(cf[ks], vh, acc);
-        acc = mfma(cf[ks], vl, acc);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (q < npt) {
+            const int off = ((pt0 + q) * 32 + l32) * kNPad + ks * 16 + 8 * lg;
+            const bf16x8 vh = *reinterpret_cast<const bf16x8 *>(&s_hh[off]);
+            const bf16x8 vl = *reinterpret_cast<const bf16x8 *>(&s_hl[off]);
+            acc[q] = mfma(cf[ks], vh, acc[q]);
+            acc[q] = mfma(cf[ks], vl, acc[q]);
+          }
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] *= fast_exp2(s_S[I * 32 + 8 * (r / 4) + 4 * lg + (r % 4)]);
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(s_S[I * 32 + 8 * (r / 4) + 4 * lg + (r % 4)]);
+        acc[0][r] *= e;
+        acc[1][r] *= e;
+      }
       const float S_i = s_S[i_lane < Q ? i_lane : Q - 1];
       for (int J = 0; J <= I; ++J) {
         const f32x16 cb = cb_block(J, cf);
@@ -498,29 +508,42 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
           ml[r / 8][r % 8] = x2;
         }
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int jb = J * 32 + 16 * k2 + 4 * lg;
-          const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&s_x[p_lane * kQPad + jb]);
-          const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&s_x[p_lane * kQPad + jb + 8]);
-          const bf16x8 xf = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          acc = mfma(mh[k2], xf, acc);
-          acc = mfma(ml[k2], xf, acc);
+        for (int q = 0; q < 2; ++q) {
+          if (q < npt) {
+            const int pl = (pt0 + q) * 32 + l32;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+              const int jb = J * 32 + 16 * k2 + 4 * lg;
+              const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&s_x[pl * kQPad + jb]);
+              const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&s_x[pl * kQPad + jb + 8]);
+              const bf16x8 xf = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+              acc[q] = mfma(mh[k2], xf, acc[q]);
+              acc[q] = mfma(ml[k2], xf, acc[q]);
+            }
+          }
         }
       }
       // y and z of this (chunk, head) through buffer resources with 32-bit
       // offsets: row i, column p at ((i * H) * P + p) * 2 bytes
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = I * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-        const float xv = bf_to_f(bf16_bits(s_x[p_lane * kQPad + i]));
-        float v = fmaf(Dh, xv, acc[r]);
-        const int off = (i * static_cast<int>(H) * kP + p_lane) * 2;
-        if (zp) {
-          const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
-          v *= silu(__uint_as_float(zb << 16));
+      for (int q = 0; q < 2; ++q) {
+        if (q < npt) {
+          const int pl = (pt0 + q) * 32 + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = I * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+            const float xv = bf_to_f(bf16_bits(s_x[pl * kQPad + i]));
+            float v = fmaf(Dh, xv, acc[q][r]);
+            const int off = (i * static_cast<int>(H) * kP + pl) * 2;
+            if (zp) {
+              const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
+              v *= silu(__uint_as_float(zb << 16));
+            }
+            // rows past the chunk's valid tokens lie past the resource: dropped
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)), ry, off,
+                                                  0, 0);
+          }
         }
-        // rows past the chunk's valid tokens lie past the resource: dropped
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)), ry, off, 0, 0);
       }
     };
     row_block(IA, cfA);
