@@ -356,14 +356,19 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     cfA[ks] = load8(Cp + ((b * L + t0 + iA) * G + g) * N + ks * 16 + 8 * lg, active && iA < nvalid);
+  // two accumulation chains over the K steps, added at the end, so the
+  // dependent MFMA chain is half as long
   auto cb_block = [&](int J, const bf16x8 *cf) {
-    f32x16 acc = f32x16{};
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(&s_b[(J * 32 + l32) * kNPad + ks * 16 + 8 * lg]);
-      acc = mfma(bfr, cf[ks], acc);
+      if (ks % 2 == 0)
+        acc0 = mfma(bfr, cf[ks], acc0);
+      else
+        acc1 = mfma(bfr, cf[ks], acc1);
     }
-    return acc;
+    return acc0 + acc1;
   };
 
   // per-head inputs in flight: x (pairs of rows, 8 columns each) and (wave
