@@ -290,8 +290,9 @@ ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtyp
  * Bm, Cm    : (B, L, G, N) dtype `dt`;  A, D_skip : (H) fp32 (D_skip may be NULL)
  * h0, h_final : (B, H, P, N) fp32 or NULL.  z may be NULL.
  * Supported: dt == SSM_BF16; P == 64; N a multiple of 32 with
- * N <= SSM_SSD_MAX_N; chunk in {64, 128, 256}; H % G == 0.  Other sizes
- * return SSM_ERR_UNSUPPORTED.  Any L >= 0 (a ragged last chunk is handled).
+ * N <= SSM_SSD_MAX_N; chunk in {64, 128, 256}; H % G == 0; x, Bm, Cm,
+ * h0, h_final and workspace 16-byte aligned.  Other sizes return
+ * SSM_ERR_UNSUPPORTED.  Any L >= 0 (a ragged last chunk is handled).
  */
 ssm_status ssm_ssd_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                        int64_t N, int64_t chunk, ssm_dtype dt, const void *x,

@@ -445,6 +445,12 @@ ssm_status ssm_ssd_fwd_ex(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
   if (P != 64 || N % 32 != 0 || N > SSM_SSD_MAX_N || N == 0) return SSM_ERR_UNSUPPORTED;
   if (chunk != 64 && chunk != 128 && chunk != 256) return SSM_ERR_UNSUPPORTED;
   if (G <= 0 || H % G != 0) return SSM_ERR_UNSUPPORTED;
+  {
+    // x, B, C are read and the states moved in 16-byte pieces
+    auto a16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    if (!a16(x) || !a16(Bm) || !a16(Cm) || !a16(h0) || !a16(h_final) || !a16(workspace))
+      return SSM_ERR_UNSUPPORTED;
+  }
   if (B == 0 || H == 0) return SSM_OK;
   const int64_t nc = (L + chunk - 1) / chunk;
   if (B > kMaxGridYZ || H > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;

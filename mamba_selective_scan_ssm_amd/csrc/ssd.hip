@@ -253,25 +253,176 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(SSDArgs a, fl
   }
 }
 
+// Chunk states for N <= 128: one workgroup of 8 waves per (chunk, group)
+// loops over the group's heads, so the chunk's B (shared by the heads of the
+// group) is read once instead of once per head.  B^T is staged through LDS
+// once and each wave keeps its MFMA fragments of it (its 32 states n, every
+// token of the chunk) in registers for all the heads; the LDS then holds x.
+// Per head: the cumulative decay, then x scaled by exp(S_end - S_j) dt_j,
+// split into bf16 hi + lo and transposed into LDS, then one 32x32 output tile
+// per wave over the chunk's tokens.  The next head's x and dt are loaded into
+// registers while the current head computes.  The LDS use (67.6 KB) leaves
+// room for two workgroups per CU, one staging while the other multiplies.
+constexpr int kCSThreads = 512;
+constexpr int kCSPad = 256 + 8;
+
+template <int N, int KS>  // KS = chunk / 16
+__global__ __launch_bounds__(kCSThreads, 4) void ssd_chunk_state_group_kernel(SSDArgs a, float *ws_states,
+                                                                              float *ws_decay) {
+  constexpr int Q = 16 * KS;
+  const int64_t c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int64_t nc = gridDim.x, H = a.H, L = a.L, G = a.G;
+  const int64_t HPG = H / G;
+  const int64_t t0 = c * Q;
+  const int nvalid = static_cast<int>((L - t0) < Q ? (L - t0) : Q);
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64, lg = lane / 32, l32 = lane % 32;
+  constexpr int NT = N / 32;                               // n tiles
+  constexpr int kXU = (256 / 2) * (kP / 8) / kCSThreads;  // x units per thread at Q = 256
+  static_assert(kXU * kCSThreads == (256 / 2) * (kP / 8), "x staging must tile");
+  static_assert(N <= 2 * kP, "B^T must fit the x buffer");
+
+  __shared__ float s_S[256];
+  __shared__ float s_w[256];
+  __shared__ float s_wave[kCSThreads / 64];
+  // B^T ([n][j]) at the start, then (x w)^T hi ([p][j]) and lo (rows kP..)
+  __shared__ __attribute__((aligned(16))) uint16_t s_buf[2 * kP * kCSPad];
+  uint16_t *s_xh = s_buf, *s_xl = s_buf + kP * kCSPad;
+
+  const uint16_t *xp = static_cast<const uint16_t *>(a.x);
+  const uint16_t *Bp = static_cast<const uint16_t *>(a.Bm);
+  const uint16_t *dtp = static_cast<const uint16_t *>(a.dt);
+
+  // x of a head, raw, and its dt (one per thread)
+  uint4 xr[kXU][2];
+  float dtv = 0.f;
+  auto prefetch = [&](int64_t h) {
+#pragma unroll
+    for (int k = 0; k < kXU; ++k) {
+      const int u = tid + k * kCSThreads;
+      const int jp = u % 128, pc = u / 128;
+      const int j0 = 2 * jp;
+      const int64_t base = ((b * L + t0 + j0) * H + h) * kP + pc * 8;
+      xr[k][0] = load8_raw(xp + base, j0 < nvalid);
+      xr[k][1] = load8_raw(xp + base + H * kP, j0 + 1 < nvalid);
+    }
+    dtv = tid < nvalid ? step_size(bf_to_f(bf16_bits(dtp[(b * L + t0 + tid) * H + h])),
+                                   a.dt_bias ? a.dt_bias[h] : 0.f, a.dt_softplus)
+                       : 0.f;
+  };
+  prefetch(g * HPG);
+
+  // B^T of the chunk; unit u: token pair u % 128, 8-wide n chunk u / 128
+  // (consecutive lanes on consecutive token pairs: distinct LDS banks)
+  for (int u = tid; u < 128 * (N / 8); u += kCSThreads) {
+    const int jp = u % 128, nc8 = u / 128;
+    const int j0 = 2 * jp;
+    const int64_t base = ((b * L + t0 + j0) * G + g) * N + nc8 * 8;
+    const uint4 r0 = load8_raw(Bp + base, j0 < nvalid);
+    const uint4 r1 = load8_raw(Bp + base + G * N, j0 + 1 < nvalid);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<uint32_t *>(&s_buf[(nc8 * 8 + e) * kCSPad + j0]) = pack2(elem16(r0, e), elem16(r1, e));
+  }
+  __syncthreads();
+  const int pt = wave % 2, nt = wave / 2;  // this wave's output tile
+  const int p = pt * 32 + l32, n = nt * 32 + l32;
+  bf16x8 bfr[KS];                          // B^T fragments of tokens 16 ks + 8 lg .. + 7
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    bfr[ks] = nt < NT ? *reinterpret_cast<const bf16x8 *>(&s_buf[n * kCSPad + ks * 16 + 8 * lg]) : bf16x8{};
+
+  for (int64_t hh = 0; hh < HPG; ++hh) {
+    const int64_t h = g * HPG + hh;
+    const float A2 = a.A[h] * kLog2e;
+    // (its barriers also end the reads of B^T and of the previous head's x)
+    block_inclusive_scan(dtv * A2, s_S, s_wave, Q);
+    const float S_end = s_S[Q - 1];
+    if (tid < Q) s_w[tid] = fast_exp2(S_end - s_S[tid]) * dtv;
+    if (tid == 0) ws_decay[(b * nc + c) * H + h] = fast_exp2(S_end);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kXU; ++k) {
+      const int u = tid + k * kCSThreads;
+      const int jp = u % 128, pc = u / 128;
+      const int j0 = 2 * jp;
+      const float w0 = j0 < Q ? s_w[j0] : 0.f, w1 = j0 + 1 < Q ? s_w[j0 + 1] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 h0v, l0v, h1v, l1v;
+        split_bf16(elem_f32(xr[k][0], e) * w0, h0v, l0v);
+        split_bf16(elem_f32(xr[k][1], e) * w1, h1v, l1v);
+        const int off = (pc * 8 + e) * kCSPad + j0;
+        *reinterpret_cast<uint32_t *>(&s_xh[off]) =
+            pack2(__builtin_bit_cast(uint16_t, h0v), __builtin_bit_cast(uint16_t, h1v));
+        *reinterpret_cast<uint32_t *>(&s_xl[off]) =
+            pack2(__builtin_bit_cast(uint16_t, l0v), __builtin_bit_cast(uint16_t, l1v));
+      }
+    }
+    __syncthreads();
+    if (hh + 1 < HPG) prefetch(h + 1);
+    if (nt < NT) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int jo = ks * 16 + 8 * lg;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(&s_xh[p * kCSPad + jo]);
+        const bf16x8 al = *reinterpret_cast<const bf16x8 *>(&s_xl[p * kCSPad + jo]);
+        acc = mfma(ah, bfr[ks], acc);
+        acc = mfma(al, bfr[ks], acc);
+      }
+      float *out = ws_states + ((b * nc + c) * H + h) * (int64_t)kP * N;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pr = pt * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        out[pr * N + n] = acc[r];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 2. state passing
 // ---------------------------------------------------------------------------
+// Each thread carries four consecutive state elements of one (b, h) over the
+// chunks, in place: the slot of chunk c receives the state entering chunk c.
+// The chunk loop loads kBatch chunks' updates before it stores any carry, so
+// a thread keeps kBatch 16-byte loads in flight (a load of chunk c + 1 would
+// otherwise wait for the store to chunk c, which may alias it).
+constexpr int kPassBatch = 8;
+
 __global__ __launch_bounds__(256) void ssd_state_pass_kernel(int64_t B, int64_t H, int64_t PN,
                                                               int64_t nc, const float *h0,
                                                               const float *ws_decay,
                                                               float *ws_states, float *h_final) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= B * H * PN) return;
-  const int64_t bh = i / PN, e = i % PN;
+  const int64_t i4 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t PN4 = PN / 4;
+  if (i4 >= B * H * PN4) return;
+  const int64_t bh = i4 / PN4, e4 = i4 % PN4;
   const int64_t b = bh / H, h = bh % H;
-  float carry = h0 ? h0[i] : 0.f;
-  for (int64_t c = 0; c < nc; ++c) {
-    const int64_t k = ((b * nc + c) * H + h) * PN + e;
-    const float dS = ws_states[k];
-    ws_states[k] = carry;
-    carry = fmaf(ws_decay[(b * nc + c) * H + h], carry, dS);
+  float4 carry = h0 ? reinterpret_cast<const float4 *>(h0)[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 *st = reinterpret_cast<float4 *>(ws_states);
+  for (int64_t c0 = 0; c0 < nc; c0 += kPassBatch) {
+    float4 dS[kPassBatch];
+    float dc[kPassBatch];
+#pragma unroll
+    for (int k = 0; k < kPassBatch; ++k) {
+      if (c0 + k < nc) {
+        dS[k] = st[((b * nc + c0 + k) * H + h) * PN4 + e4];
+        dc[k] = ws_decay[(b * nc + c0 + k) * H + h];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPassBatch; ++k) {
+      if (c0 + k < nc) {
+        st[((b * nc + c0 + k) * H + h) * PN4 + e4] = carry;
+        carry.x = fmaf(dc[k], carry.x, dS[k].x);
+        carry.y = fmaf(dc[k], carry.y, dS[k].y);
+        carry.z = fmaf(dc[k], carry.z, dS[k].z);
+        carry.w = fmaf(dc[k], carry.w, dS[k].w);
+      }
+    }
   }
-  if (h_final) h_final[i] = carry;
+  if (h_final) reinterpret_cast<float4 *>(h_final)[i4] = carry;
 }
 
 // ---------------------------------------------------------------------------
@@ -749,14 +900,24 @@ hipError_t launch_n(const SSDArgs &a, void *ws, hipStream_t s) {
   float *states = static_cast<float *>(ws);
   float *decay = states + a.B * nc * a.H * kP * N;
   if (a.L == 0) {
-    const int64_t tot = a.B * a.H * kP * N;
+    const int64_t tot = a.B * a.H * kP * N / 4;
     ssd_state_pass_kernel<<<static_cast<unsigned>((tot + 255) / 256), 256, 0, s>>>(
         a.B, a.H, kP * N, 0, a.h0, decay, states, a.h_final);
     return hipGetLastError();
   }
   dim3 grid(static_cast<unsigned>(nc), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
-  ssd_chunk_state_kernel<N><<<grid, kThreads, 0, s>>>(a, states, decay);
-  const int64_t tot = a.B * a.H * kP * N;
+  if constexpr (N <= 128) {
+    dim3 grid_g(static_cast<unsigned>(nc), static_cast<unsigned>(a.G), static_cast<unsigned>(a.B));
+    if (a.chunk == 64)
+      ssd_chunk_state_group_kernel<N, 4><<<grid_g, kCSThreads, 0, s>>>(a, states, decay);
+    else if (a.chunk == 128)
+      ssd_chunk_state_group_kernel<N, 8><<<grid_g, kCSThreads, 0, s>>>(a, states, decay);
+    else
+      ssd_chunk_state_group_kernel<N, 16><<<grid_g, kCSThreads, 0, s>>>(a, states, decay);
+  } else {
+    ssd_chunk_state_kernel<N><<<grid, kThreads, 0, s>>>(a, states, decay);
+  }
+  const int64_t tot = a.B * a.H * kP * N / 4;  // float4 per thread
   ssd_state_pass_kernel<<<static_cast<unsigned>((tot + 255) / 256), 256, 0, s>>>(
       a.B, a.H, kP * N, nc, a.h0, decay, states, a.h_final);
   if constexpr (N <= 128) {

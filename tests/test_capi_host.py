@@ -153,6 +153,10 @@ def test_ssd_validation(lib):
     assert ssd(lib, H=8, G=3) == UNSUPPORTED
     assert ssd(lib, y=P[0]) == INVALID
     assert ssd(lib, B=0) == OK
+    for k in ("x", "Bm", "Cm", "h0", "h_final"):   # 16-byte pieces
+        assert ssd(lib, **{k: ctypes.c_void_p(P[["x", "dtv", "A", "Bm", "Cm", "D_skip", "z", "h0", "y",
+                                                  "h_final"].index(k)].value + 4)}) == UNSUPPORTED, k
+    assert ssd(lib, ws=ctypes.c_void_p(P[12].value + 8), ws_len=1 << 40) == UNSUPPORTED
 
 
 def test_scan_lanesplit_variant_limits(lib):
