@@ -442,7 +442,18 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(int64_t B, int64_t 
 // 256) each wave owns one row block and both p tiles, and the two waves that
 // share a SIMD take blocks s and 7 - s, so every SIMD does the same 9 (I, J)
 // blocks and each block's M is formed once for both tiles.
-constexpr int kQPad = 256 + 8;
+// x^T row pitch (elements): 130 dwords, so the 8-byte fragment reads of 32
+// consecutive rows cover all 64 banks once
+constexpr int kQPad = 256 + 4;
+// x staging unit u (of 128 token pairs x 8 groups of 8 channels): 4
+// consecutive lanes read 64 contiguous bytes of a row (p-groups 0-3 or
+// 4-7) and a wave covers 16 token pairs, so the transposed 4-byte LDS
+// writes of a wave (p-group stride 16 banks at this pitch, token pairs
+// consecutive) fall on 64 distinct banks.
+__device__ __forceinline__ void x_unit(int u, int &jp, int &pc) {
+  jp = (u / 4) % 128;
+  pc = (u / 512) * 4 + u % 4;
+}
 constexpr int kScanThreads = 512;
 
 template <int N>
@@ -462,7 +473,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
   static_assert(kXU >= 1 && kXU * kScanThreads == (256 / 2) * (kP / 8), "x staging must tile");
 
   __shared__ float s_S[256];   // in-chunk cumulative log2 decay of the current head
-  __shared__ float s_T[256];   // log2(dt_j) - S_j
+  __shared__ __attribute__((aligned(16))) float s_T[256];   // log2(dt_j) - S_j
   __shared__ __attribute__((aligned(16))) uint16_t s_b[256 * kNPad];  // B rows: [j][n]
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kP * kQPad];   // x^T: [p][j]
   __shared__ __attribute__((aligned(16))) uint16_t s_hh[kP * kNPad];  // h_in hi: [p][n]
@@ -507,19 +518,24 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     cfA[ks] = load8(Cp + ((b * L + t0 + iA) * G + g) * N + ks * 16 + 8 * lg, active && iA < nvalid);
-  // two accumulation chains over the K steps, added at the end, so the
-  // dependent MFMA chain is half as long
-  auto cb_block = [&](int J, const bf16x8 *cf) {
-    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+  // C B^T block (column block J of the row block whose C fragments are cf)
+  // as two accumulation chains over the K steps (even and odd steps), summed
+  // where they are used, so the dependent MFMA chain is half as long.  All
+  // B fragments are read from LDS before the first product.
+  auto cb_block = [&](int J, const bf16x8 *cf, f32x16 &acc0, f32x16 &acc1) {
+    bf16x8 bfr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bfr[ks] = *reinterpret_cast<const bf16x8 *>(&s_b[(J * 32 + l32) * kNPad + ks * 16 + 8 * lg]);
+    acc0 = f32x16{};
+    acc1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(&s_b[(J * 32 + l32) * kNPad + ks * 16 + 8 * lg]);
       if (ks % 2 == 0)
-        acc0 = mfma(bfr, cf[ks], acc0);
+        acc0 = mfma(bfr[ks], cf[ks], acc0);
       else
-        acc1 = mfma(bfr, cf[ks], acc1);
+        acc1 = mfma(bfr[ks], cf[ks], acc1);
     }
-    return acc0 + acc1;
   };
 
   // per-head inputs in flight: x (pairs of rows, 8 columns each) and (wave
@@ -534,8 +550,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
         const_cast<uint16_t *>(xp + ((b * L + t0) * H + h) * kP), 0, x_bytes, 0x00020000);
 #pragma unroll
     for (int k = 0; k < kXU; ++k) {
-      const int u = tid + k * kScanThreads;
-      const int jp = u / (kP / 8), pc = u % (kP / 8);
+      int jp, pc;
+      x_unit(tid + k * kScanThreads, jp, pc);
       const int j0 = 2 * jp;
       const int off = (j0 * static_cast<int>(H) * kP + pc * 8) * 2;
       const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
@@ -543,13 +559,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
       px[k][0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
       px[k][1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
     }
-    if (wave == 0) {
+    if (wave == 0) {  // raw values: the step-size transform waits for the loads
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * lane + e;
-        pdt[e] = j < nvalid ? step_size(bf_to_f(bf16_bits(dtp[(b * L + t0 + j) * H + h])),
-                                        a.dt_bias ? a.dt_bias[h] : 0.f, a.dt_softplus)
-                            : 0.f;
+        pdt[e] = j < nvalid ? bf_to_f(bf16_bits(dtp[(b * L + t0 + j) * H + h])) : 0.f;
       }
     }
   };
@@ -569,8 +583,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
     }
 #pragma unroll
     for (int k = 0; k < kXU; ++k) {
-      const int u = tid + k * kScanThreads;
-      const int jp = u / (kP / 8), pc = u % (kP / 8);
+      int jp, pc;
+      x_unit(tid + k * kScanThreads, jp, pc);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int off = (pc * 8 + e) * kQPad + 2 * jp;
@@ -598,6 +612,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
     // wave 0: S = inclusive cumsum of dt A (log2 units) and T = log2(dt) - S
     if (wave == 0) {
       const float A2 = a.A[h] * kLog2e;
+      const float bias = a.dt_bias ? a.dt_bias[h] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pdt[e] = 4 * lane + e < nvalid ? step_size(pdt[e], bias, a.dt_softplus) : 0.f;
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = pdt[e] * A2 + (e > 0 ? v[e - 1] : 0.f);
@@ -650,55 +667,93 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
         acc[1][r] *= e;
       }
       const float S_i = s_S[i_lane < Q ? i_lane : Q - 1];
+      // software pipeline over the column blocks: the C B^T products of
+      // block J + 1 run on the matrix cores while block J's M is formed
+      f32x16 cnA, cnB;
+      cb_block(0, cf, cnA, cnB);
       for (int J = 0; J <= I; ++J) {
-        const f32x16 cb = cb_block(J, cf);
+        const f32x16 cb = cnA + cnB;  // (its products were issued a block ago)
+        // this block's log2(dt_j) - S_j (rows r of the MFMA layout) and x
+        // fragments, read before the next block's products are issued
+        float tj[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 t = *reinterpret_cast<const float4 *>(&s_T[J * 32 + 8 * r4 + 4 * lg]);
+          tj[4 * r4] = t.x;
+          tj[4 * r4 + 1] = t.y;
+          tj[4 * r4 + 2] = t.z;
+          tj[4 * r4 + 3] = t.w;
+        }
+        bf16x8 xf[2][2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int pl = (pt0 + (q < npt ? q : 0)) * 32 + l32;
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int jb = J * 32 + 16 * k2 + 4 * lg;
+            const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&s_x[pl * kQPad + jb]);
+            const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&s_x[pl * kQPad + jb + 8]);
+            xf[q][k2] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          }
+        }
+        if (J < I) cb_block(J + 1, cf, cnA, cnB);
+        __builtin_amdgcn_sched_barrier(0);
+        float ev[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ev[r] = fast_exp2(S_i + tj[r]);
         bf16x8 mh[2], ml[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = J * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          float m = cb[r] * fast_exp2(S_i + s_T[j]);
+          float m = cb[r] * ev[r];
           if (J == I && j > i_lane) m = 0.f;
           __bf16 x1, x2;
           split_bf16(m, x1, x2);
           mh[r / 8][r % 8] = x1;
           ml[r / 8][r % 8] = x2;
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           if (q < npt) {
-            const int pl = (pt0 + q) * 32 + l32;
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-              const int jb = J * 32 + 16 * k2 + 4 * lg;
-              const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&s_x[pl * kQPad + jb]);
-              const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&s_x[pl * kQPad + jb + 8]);
-              const bf16x8 xf = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-              acc[q] = mfma(mh[k2], xf, acc[q]);
-              acc[q] = mfma(ml[k2], xf, acc[q]);
+              acc[q] = mfma(mh[k2], xf[q][k2], acc[q]);
+              acc[q] = mfma(ml[k2], xf[q][k2], acc[q]);
             }
           }
         }
       }
       // y and z of this (chunk, head) through buffer resources with 32-bit
       // offsets: row i, column p at ((i * H) * P + p) * 2 bytes
+      // (all reads of a tile are issued before its arithmetic and stores)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         if (q < npt) {
           const int pl = (pt0 + q) * 32 + l32;
+          float v[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = I * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-            const float xv = bf_to_f(bf16_bits(s_x[pl * kQPad + i]));
-            float v = fmaf(Dh, xv, acc[q][r]);
-            const int off = (i * static_cast<int>(H) * kP + pl) * 2;
-            if (zp) {
-              const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
-              v *= silu(__uint_as_float(zb << 16));
-            }
-            // rows past the chunk's valid tokens lie past the resource: dropped
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)), ry, off,
-                                                  0, 0);
+          for (int r4 = 0; r4 < 4; ++r4) {  // x of rows i = I*32 + 8 r4 + 4 lg + 0..3
+            const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(&s_x[pl * kQPad + I * 32 + 8 * r4 + 4 * lg]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * r4 + e] = fmaf(Dh, static_cast<float>(xv[e]), acc[q][4 * r4 + e]);
           }
+          int off[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            off[r] = ((I * 32 + 8 * (r / 4) + 4 * lg + (r % 4)) * static_cast<int>(H) * kP + pl) * 2;
+          if (zp) {
+            uint32_t zb[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) zb[r] = __builtin_amdgcn_raw_buffer_load_b16(rz, off[r], 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[r] *= silu(__uint_as_float(zb[r] << 16));
+          }
+          // rows past the chunk's valid tokens lie past the resource: dropped
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[r])), ry,
+                                                  off[r], 0, 0);
         }
       }
     };
