@@ -59,6 +59,15 @@ __device__ __forceinline__ void split_bf16(float v, __bf16 &hi, __bf16 &lo) {
   hi = static_cast<__bf16>(v);
   lo = static_cast<__bf16>(v - static_cast<float>(hi));
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// split_bf16 of two values, each half converted as a pair
+__device__ __forceinline__ void split_bf16x2(float a, float b, bf16x2 &hi, bf16x2 &lo) {
+  hi = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+  lo = __builtin_convertvector(f32x2{a - __uint_as_float(hb << 16), b - __uint_as_float(hb & 0xffff0000u)},
+                               bf16x2);
+}
 
 // Inclusive prefix sum over the Q <= 256 values v (one per thread, threads
 // >= Q pass 0) into s_out[0..Q).  Uses wave shuffles and one LDS round.
@@ -472,8 +481,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
   constexpr int kHU = (kHTot + kScanThreads - 1) / kScanThreads;
   static_assert(kXU >= 1 && kXU * kScanThreads == (256 / 2) * (kP / 8), "x staging must tile");
 
-  __shared__ float s_S[256];   // in-chunk cumulative log2 decay of the current head
+  __shared__ __attribute__((aligned(16))) float s_S[256];   // in-chunk cumulative log2 decay of the current head
   __shared__ __attribute__((aligned(16))) float s_T[256];   // log2(dt_j) - S_j
+  __shared__ __attribute__((aligned(16))) float s_wt[kScanThreads / 64 * 256];  // per wave: w_j
   __shared__ __attribute__((aligned(16))) uint16_t s_b[256 * kNPad];  // B rows: [j][n]
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kP * kQPad];   // x^T: [p][j]
   __shared__ __attribute__((aligned(16))) uint16_t s_hh[kP * kNPad];  // h_in hi: [p][n]
@@ -660,11 +670,36 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
           }
         }
       }
+      // Decay of rows i against the columns j < I0 = 32 I left of the
+      // diagonal block, factored at row I0:
+      //   exp2(S_i - S_j) dt_j = exp2(S_i - S_I0) * (exp2(S_I0 - S_j) dt_j),
+      // both factors at most 1 (S falls along the chunk), so neither
+      // overflows and one that underflows only drops a product below the
+      // fp32 range.  The column factors w_j of this wave's row block are
+      // tabulated once per head; Y (with the carried-in term scaled by
+      // exp2(S_I0) only) takes the row factors once, before the diagonal
+      // block, whose decay is formed element by element.
+      const int I0 = I * 32;
+      const float S_I0 = s_S[I0];
+      float *wt = s_wt + wave * 256;
+      {
+        const float4 t = *reinterpret_cast<const float4 *>(&s_T[4 * lane]);
+        const float tv[4] = {t.x, t.y, t.z, t.w};
+        float w[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(s_S[I * 32 + 8 * (r / 4) + 4 * lg + (r % 4)]);
-        acc[0][r] *= e;
-        acc[1][r] *= e;
+        for (int e = 0; e < 4; ++e) w[e] = 4 * lane + e < I0 ? fast_exp2(S_I0 + tv[e]) : 0.f;
+        *reinterpret_cast<float4 *>(&wt[4 * lane]) = make_float4(w[0], w[1], w[2], w[3]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      {
+        const float e0 = fast_exp2(S_I0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[0][r] *= e0;
+          acc[1][r] *= e0;
+        }
       }
       const float S_i = s_S[i_lane < Q ? i_lane : Q - 1];
       // software pipeline over the column blocks: the C B^T products of
@@ -673,12 +708,15 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
       cb_block(0, cf, cnA, cnB);
       for (int J = 0; J <= I; ++J) {
         const f32x16 cb = cnA + cnB;  // (its products were issued a block ago)
-        // this block's log2(dt_j) - S_j (rows r of the MFMA layout) and x
-        // fragments, read before the next block's products are issued
+        const bool diag = J == I;
+        // this block's w_j (log2(dt_j) - S_j on the diagonal) at the rows r
+        // of the MFMA layout, and x fragments, read before the next block's
+        // products are issued
+        const float *src = diag ? s_T : wt;
         float tj[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 t = *reinterpret_cast<const float4 *>(&s_T[J * 32 + 8 * r4 + 4 * lg]);
+          const float4 t = *reinterpret_cast<const float4 *>(&src[J * 32 + 8 * r4 + 4 * lg]);
           tj[4 * r4] = t.x;
           tj[4 * r4 + 1] = t.y;
           tj[4 * r4 + 2] = t.z;
@@ -698,19 +736,37 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
         }
         if (J < I) cb_block(J + 1, cf, cnA, cnB);
         __builtin_amdgcn_sched_barrier(0);
-        float ev[16];
+        float m[16];
+        if (!diag) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ev[r] = fast_exp2(S_i + tj[r]);
+          for (int r = 0; r < 16; ++r) m[r] = cb[r] * tj[r];
+        } else {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {  // rows I0 + 8 r4 + 4 lg + 0..3 of Y
+            const float4 sv = *reinterpret_cast<const float4 *>(&s_S[I0 + 8 * r4 + 4 * lg]);
+            const float su[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float u = fast_exp2(su[e] - S_I0);
+              acc[0][4 * r4 + e] *= u;
+              acc[1][4 * r4 + e] *= u;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = J * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+            m[r] = j > i_lane ? 0.f : cb[r] * fast_exp2(S_i + tj[r]);
+          }
+        }
         bf16x8 mh[2], ml[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = J * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          float m = cb[r] * ev[r];
-          if (J == I && j > i_lane) m = 0.f;
-          __bf16 x1, x2;
-          split_bf16(m, x1, x2);
-          mh[r / 8][r % 8] = x1;
-          ml[r / 8][r % 8] = x2;
+        for (int r = 0; r < 16; r += 2) {
+          bf16x2 hv, lv;
+          split_bf16x2(m[r], m[r + 1], hv, lv);
+          mh[r / 8][r % 8] = hv[0];
+          mh[r / 8][r % 8 + 1] = hv[1];
+          ml[r / 8][r % 8] = lv[0];
+          ml[r / 8][r % 8 + 1] = lv[1];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

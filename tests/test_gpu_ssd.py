@@ -70,6 +70,29 @@ def test_ssd_chunk_invariance(oracle_mod):
         assert_close(hf, rh, "bf16", f"h chunk {ch}")
 
 
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_ssd_decay_extremes(oracle_mod, chunk):
+    """Heads in different decay regimes: strong (dt 4, A -16: the decay
+    across a 32-token block underflows fp32), nearly none (dt 1e-3, A
+    -0.01), sparse large steps that reset the state inside a block, and the
+    default mix -- the off-diagonal decay is formed from factors split at
+    block starts and the diagonal block's directly."""
+    w = gen.make_ssd(1, 600, 4, 64, 2, 128, chunk=chunk, dtype="bf16", seed=413)
+    dt = w.dt.f32.copy()
+    rng = np.random.default_rng(414)
+    dt[:, :, 0] = 4.0
+    dt[:, :, 1] = 1e-3
+    dt[:, :, 2] = np.where(rng.random(dt.shape[:2]) < 0.05, 8.0, 0.01)
+    w.dt = gen._store(dt.astype(np.float32), "bf16")
+    w.A = np.array([-16.0, -0.01, -8.0, w.A[3]], np.float32)
+    _say("ssd decay extremes", chunk)
+    y, hf = run_gpu(w)
+    assert np.isfinite(y).all() and np.isfinite(hf).all()
+    ry, rh = run_oracle(oracle_mod, w)
+    assert_close(y, ry, "bf16", "y")
+    assert_close(hf, rh, "bf16", "h_final")
+
+
 def test_ssd_empty_sequence():
     w = gen.make_ssd(1, 0, 4, 64, 2, 128, chunk=256, dtype="bf16", seed=412)
     _say("ssd L=0")
