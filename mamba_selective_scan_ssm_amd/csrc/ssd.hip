@@ -528,24 +528,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     cfA[ks] = load8(Cp + ((b * L + t0 + iA) * G + g) * N + ks * 16 + 8 * lg, active && iA < nvalid);
-  // C B^T block (column block J of the row block whose C fragments are cf)
-  // as two accumulation chains over the K steps (even and odd steps), summed
-  // where they are used, so the dependent MFMA chain is half as long.  All
-  // B fragments are read from LDS before the first product.
-  auto cb_block = [&](int J, const bf16x8 *cf, f32x16 &acc0, f32x16 &acc1) {
+  // C B^T block (column block J of the row block whose C fragments are cf),
+  // one accumulation chain over the K steps (it runs while the previous
+  // block's scores are formed, so its latency is hidden).  All B fragments
+  // are read from LDS before the first product.
+  auto cb_block = [&](int J, const bf16x8 *cf, f32x16 &acc0) {
     bf16x8 bfr[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       bfr[ks] = *reinterpret_cast<const bf16x8 *>(&s_b[(J * 32 + l32) * kNPad + ks * 16 + 8 * lg]);
     acc0 = f32x16{};
-    acc1 = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks % 2 == 0)
-        acc0 = mfma(bfr[ks], cf[ks], acc0);
-      else
-        acc1 = mfma(bfr[ks], cf[ks], acc1);
-    }
+    for (int ks = 0; ks < KS; ++ks) acc0 = mfma(bfr[ks], cf[ks], acc0);
   };
 
   // per-head inputs in flight: x (pairs of rows, 8 columns each) and (wave
@@ -704,10 +698,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
       const float S_i = s_S[i_lane < Q ? i_lane : Q - 1];
       // software pipeline over the column blocks: the C B^T products of
       // block J + 1 run on the matrix cores while block J's M is formed
-      f32x16 cnA, cnB;
-      cb_block(0, cf, cnA, cnB);
+      f32x16 cn;
+      cb_block(0, cf, cn);
+#pragma unroll 2
       for (int J = 0; J <= I; ++J) {
-        const f32x16 cb = cnA + cnB;  // (its products were issued a block ago)
+        const f32x16 cb = cn;  // (its products were issued a block ago)
         const bool diag = J == I;
         // this block's w_j (log2(dt_j) - S_j on the diagonal) at the rows r
         // of the MFMA layout, and x fragments, read before the next block's
@@ -734,7 +729,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
             xf[q][k2] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
           }
         }
-        if (J < I) cb_block(J + 1, cf, cnA, cnB);
+        if (J < I) cb_block(J + 1, cf, cn);
         __builtin_amdgcn_sched_barrier(0);
         float m[16];
         if (!diag) {
