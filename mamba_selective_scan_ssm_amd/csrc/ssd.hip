@@ -272,6 +272,15 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_state_kernel(SSDArgs a, fl
 // per wave over the chunk's tokens.  The next head's x and dt are loaded into
 // registers while the current head computes.  The LDS use (67.6 KB) leaves
 // room for two workgroups per CU, one staging while the other multiplies.
+// x staging unit u (of 128 token pairs x 8 groups of 8 channels): 4
+// consecutive lanes read 64 contiguous bytes of a row (p-groups 0-3 or
+// 4-7) and a wave covers 16 token pairs.  The transposed 4-byte LDS writes
+// of a wave fall on 64 distinct banks at a 130-dword row pitch (p-group
+// stride 16 banks, token pairs consecutive), on 32 at 132 dwords.
+__device__ __forceinline__ void x_unit(int u, int &jp, int &pc) {
+  jp = (u / 4) % 128;
+  pc = (u / 512) * 4 + u % 4;
+}
 constexpr int kCSThreads = 512;
 constexpr int kCSPad = 256 + 8;
 
@@ -307,8 +316,8 @@ __global__ __launch_bounds__(kCSThreads, 4) void ssd_chunk_state_group_kernel(SS
   auto prefetch = [&](int64_t h) {
 #pragma unroll
     for (int k = 0; k < kXU; ++k) {
-      const int u = tid + k * kCSThreads;
-      const int jp = u % 128, pc = u / 128;
+      int jp, pc;
+      x_unit(tid + k * kCSThreads, jp, pc);
       const int j0 = 2 * jp;
       const int64_t base = ((b * L + t0 + j0) * H + h) * kP + pc * 8;
       xr[k][0] = load8_raw(xp + base, j0 < nvalid);
@@ -320,10 +329,10 @@ __global__ __launch_bounds__(kCSThreads, 4) void ssd_chunk_state_group_kernel(SS
   };
   prefetch(g * HPG);
 
-  // B^T of the chunk; unit u: token pair u % 128, 8-wide n chunk u / 128
-  // (consecutive lanes on consecutive token pairs: distinct LDS banks)
+  // B^T of the chunk; unit u: token pair (u / 4) % 128, 8-wide n chunk
+  // 4 (u / 512) + u % 4 (4 lanes read 64 contiguous bytes of a row)
   for (int u = tid; u < 128 * (N / 8); u += kCSThreads) {
-    const int jp = u % 128, nc8 = u / 128;
+    const int jp = (u / 4) % 128, nc8 = (u / 512) * 4 + u % 4;
     const int j0 = 2 * jp;
     const int64_t base = ((b * L + t0 + j0) * G + g) * N + nc8 * 8;
     const uint4 r0 = load8_raw(Bp + base, j0 < nvalid);
@@ -351,8 +360,8 @@ __global__ __launch_bounds__(kCSThreads, 4) void ssd_chunk_state_group_kernel(SS
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kXU; ++k) {
-      const int u = tid + k * kCSThreads;
-      const int jp = u % 128, pc = u / 128;
+      int jp, pc;
+      x_unit(tid + k * kCSThreads, jp, pc);
       const int j0 = 2 * jp;
       const float w0 = j0 < Q ? s_w[j0] : 0.f, w1 = j0 + 1 < Q ? s_w[j0 + 1] : 0.f;
 #pragma unroll
@@ -454,15 +463,6 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(int64_t B, int64_t 
 // x^T row pitch (elements): 130 dwords, so the 8-byte fragment reads of 32
 // consecutive rows cover all 64 banks once
 constexpr int kQPad = 256 + 4;
-// x staging unit u (of 128 token pairs x 8 groups of 8 channels): 4
-// consecutive lanes read 64 contiguous bytes of a row (p-groups 0-3 or
-// 4-7) and a wave covers 16 token pairs, so the transposed 4-byte LDS
-// writes of a wave (p-group stride 16 banks at this pitch, token pairs
-// consecutive) fall on 64 distinct banks.
-__device__ __forceinline__ void x_unit(int u, int &jp, int &pc) {
-  jp = (u / 4) % 128;
-  pc = (u / 512) * 4 + u % 4;
-}
 constexpr int kScanThreads = 512;
 
 template <int N>
