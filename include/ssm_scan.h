@@ -344,7 +344,7 @@ ssm_status ssm_conv1d_fwd(int64_t B, int64_t L, int64_t D, int64_t K, ssm_dtype 
  *
  * state : (S, D, K-1) fp32 in/out;  x, y : (S, D) dtype `dt`
  * w : (D, K) fp32;  bias : (D) fp32 or NULL.  y must not overlap the other
- * arguments.  2 <= K <= 8.
+ * arguments.  2 <= K <= 8 and S <= 65535 (else SSM_ERR_UNSUPPORTED).
  */
 ssm_status ssm_conv1d_update(int64_t S, int64_t D, int64_t K, ssm_dtype dt, float *state,
                              const void *x, const float *w, const float *bias,

@@ -122,6 +122,7 @@ ssm_status ssm_conv1d_update(int64_t S, int64_t D, int64_t K, ssm_dtype dt, floa
   if (S < 0 || D < 0 || K < 0) return SSM_ERR_INVALID_ARG;
   if (!valid_dtype(dt) || (activation != 0 && activation != 1)) return SSM_ERR_INVALID_ARG;
   if (K < 2 || K > 8) return SSM_ERR_UNSUPPORTED;
+  if (S > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;  // one grid row per sequence
   if (S == 0 || D == 0) return SSM_OK;
   if (!state || !x || !w || !y) return SSM_ERR_INVALID_ARG;
   const int64_t es = esize(dt);

@@ -125,11 +125,14 @@ __global__ __launch_bounds__(256) void conv1d_state_kernel(ConvArgs a) {
 
 // One decode step per (s, d): window [state, x], state shifted in place.
 template <typename T, int K, bool ACT>
+// grid (channel blocks, sequences): no index division; the bias is read
+// unconditionally (from w when absent) so no load sits behind a branch
 __global__ __launch_bounds__(256) void conv1d_update_kernel(ConvArgs a) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= a.B * a.D) return;
-  const int64_t d = i % a.D;
+  const int64_t d = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (d >= a.D) return;
+  const int64_t i = static_cast<int64_t>(blockIdx.y) * a.D + d;
   float *st = a.state_out + i * (K - 1);
+  const float bv = (a.bias ? a.bias : a.w)[d];
   float win[K];
 #pragma unroll
   for (int k = 0; k < K - 1; ++k) win[k] = st[k];
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void conv1d_update_kernel(ConvArgs a) {
   float v = 0.f;
 #pragma unroll
   for (int k = 0; k < K; ++k) v = fmaf(a.w[d * K + k], win[k], v);
-  v += a.bias ? a.bias[d] : 0.f;
+  v += a.bias ? bv : 0.f;
   if (ACT) v *= __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e));
   static_cast<T *>(a.y)[i] = from_f32<T>(v);
 #pragma unroll
@@ -163,11 +166,11 @@ hipError_t launch_fwd_k(const ConvArgs &a, hipStream_t s) {
 
 template <typename T, int K>
 hipError_t launch_update_k(const ConvArgs &a, hipStream_t s) {
-  const int64_t n = a.B * a.D;
+  const dim3 grid(static_cast<unsigned>((a.D + 255) / 256), static_cast<unsigned>(a.B));
   if (a.act)
-    conv1d_update_kernel<T, K, true><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(a);
+    conv1d_update_kernel<T, K, true><<<grid, 256, 0, s>>>(a);
   else
-    conv1d_update_kernel<T, K, false><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(a);
+    conv1d_update_kernel<T, K, false><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

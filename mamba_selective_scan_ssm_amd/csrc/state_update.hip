@@ -8,10 +8,13 @@
 // holding four consecutive states each, so one 16-byte load per lane covers
 // the state tensor contiguously across the wave.  The y contraction over n is
 // finished with a butterfly over those N/4 lanes.  The single-token step
-// gives each thread two channels whose loads are all issued before either is
-// used, so a wave keeps twice the state bytes in flight (the step is bound by
-// how many bytes are in flight, not by the instruction stream).  Sizes this
-// layout does not
+// gives each thread one channel of two sequences: the channel's A row (read
+// by every sequence) is loaded once for both, and all loads of the thread
+// are issued before any is used, so a wave keeps twice the state bytes in
+// flight (the step is bound by how many bytes are in flight, not by the
+// instruction stream).  Optional inputs (gate, skip, step bias) are read
+// unconditionally, since a load inside a branch brings a wait that drains
+// every load before it.  Sizes this layout does not
 // cover (N not a multiple of 4, or a state/A not 16-byte aligned) go to the
 // per-lane scan kernel with L = T, whose lanes read and then write only their
 // own state row.
@@ -51,7 +54,12 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
   float4 *st = reinterpret_cast<float4 *>(a.state + (row * D + d) * N) + q;
   const float4 hv = *st;
   const float4 Av = reinterpret_cast<const float4 *>(a.A + d * N)[q];
-  const float bias = a.delta_bias ? a.delta_bias[d] : 0.f;
+  // optional inputs read unconditionally (from A, or x, when absent): a load
+  // in a branch would bring a wait that drains the loads issued before it
+  const float bv0 = (a.delta_bias ? a.delta_bias : a.A)[d];
+  const float bias = a.delta_bias ? bv0 : 0.f;
+  const float skp = (a.D_skip ? a.D_skip : a.A)[d];
+  const T *zsrc = zp ? zp : xp;
   float h[4] = {hv.x, hv.y, hv.z, hv.w};
   const float Ar[4] = {Av.x, Av.y, Av.z, Av.w};
 
@@ -64,7 +72,7 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
       const int64_t tok = s * nT + (t0 + k < nT ? t0 + k : nT - 1);  // row of (S, T, .) inputs
       xv[k] = to_f32(xp[tok * D + d]);
       dv[k] = to_f32(dp[tok * D + d]);
-      zv[k] = zp ? to_f32(zp[tok * D + d]) : 0.f;
+      zv[k] = to_f32(zsrc[tok * D + d]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bv[k][j] = to_f32(Bp[tok * N + 4 * q + j]);
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
       for (int off = LPC / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPC);
       if (active && q == 0) {
         float v = acc;
-        if (a.D_skip) v = fmaf(a.D_skip[d], xv[k], v);
+        if (a.D_skip) v = fmaf(skp, xv[k], v);
         if (zp) v *= silu(zv[k]);
         static_cast<T *>(a.y)[tok * D + d] = from_f32<T>(v);
       }
@@ -98,72 +106,78 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
   *st = make_float4(h[0], h[1], h[2], h[3]);
 }
 
-// Single-token step with CPT channels per thread: every load of the CPT
-// channels (and the sequence's B/C slice, shared by them) is issued before
-// any of them is used, so a wave keeps CPT times the state bytes in flight.
-template <typename T, int LPC, int CPT>
-__global__ __launch_bounds__(kBlock) void state_step_kernel(StepArgs a) {
+// Single-token step with SPT sequences per thread for one channel: the
+// channel's A row (read by every sequence) is loaded once for the SPT
+// sequences, and all loads of the thread are issued before any is used.  A
+// sequence whose slot is outside the pool is skipped (its loads are clamped
+// to row 0 and nothing is stored).
+template <typename T, int LPC, int SPT>
+__global__ __launch_bounds__(kBlock) void state_step_seq_kernel(StepArgs a) {
   constexpr int N = 4 * LPC;
-  constexpr int kCh = kBlock / LPC;  // channels per pass of the block
+  constexpr int kCh = kBlock / LPC;  // channels per block
   const int q = threadIdx.x % LPC;
-  const int64_t s = blockIdx.y;
-  const int64_t D = a.D;
-  int64_t row = s;
-  if (a.slots != nullptr) {
-    const int32_t sl = a.slots[s];
-    if (sl < 0 || sl >= a.pool_rows) return;  // uniform over the block
-    row = sl;
-  }
+  const int64_t D = a.D, S = a.S;
+  const int64_t d_raw = static_cast<int64_t>(blockIdx.x) * kCh + threadIdx.x / LPC;
+  const bool act = d_raw < D;
+  const int64_t d = act ? d_raw : D - 1;
   const T *xp = static_cast<const T *>(a.x);
   const T *dp = static_cast<const T *>(a.delta);
   const T *zp = static_cast<const T *>(a.z);
-  float Bv[4], Cv[4];
+  const T *zsrc = zp ? zp : xp;  // optional inputs read unconditionally (see above)
+  const float bv0 = (a.delta_bias ? a.delta_bias : a.A)[d];
+  const float skp = (a.D_skip ? a.D_skip : a.A)[d];
+  const float4 Av = reinterpret_cast<const float4 *>(a.A + d * N)[q];
+  int64_t sq[SPT], row[SPT];
+  bool ok[SPT];
+  float4 hv[SPT];
+  float xv[SPT], dv[SPT], zv[SPT], Bv[SPT][4], Cv[SPT][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    Bv[j] = to_f32(static_cast<const T *>(a.Bm)[s * N + 4 * q + j]);
-    Cv[j] = to_f32(static_cast<const T *>(a.Cm)[s * N + 4 * q + j]);
+  for (int k = 0; k < SPT; ++k) {
+    const int64_t s_raw = static_cast<int64_t>(blockIdx.y) * SPT + k;
+    sq[k] = s_raw < S ? s_raw : S - 1;
+    ok[k] = s_raw < S;
+    row[k] = sq[k];
+    if (a.slots != nullptr) {
+      const int32_t sl = a.slots[sq[k]];
+      ok[k] = ok[k] && sl >= 0 && sl < a.pool_rows;
+      row[k] = ok[k] ? sl : 0;
+    }
+    hv[k] = reinterpret_cast<const float4 *>(a.state + (row[k] * D + d) * N)[q];
+    xv[k] = to_f32(xp[sq[k] * D + d]);
+    dv[k] = to_f32(dp[sq[k] * D + d]);
+    zv[k] = to_f32(zsrc[sq[k] * D + d]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Bv[k][j] = to_f32(static_cast<const T *>(a.Bm)[sq[k] * N + 4 * q + j]);
+      Cv[k][j] = to_f32(static_cast<const T *>(a.Cm)[sq[k] * N + 4 * q + j]);
+    }
   }
-  int64_t d[CPT];
-  bool act[CPT];
-  float4 hv[CPT], Av[CPT];
-  float xv[CPT], dv[CPT], zv[CPT];
+  const float Ar[4] = {Av.x, Av.y, Av.z, Av.w};
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const int64_t dr = (static_cast<int64_t>(blockIdx.x) * CPT + k) * kCh + threadIdx.x / LPC;
-    act[k] = dr < D;
-    d[k] = act[k] ? dr : D - 1;
-    hv[k] = reinterpret_cast<const float4 *>(a.state + (row * D + d[k]) * N)[q];
-    Av[k] = reinterpret_cast<const float4 *>(a.A + d[k] * N)[q];
-    xv[k] = to_f32(xp[s * D + d[k]]);
-    dv[k] = to_f32(dp[s * D + d[k]]);
-    zv[k] = zp ? to_f32(zp[s * D + d[k]]) : 0.f;
-  }
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const float dl = step_size(dv[k], a.delta_bias ? a.delta_bias[d[k]] : 0.f, a.delta_softplus);
+  for (int k = 0; k < SPT; ++k) {
+    const float dl = step_size(dv[k], a.delta_bias ? bv0 : 0.f, a.delta_softplus);
     const float u = dl * xv[k];
     float h[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
-    const float Ar[4] = {Av[k].x, Av[k].y, Av[k].z, Av[k].w};
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float dA = fast_exp2(dl * (Ar[j] * kLog2e));
-      h[j] = fmaf(dA, h[j], u * Bv[j]);
-      acc = fmaf(Cv[j], h[j], acc);
+      h[j] = fmaf(dA, h[j], u * Bv[k][j]);
+      acc = fmaf(Cv[k][j], h[j], acc);
     }
 #pragma unroll
     for (int off = LPC / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPC);
     hv[k] = make_float4(h[0], h[1], h[2], h[3]);
-    if (act[k] && q == 0) {
+    if (act && ok[k] && q == 0) {
       float v = acc;
-      if (a.D_skip) v = fmaf(a.D_skip[d[k]], xv[k], v);
+      if (a.D_skip) v = fmaf(skp, xv[k], v);
       if (zp) v *= silu(zv[k]);
-      static_cast<T *>(a.y)[s * D + d[k]] = from_f32<T>(v);
+      static_cast<T *>(a.y)[sq[k] * D + d] = from_f32<T>(v);
     }
   }
 #pragma unroll
-  for (int k = 0; k < CPT; ++k)
-    if (act[k]) reinterpret_cast<float4 *>(a.state + (row * D + d[k]) * N)[q] = hv[k];
+  for (int k = 0; k < SPT; ++k)
+    if (act && ok[k]) reinterpret_cast<float4 *>(a.state + (row[k] * D + d) * N)[q] = hv[k];
 }
 
 template <typename T, int LPC>
@@ -171,12 +185,9 @@ hipError_t launch_t(const StepArgs &a, hipStream_t st) {
   constexpr int kCh = kBlock / LPC;
   dim3 grid(static_cast<unsigned>((a.D + kCh - 1) / kCh), static_cast<unsigned>(a.S));
   if (a.T == 1) {
-#ifndef SSM_STEP_CPT
-#define SSM_STEP_CPT 2
-#endif
-    constexpr int kCPT = SSM_STEP_CPT;
-    dim3 g1(static_cast<unsigned>((a.D + kCPT * kCh - 1) / (kCPT * kCh)), static_cast<unsigned>(a.S));
-    state_step_kernel<T, LPC, kCPT><<<g1, kBlock, 0, st>>>(a);
+    constexpr int kSPT = 2;
+    dim3 gs(static_cast<unsigned>((a.D + kCh - 1) / kCh), static_cast<unsigned>((a.S + kSPT - 1) / kSPT));
+    state_step_seq_kernel<T, LPC, kSPT><<<gs, kBlock, 0, st>>>(a);
   } else
     state_update_kernel<T, LPC, 4><<<grid, kBlock, 0, st>>>(a);
   return hipGetLastError();

@@ -206,6 +206,7 @@ def test_conv_update_validation(lib):
     assert conv_upd(lib, state=None) == INVALID
     assert conv_upd(lib, y=P[0]) == INVALID              # y on the state
     assert conv_upd(lib, x=P[0]) == INVALID              # x on the state
+    assert conv_upd(lib, S=65536) == UNSUPPORTED   # one grid row per sequence
 
 
 def test_delta_opts_validation(lib):
