@@ -116,22 +116,37 @@ struct SegRegs {
   static constexpr int kCh = kBwdThreads / LPC;
   static constexpr int kE = (kTok * kCh + kBwdThreads - 1) / kBwdThreads;
   static constexpr int kEB = (kTok * N + kBwdThreads - 1) / kBwdThreads;
-  float d[kE], x[kE], z[kFull ? kE : 1], g[kFull ? kE : 1], bb[kEB], cc[kFull ? kEB : 1];
+  // raw bits as loaded (bf16 in the low half): converted where they are
+  // staged, so the loads stay in flight until then (a conversion here would
+  // wait for them at once)
+  uint32_t d[kE], x[kE], z[kFull ? kE : 1], g[kFull ? kE : 1], bb[kEB], cc[kFull ? kEB : 1];
+
+  __device__ __forceinline__ static uint32_t raw(const T &v) {
+    if constexpr (sizeof(T) == 2) return v.bits;
+    else return __float_as_uint(v);
+  }
+  __device__ __forceinline__ static float f(uint32_t r) {
+    if constexpr (sizeof(T) == 2) return __uint_as_float(r << 16);
+    else return __uint_as_float(r);
+  }
 
   __device__ __forceinline__ void load(const BwdArgs &a, int64_t b, int64_t t0, int64_t dst, int tid) {
     const T *xp = static_cast<const T *>(a.x), *dp = static_cast<const T *>(a.delta);
-    const T *zp = static_cast<const T *>(a.z), *gp = static_cast<const T *>(a.dy);
+    const T *gp = static_cast<const T *>(a.dy);
+    // z read unconditionally (x stands in when there is no gate): a load in
+    // a branch brings a wait for every load issued before it
+    const T *zp = a.z ? static_cast<const T *>(a.z) : xp;
     const T *Bp = static_cast<const T *>(a.Bm), *Cp = static_cast<const T *>(a.Cm);
     const int64_t L = a.L, D = a.D;
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
       const int64_t t = t0 + tid / kCh + e * LPC;
       const int64_t i = (b * L + (t < L ? t : L - 1)) * D + dst;
-      d[e] = to_f32(dp[i]);
-      x[e] = to_f32(xp[i]);
+      d[e] = raw(dp[i]);
+      x[e] = raw(xp[i]);
       if constexpr (kFull) {
-        z[e] = zp ? to_f32(zp[i]) : 0.f;
-        g[e] = to_f32(gp[i]);
+        z[e] = raw(zp[i]);
+        g[e] = raw(gp[i]);
       }
     }
 #pragma unroll
@@ -139,8 +154,8 @@ struct SegRegs {
       const int idx = (tid + e * kBwdThreads) % (kTok * N);
       const int64_t t = t0 + idx / N;
       const int64_t i = (b * L + (t < L ? t : L - 1)) * N + idx % N;
-      bb[e] = to_f32(Bp[i]);
-      if constexpr (kFull) cc[e] = to_f32(Cp[i]);
+      bb[e] = raw(Bp[i]);
+      if constexpr (kFull) cc[e] = raw(Cp[i]);
     }
   }
 };
@@ -217,14 +232,14 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
       for (int e = 0; e < SegRegs<T, LPC, SPL, false, kP1>::kE; ++e) {
         const int k = k0 + e * LPC;
         if (k < kP1) {
-          p_dl[k][cs] = step_size(r.d[e], bias_s, a.delta_softplus);
-          p_x[k][cs] = r.x[e];
+          p_dl[k][cs] = step_size(r.f(r.d[e]), bias_s, a.delta_softplus);
+          p_x[k][cs] = r.f(r.x[e]);
         }
       }
 #pragma unroll
       for (int e = 0; e < SegRegs<T, LPC, SPL, false, kP1>::kEB; ++e) {
         const int idx = tid + e * kBwdThreads;
-        if (idx < kP1 * N) p_B[idx / N][idx % N] = r.bb[e];
+        if (idx < kP1 * N) p_B[idx / N][idx % N] = r.f(r.bb[e]);
       }
       if (blk + 1 < nblk) r.load(a, b, t0 + kP1, dst, tid);
       __syncthreads();
@@ -251,9 +266,11 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
   float dDacc = 0.f, dbacc = 0.f;
   SegRegs<T, LPC, SPL, true> r;
   float hck[SPL] = {};
+  // (d is clamped, so every lane's address is valid: the loads of the
+  // entering states are unconditional, like the inputs')
   if (nseg > 0) {
     r.load(a, b, (nseg - 1) * kSeg, dst, tid);
-    if (active) ld_spl<SPL>(ckr + ((b * nseg + nseg - 1) * D + d) * N + SPL * q, hck);
+    ld_spl<SPL>(ckr + ((b * nseg + nseg - 1) * D + d) * N + SPL * q, hck);
   }
   for (int64_t s = nseg - 1; s >= 0; --s) {
     const int64_t t0 = s * kSeg;
@@ -263,19 +280,20 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
       const int k = k0 + e * LPC;
-      const float raw = r.d[e];
+      const float raw = r.f(r.d[e]);
       slope[e] = a.delta_softplus ? sigmoid_f(raw + bias_s) : 1.f;
-      float gq = r.g[e], w = 0.f;
+      const float gv = r.f(r.g[e]);
+      float gq = gv, w = 0.f;
       if (has_z) {
-        const float zv = r.z[e];
+        const float zv = r.f(r.z[e]);
         const float sg = sigmoid_f(zv);
-        gq = r.g[e] * zv * sg;
-        w = r.g[e] * sg * fmaf(zv, 1.f - sg, 1.f);
+        gq = gv * zv * sg;
+        w = gv * sg * fmaf(zv, 1.f - sg, 1.f);
       }
       wz[e] = w;
       if (k < kSeg) {
         s_dl[k][cs] = step_size(raw, bias_s, a.delta_softplus);
-        s_x[k][cs] = r.x[e];
+        s_x[k][cs] = r.f(r.x[e]);
         s_g[k][cs] = s_active ? gq : 0.f;  // channels past D: no gradient flows
       }
     }
@@ -283,18 +301,20 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
     for (int e = 0; e < kEB; ++e) {
       const int idx = tid + e * kBwdThreads;
       if (idx < kSeg * N) {
-        s_B[idx / N][idx % N] = r.bb[e];
-        s_C[idx / N][idx % N] = r.cc[e];
+        s_B[idx / N][idx % N] = r.f(r.bb[e]);
+        s_C[idx / N][idx % N] = r.f(r.cc[e]);
       }
     }
     float H[kSeg + 1][SPL];  // H[k] = state before token t0 + k
     float aS[kSeg][SPL];     // exp(delta A) of token t0 + k
 #pragma unroll
     for (int j = 0; j < SPL; ++j) H[0][j] = hck[j];
-    if (s > 0) {
-      r.load(a, b, t0 - kSeg, dst, tid);
-      if (active) ld_spl<SPL>(ckr + ((b * nseg + s - 1) * D + d) * N + SPL * q, hck);
-    }
+    if (s > 0) r.load(a, b, t0 - kSeg, dst, tid);
+    // the state entering the previous segment, loaded every step (segment 0's
+    // again at the last one): with one value per step the loop carries it in
+    // the registers it is loaded into, where a merge would need a copy and
+    // the copy a wait for every load and store in flight
+    ld_spl<SPL>(ckr + ((b * nseg + (s > 0 ? s - 1 : 0)) * D + d) * N + SPL * q, hck);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kSeg; ++k) {
