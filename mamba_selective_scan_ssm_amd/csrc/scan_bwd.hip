@@ -110,6 +110,15 @@ __device__ __forceinline__ void st_spl(float *p, const float *v) {
 // tid / kCh + e * LPC (e < kE), and B/C entries tid + e * 256 of the
 // block's (kTok, N) rows.  Indices past the sequence or the channel range
 // are clamped (their values are never used).
+// store of one element through a buffer resource (out-of-range offsets dropped)
+template <typename T>
+__device__ __forceinline__ void out_st(__amdgpu_buffer_rsrc_t r, int off, float v) {
+  if constexpr (sizeof(T) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(from_f32<bf16_t>(v).bits, r, off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
 template <typename T, int LPC, int SPL, bool kFull, int kTok = kSeg>
 struct SegRegs {
   static constexpr int N = SPL * LPC;
@@ -161,7 +170,7 @@ struct SegRegs {
 };
 
 template <typename T, int LPC, int SPL>
-__global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel(BwdArgs a) {
   constexpr int N = SPL * LPC;
   constexpr int kCh = kBwdThreads / LPC;        // channels per workgroup
   constexpr int kE = (kSeg * kCh + kBwdThreads - 1) / kBwdThreads;  // staged entries per thread
@@ -387,16 +396,31 @@ __global__ __launch_bounds__(kBwdThreads) void scan_bwd_kernel(BwdArgs a) {
       P[((b * L + t0 + k) * ntile + tile) * 2 * N + j] = v;
     }
     // per-token outputs, stored by the staging role (coalesced over channels)
+    // through buffer resources over this segment's rows: entries past the
+    // segment or the channel range take an offset past the resource and are
+    // dropped, and dz's resource is empty without a gate, so every thread
+    // issues the same stores on every path (a store count that varies by
+    // path makes the compiler wait for every load and store in flight)
+    {
+      constexpr uint32_t kES = sizeof(T);
+      const int64_t row0 = (b * L + t0) * D;
+      const int seg_bytes = static_cast<int>(static_cast<int64_t>(nt) * D * kES);
+      auto rsrc = [&](void *p, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(static_cast<char *>(p) + row0 * kES, 0, bytes, 0x00020000);
+      };
+      const __amdgpu_buffer_rsrc_t rdx = rsrc(a.dx, seg_bytes), rdd = rsrc(a.ddelta, seg_bytes),
+                                   rdz = rsrc(has_z ? a.dz : a.dx, has_z ? seg_bytes : 0);
 #pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      const int k = k0 + e * LPC;
-      if (k < nt && s_active) {
-        const int64_t i = (b * L + t0 + k) * D + ds_raw;
-        const float ddl = s_o[1][k][cs] * slope[e];
-        static_cast<T *>(a.dx)[i] = from_f32<T>(s_o[0][k][cs]);
-        static_cast<T *>(a.ddelta)[i] = from_f32<T>(ddl);
-        if (has_z) static_cast<T *>(a.dz)[i] = from_f32<T>(s_o[2][k][cs] * wz[e]);
-        dbacc += ddl;
+      for (int e = 0; e < kE; ++e) {
+        const int k = k0 + e * LPC;
+        const bool ok = k < nt && s_active;
+        const int kk = k < kSeg ? k : 0;
+        const float ddl = s_o[1][kk][cs] * slope[e];
+        const int off = ok ? static_cast<int>((static_cast<int64_t>(k) * D + ds_raw) * kES) : 0x7fffffff;
+        out_st<T>(rdx, off, s_o[0][kk][cs]);
+        out_st<T>(rdd, off, ddl);
+        out_st<T>(rdz, off, s_o[2][kk][cs] * wz[e]);
+        if (ok) dbacc += ddl;
       }
     }
   }
