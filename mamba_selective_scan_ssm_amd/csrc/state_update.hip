@@ -26,9 +26,31 @@ namespace {
 
 constexpr int kBlock = 256;
 
+// four consecutive B or C values of a lane: one 8- (bf16) or 16-byte (fp32)
+// load when the rows are aligned (V), else four element loads
+template <typename T, bool V>
+__device__ __forceinline__ void load4(const T *p, float *v) {
+  if constexpr (V && sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else if constexpr (V) {
+    const float4 f = *reinterpret_cast<const float4 *>(p);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = to_f32(p[j]);
+  }
+}
+
 // LPC = lanes per channel (N / 4).  TT = tokens whose inputs are loaded
 // together before any of them is computed (1 for the single-token step).
-template <typename T, int LPC, int TT>
+template <typename T, int LPC, int TT, bool BCV>
 __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
   constexpr int N = 4 * LPC;
   constexpr int kCh = kBlock / LPC;  // channels per block
@@ -73,11 +95,8 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
       xv[k] = to_f32(xp[tok * D + d]);
       dv[k] = to_f32(dp[tok * D + d]);
       zv[k] = to_f32(zsrc[tok * D + d]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bv[k][j] = to_f32(Bp[tok * N + 4 * q + j]);
-        cv[k][j] = to_f32(Cp[tok * N + 4 * q + j]);
-      }
+      load4<T, BCV>(Bp + tok * N + 4 * q, bv[k]);
+      load4<T, BCV>(Cp + tok * N + 4 * q, cv[k]);
     }
 #pragma unroll
     for (int k = 0; k < TT; ++k) {
@@ -111,7 +130,7 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
 // sequences, and all loads of the thread are issued before any is used.  A
 // sequence whose slot is outside the pool is skipped (its loads are clamped
 // to row 0 and nothing is stored).
-template <typename T, int LPC, int SPT>
+template <typename T, int LPC, int SPT, bool BCV>
 __global__ __launch_bounds__(kBlock) void state_step_seq_kernel(StepArgs a) {
   constexpr int N = 4 * LPC;
   constexpr int kCh = kBlock / LPC;  // channels per block
@@ -146,11 +165,8 @@ __global__ __launch_bounds__(kBlock) void state_step_seq_kernel(StepArgs a) {
     xv[k] = to_f32(xp[sq[k] * D + d]);
     dv[k] = to_f32(dp[sq[k] * D + d]);
     zv[k] = to_f32(zsrc[sq[k] * D + d]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      Bv[k][j] = to_f32(static_cast<const T *>(a.Bm)[sq[k] * N + 4 * q + j]);
-      Cv[k][j] = to_f32(static_cast<const T *>(a.Cm)[sq[k] * N + 4 * q + j]);
-    }
+    load4<T, BCV>(static_cast<const T *>(a.Bm) + sq[k] * N + 4 * q, Bv[k]);
+    load4<T, BCV>(static_cast<const T *>(a.Cm) + sq[k] * N + 4 * q, Cv[k]);
   }
   const float Ar[4] = {Av.x, Av.y, Av.z, Av.w};
 #pragma unroll
@@ -180,17 +196,28 @@ __global__ __launch_bounds__(kBlock) void state_step_seq_kernel(StepArgs a) {
     if (act && ok[k]) reinterpret_cast<float4 *>(a.state + (row[k] * D + d) * N)[q] = hv[k];
 }
 
-template <typename T, int LPC>
-hipError_t launch_t(const StepArgs &a, hipStream_t st) {
+template <typename T, int LPC, bool BCV>
+hipError_t launch_tv(const StepArgs &a, hipStream_t st) {
   constexpr int kCh = kBlock / LPC;
-  dim3 grid(static_cast<unsigned>((a.D + kCh - 1) / kCh), static_cast<unsigned>(a.S));
   if (a.T == 1) {
     constexpr int kSPT = 2;
     dim3 gs(static_cast<unsigned>((a.D + kCh - 1) / kCh), static_cast<unsigned>((a.S + kSPT - 1) / kSPT));
-    state_step_seq_kernel<T, LPC, kSPT><<<gs, kBlock, 0, st>>>(a);
-  } else
-    state_update_kernel<T, LPC, 4><<<grid, kBlock, 0, st>>>(a);
+    state_step_seq_kernel<T, LPC, kSPT, BCV><<<gs, kBlock, 0, st>>>(a);
+  } else {
+    dim3 grid(static_cast<unsigned>((a.D + kCh - 1) / kCh), static_cast<unsigned>(a.S));
+    state_update_kernel<T, LPC, 4, BCV><<<grid, kBlock, 0, st>>>(a);
+  }
   return hipGetLastError();
+}
+
+template <typename T, int LPC>
+hipError_t launch_t(const StepArgs &a, hipStream_t st) {
+  // a lane's 4 B (or C) values start at a multiple of 4 elements: one load
+  // when the rows are aligned to 4 elements
+  const uintptr_t al = 4 * sizeof(T);
+  if (reinterpret_cast<uintptr_t>(a.Bm) % al == 0 && reinterpret_cast<uintptr_t>(a.Cm) % al == 0)
+    return launch_tv<T, LPC, true>(a, st);
+  return launch_tv<T, LPC, false>(a, st);
 }
 
 template <typename T>
