@@ -103,6 +103,45 @@ def test_decode_unaligned_state_uses_per_lane_path(oracle_mod):
     assert_close(to_np(state), rh, "f32", "state")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_unaligned_bc_element_loads(oracle_mod, dtype):
+    """B and C rows offset by one element (not 4-element aligned) take the
+    element-load path of the vectorised step, single- and multi-token, and
+    agree bit for bit with the aligned rows."""
+    import mamba_selective_scan_ssm_amd as ssm
+    S, D, N, T = 3, 96, 16, 5
+    dec = gen.make_decode(S, D, N, T, dtype=dtype, seed=33)
+    _say("decode unaligned B/C", dtype)
+
+    def shifted(t):  # same values, one element past an aligned start
+        buf = torch.zeros(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    xs, ds, zs, bs, cs = (to_dev(getattr(dec, k)) for k in ("x", "delta", "z", "Bm", "Cm"))
+    A, Ds = to_dev(dec.A), to_dev(dec.D_skip)
+    outs = {}
+    for name, mk in (("aligned", lambda t: t), ("shifted", shifted)):
+        st1 = to_dev(dec.state0).clone()
+        y1 = [ssm.state_update(st1, xs[t], ds[t], A, mk(bs[t].contiguous()), mk(cs[t].contiguous()), Ds, zs[t])
+              for t in range(T)]
+        stT = to_dev(dec.state0).clone()
+        tr = lambda v: v.transpose(0, 1).contiguous()  # (S, T, ...)
+        yT = ssm.decode_steps(stT, tr(xs), tr(ds), A, mk(tr(bs)), mk(tr(cs)), Ds, tr(zs))
+        torch.cuda.synchronize()
+        outs[name] = (torch.stack(y1, 1), st1, yT, stT)
+    for a, b in zip(outs["aligned"], outs["shifted"]):
+        assert torch.equal(a, b)
+    ry, rh = oracle_mod.scan(_tr(dec.x.f32), _tr(dec.delta.f32), dec.A, _tr(dec.Bm.f32),
+                             _tr(dec.Cm.f32), dec.D_skip, _tr(dec.z.f32), dec.state0)
+    y1, st1, yT, stT = outs["shifted"]
+    assert_close(to_np(y1), ry, dtype, "y single-token")
+    assert_close(to_np(st1), rh, dtype, "state single-token")
+    assert_close(to_np(yT), ry, dtype, "y multi-token")
+    assert_close(to_np(stT), rh, dtype, "state multi-token")
+
+
 def test_decode_batch_invariance_bitwise():
     import mamba_selective_scan_ssm_amd as ssm
     dec = gen.make_decode(5, 640, 16, 4, dtype="bf16", seed=33)
