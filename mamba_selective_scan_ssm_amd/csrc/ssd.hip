@@ -700,7 +700,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
       // block J + 1 run on the matrix cores while block J's M is formed
       f32x16 cn;
       cb_block(0, cf, cn);
-#pragma unroll 2
       for (int J = 0; J <= I; ++J) {
         const f32x16 cb = cn;  // (its products were issued a block ago)
         const bool diag = J == I;
