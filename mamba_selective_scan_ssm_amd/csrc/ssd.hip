@@ -17,13 +17,19 @@
 // rounding order.  All exponents are <= 0 (A < 0 is not required: the code
 // never forms exp(-S_j) alone, only differences with i >= j).
 //
-// Three kernels (grid = chunk x head x batch for 1 and 3):
+// Three kernels:
 //  1. ssd_chunk_state: dS = Xw^T B on MFMA (Xw = x scaled by the decay to the
 //     chunk end and dt), written fp32 to the workspace; also exp(S_end).
-//  2. ssd_state_pass: per (b, h, p, n) the fp32 recurrence over chunks,
-//     seeded by h0, replacing each dS_c with the state entering chunk c.
-//  3. ssd_chunk_scan: CB^T = B C^T on MFMA per 32x32 block pair, masked and
-//     decayed in registers, then Y += M X and Y_off = C h_in on MFMA.
+//     N <= 128: one workgroup per (chunk, group) looping over the group's
+//     heads (the chunk's B read once); larger N: one per (chunk, head).
+//  2. ssd_state_pass: per (b, h, four consecutive (p, n)) the fp32
+//     recurrence over chunks, seeded by h0, replacing each dS_c with the
+//     state entering chunk c.
+//  3. ssd_chunk_scan: CB^T = B C^T on MFMA per 32x32 block pair, decayed in
+//     registers (left of the diagonal with the decay factored at the row
+//     block's first row, on it element by element and masked), then
+//     Y += M X and Y_off = C h_in on MFMA.  N <= 128: one workgroup per
+//     (chunk, group) looping over the heads; larger N: one per (chunk, head).
 //
 // Precision: B, C and x arrive in bf16 and enter the MFMA unchanged (exact).
 // Operands that are products computed here (the decayed scores M, the scaled
