@@ -23,9 +23,11 @@
 // backwards: it reloads a segment's entering state, recomputes the
 // segment's 8 states into registers, then runs the reverse recurrence over
 // them.  A segment's inputs are loaded by the whole workgroup one segment
-// ahead (coalesced over channels), converted once, and staged in LDS with
-// the gate and step-size factors already applied; its per-token outputs go
-// back through LDS to coalesced stores.  Sums across lanes use DPP: over a
+// ahead (coalesced over channels, kept as raw bits until they are staged,
+// with no load behind a branch, so the loads stay in flight through the
+// current segment), converted once, and staged in LDS with the gate and
+// step-size factors already applied; its per-token outputs go back through
+// LDS to coalesced buffer stores that every thread issues on every path.  Sums across lanes use DPP: over a
 // channel's lanes, and over half the channels of a row of 16 lanes for dB
 // and dC, whose partials meet in LDS; the workgroup writes one partial per
 // (token, n).  Two small kernels then add the partials of the channel tiles
