@@ -50,7 +50,7 @@ def test_random_scan(oracle_mod, case):
 BWD_CASES = [dict(B=int(RNG.integers(1, 3)), L=int(RNG.choice([1, 7, 8, 9, 40, 65])),
                   D=int(RNG.choice([1, 3, 64, 65, 130])), N=int(RNG.choice([4, 8, 16, 32, 64])),
                   dtype=str(RNG.choice(["f32", "bf16"])), gate=bool(RNG.integers(0, 2)),
-                  softplus=bool(RNG.integers(0, 2)), seed=3100 + i) for i in range(12)]
+                  softplus=bool(RNG.integers(0, 2)), seed=3100 + i) for i in range(18)]
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{B}L{L}D{D}N{N}{dtype}".format(**c))
@@ -79,7 +79,7 @@ def test_random_bwd(oracle_mod, case):
 
 POOL_CASES = [dict(S=int(RNG.integers(1, 6)), T=int(RNG.choice([1, 2, 5, 16, 17, 30])),
                    D=int(RNG.choice([2, 31, 64, 100])), N=int(RNG.choice([4, 5, 16, 64])),
-                   dtype=str(RNG.choice(["f32", "bf16"])), seed=3200 + i) for i in range(10)]
+                   dtype=str(RNG.choice(["f32", "bf16"])), seed=3200 + i) for i in range(16)]
 
 
 @pytest.mark.parametrize("case", POOL_CASES, ids=lambda c: "S{S}T{T}D{D}N{N}{dtype}".format(**c))
@@ -131,7 +131,7 @@ def _ssd_case(i):
                 chunk=int(RNG.choice([64, 128, 256])), gate=bool(RNG.integers(0, 2)), seed=3400 + i)
 
 
-SSD_CASES = [_ssd_case(i) for i in range(10)]
+SSD_CASES = [_ssd_case(i) for i in range(18)]
 
 
 @pytest.mark.parametrize("case", SSD_CASES, ids=lambda c: "B{B}L{L}H{H}G{G}N{N}c{chunk}".format(**c))
