@@ -11,7 +11,9 @@ The JSON line also carries
   with HIP events on the launch stream), plus its algorithmic HBM bandwidth
   against the 8 TB/s peak;
 * cpu_baseline: the fp64 CPU oracle (untuned, threads over channels) timed
-  on a bounded sample of the same workload;
+  on a bounded sample of the same workload, and on one core;
+* copy_GBs: a plain elementwise kernel reading and writing 1 GiB each, the
+  practical ceiling the HBM-bound rates are also given against (copy_frac);
 * rows: the other hot-path entry points measured the same way -- the decode
   step (S=256, D=5120, N=16, 128 steps), the Mamba-2 SSD chunked scan
   (B=2, L=8192, H=80, P=64, N=128, G=8, chunk 256) and the width-4 causal
@@ -142,9 +144,28 @@ def cpu_baseline(inp, n_seq: int):
                 inp.h0, channels=ch, threads=threads)
     dt = time.perf_counter() - t0
     elems = n_seq * inp.L * D * inp.N
+    # the same oracle on one core, over the first 512 channels of sequence 0
+    ch1 = np.arange(512, dtype=np.int64)
+    t1 = time.perf_counter()
+    oracle.scan(inp.x.f32, inp.delta.f32, inp.A, inp.Bm.f32, inp.Cm.f32, inp.D_skip, inp.z.f32,
+                inp.h0, channels=ch1, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": elems / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_seq} of {inp.B} sequences (all {D} channels, L={inp.L}, N={inp.N}), "
-                      f"fp64 sequential recurrence, {dt:.2f} s wall"}
+                      f"fp64 sequential recurrence, {dt:.2f} s wall",
+            "one_core": {"value": len(ch1) * inp.L * inp.N / dt1 / 1e9, "unit": "Gelem/s",
+                         "sample": f"512 channels of sequence 0, L={inp.L}, N={inp.N}, {dt1:.2f} s"}}
+
+
+def copy_bandwidth(torch, nbytes=1 << 30):
+    """GB/s of a plain device elementwise kernel reading and writing nbytes
+    each (torch's multiply), timed like the hot-path rows: the practical
+    ceiling the HBM-bound rows are also reported against."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    mean_ms, _, _ = time_calls(lambda: torch.mul(a, 1.5, out=b), 20, 5, torch)
+    del a, b
+    return 2 * nbytes / (mean_ms * 1e-3) / 1e9
 
 
 def bench_decode(torch, ssm, gen, steps_meas=128):
@@ -427,9 +448,16 @@ def main():
         "roofline": roofline,
     }
     if not args.no_rows and args.only is None:
+        copy_gbs = copy_bandwidth(torch)
+        out["copy_GBs"] = copy_gbs
+        out["roofline"]["hbm"]["frac_of_copy"] = hbm_gbs / copy_gbs
         out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen, steps=20),
                        "conv": bench_conv(torch, ssm, gen), "pool_decode": bench_pool_decode(torch, ssm, gen),
                        "bwd": bench_bwd(torch, ssm, gen)}
+        for row in out["rows"].values():  # HBM rates also as a fraction of the copy
+            for r in [row] + [v for v in row.values() if isinstance(v, dict)]:
+                if "hbm_GBs" in r:
+                    r["copy_frac"] = r["hbm_GBs"] / copy_gbs
     if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
     print(json.dumps(out))
