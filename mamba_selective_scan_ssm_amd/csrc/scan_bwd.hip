@@ -181,8 +181,11 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
   // staged segment: step size, x, gradient reaching q (dy silu(z)); B, C rows
   __shared__ float s_dl[kSeg][kCh], s_x[kSeg][kCh], s_g[kSeg][kCh];
   __shared__ __attribute__((aligned(16))) float s_B[kSeg][N], s_C[kSeg][N];
-  // per (token, channel): dx, ddelta before the softplus slope, q
-  __shared__ float s_o[3][kSeg][kCh];
+  // per (token, channel): dx, ddelta before the softplus slope, q.  Lane q
+  // of a channel stores entries q, q + LPC, ... (all its lanes hold the same
+  // sums), rows past the third being spare, so the stores take no branch.
+  constexpr int kOS = (3 + LPC - 1) / LPC;        // stores per lane and token
+  __shared__ float s_o[kOS * LPC][kSeg][kCh];
   constexpr int kRowCh = 16 / LPC;                // channels per row of 16 lanes
   constexpr int kSPR = kRowCh >= 2 ? 2 : 1;       // partial sums per row
   constexpr int kSlots = 16 * kSPR;               // per workgroup
@@ -371,21 +374,40 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
         }
         dxp = channel_sum<LPC>(dxp);
         const float ddl = fmaf(xv, dxp, channel_sum<LPC>(dda));
-        if (q == 0) {
-          s_o[0][k][c] = fmaf(dl, dxp, Dd * g);
-          s_o[1][k][c] = ddl;
-          s_o[2][k][c] = qs;
+        {
+          const float dxv = fmaf(dl, dxp, Dd * g);
+#pragma unroll
+          for (int i = 0; i < kOS; ++i) {
+            const int row = q + i * LPC;
+            s_o[row][k][c] = row == 0 ? dxv : (row == 1 ? ddl : qs);
+          }
         }
         dDacc = fmaf(g, xv, dDacc);
-        // dB / dC: partial sums over the row's channels, written by the
-        // lanes of the row's channels 0 and R/2
-#pragma unroll
-        for (int i = 0; i < 2 * SPL; ++i) v[i] = row_half_sum<LPC>(v[i]);
         const int rc = (lane % 16) / LPC;  // channel within the row
-        if (rc % (kRowCh / kSPR) == 0) {
-          float *dst = &s_red[(wave * 4 + lane / 16) * kSPR + rc / (kRowCh / kSPR)][k][SPL * q];
-          st_spl<SPL>(dst, v);
-          st_spl<SPL>(dst + N, v + SPL);
+        if constexpr (LPC == 4) {
+          // dB / dC over the row's 4 channels, whose parity alternates: an
+          // even channel's lanes add the dB terms of the channel one over
+          // (a row rotation by 4 lanes), an odd channel's lanes its dC terms.
+          // Either pair of windows covers the row once, so every lane stores
+          // one vector of SPL partials and no lane idles in a branch.
+          const bool odd = rc & 1;
+          float w[SPL];
+#pragma unroll
+          for (int j = 0; j < SPL; ++j) {
+            const float other = odd ? v[j] : v[SPL + j];
+            w[j] = (odd ? v[SPL + j] : v[j]) + dpp_f<kRowRor + 4>(other);
+          }
+          st_spl<SPL>(&s_red[(wave * 4 + lane / 16) * kSPR + rc / 2][k][(odd ? N : 0) + SPL * q], w);
+        } else {
+          // dB / dC: partial sums over the row's channels, written by the
+          // lanes of the row's channels 0 and R/2
+#pragma unroll
+          for (int i = 0; i < 2 * SPL; ++i) v[i] = row_half_sum<LPC>(v[i]);
+          if (rc % (kRowCh / kSPR) == 0) {
+            float *dst = &s_red[(wave * 4 + lane / 16) * kSPR + rc / (kRowCh / kSPR)][k][SPL * q];
+            st_spl<SPL>(dst, v);
+            st_spl<SPL>(dst + N, v + SPL);
+          }
         }
       }
     }
