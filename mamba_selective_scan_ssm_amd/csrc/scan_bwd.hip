@@ -306,9 +306,13 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
       }
       wz[e] = w;
       if (k < kSeg) {
-        s_dl[k][cs] = step_size(raw, bias_s, a.delta_softplus);
-        s_x[k][cs] = r.f(r.x[e]);
-        s_g[k][cs] = s_active ? gq : 0.f;  // channels past D: no gradient flows
+        // tokens past L stage zeros, through which the state and lam pass
+        // unchanged (exp(0) = 1, u = g = 0), so the token loops below need no
+        // branch; channels past D: no gradient flows
+        const bool tok = t0 + k < L;
+        s_dl[k][cs] = tok ? step_size(raw, bias_s, a.delta_softplus) : 0.f;
+        s_x[k][cs] = tok ? r.f(r.x[e]) : 0.f;
+        s_g[k][cs] = tok && s_active ? gq : 0.f;
       }
     }
 #pragma unroll
@@ -332,84 +336,82 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kSeg; ++k) {
-      if (k < nt) {
-        const float dl = s_dl[k][c];
-        const float u = dl * s_x[k][c];
-        float bv[SPL];
-        ld_spl<SPL>(&s_B[k][SPL * q], bv);
+      const float dl = s_dl[k][c];
+      const float u = dl * s_x[k][c];
+      float bv[SPL];
+      ld_spl<SPL>(&s_B[k][SPL * q], bv);
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-          aS[k][j] = fast_exp2(dl * A2[j]);
-          H[k + 1][j] = fmaf(aS[k][j], H[k][j], u * bv[j]);
-        }
+      for (int j = 0; j < SPL; ++j) {
+        aS[k][j] = fast_exp2(dl * A2[j]);
+        H[k + 1][j] = fmaf(aS[k][j], H[k][j], u * bv[j]);
       }
     }
 #pragma unroll
     for (int k = kSeg - 1; k >= 0; --k) {
-      if (k < nt) {
-        const float dl = s_dl[k][c];
-        const float xv = s_x[k][c];
-        const float g = s_g[k][c];
-        float Bv[SPL], Cv[SPL];
-        ld_spl<SPL>(&s_B[k][SPL * q], Bv);
-        ld_spl<SPL>(&s_C[k][SPL * q], Cv);
-        float qp = 0.f;
+      const float dl = s_dl[k][c];
+      const float xv = s_x[k][c];
+      const float g = s_g[k][c];
+      float Bv[SPL], Cv[SPL];
+      ld_spl<SPL>(&s_B[k][SPL * q], Bv);
+      ld_spl<SPL>(&s_C[k][SPL * q], Cv);
+      float qp = 0.f;
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) qp = fmaf(Cv[j], H[k + 1][j], qp);
-        const float qs = fmaf(Dd, xv, channel_sum<LPC>(qp));
-        const float u = dl * xv;
-        float v[2 * SPL];  // dB then dC contributions of the lane's states
-        // ddelta = sum_n lam A a h_prev + x sum_n lam B; the second sum is dx's
-        float dda = 0.f, dxp = 0.f;
+      for (int j = 0; j < SPL; ++j) qp = fmaf(Cv[j], H[k + 1][j], qp);
+      const float qs = fmaf(Dd, xv, channel_sum<LPC>(qp));
+      const float u = dl * xv;
+      float v[2 * SPL];  // dB then dC contributions of the lane's states
+      // ddelta = sum_n lam A a h_prev + x sum_n lam B; the second sum is dx's
+      float dda = 0.f, dxp = 0.f;
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-          lam[j] = fmaf(g, Cv[j], lam[j]);
-          v[j] = lam[j] * u;
-          v[SPL + j] = g * H[k + 1][j];
-          const float w = lam[j] * (aS[k][j] * H[k][j]);
-          dda = fmaf(An[j], w, dda);
-          dAacc[j] = fmaf(w, dl, dAacc[j]);
-          dxp = fmaf(lam[j], Bv[j], dxp);
-          lam[j] *= aS[k][j];
-        }
-        dxp = channel_sum<LPC>(dxp);
-        const float ddl = fmaf(xv, dxp, channel_sum<LPC>(dda));
-        {
-          const float dxv = fmaf(dl, dxp, Dd * g);
+      for (int j = 0; j < SPL; ++j) {
+        lam[j] = fmaf(g, Cv[j], lam[j]);
+        v[j] = lam[j] * u;
+        v[SPL + j] = g * H[k + 1][j];
+        const float w = lam[j] * (aS[k][j] * H[k][j]);
+        dda = fmaf(An[j], w, dda);
+        dAacc[j] = fmaf(w, dl, dAacc[j]);
+        dxp = fmaf(lam[j], Bv[j], dxp);
+        lam[j] *= aS[k][j];
+      }
+      dxp = channel_sum<LPC>(dxp);
+      const float ddl = fmaf(xv, dxp, channel_sum<LPC>(dda));
+      {
+        const float dxv = fmaf(dl, dxp, Dd * g);
 #pragma unroll
-          for (int i = 0; i < kOS; ++i) {
-            const int row = q + i * LPC;
-            s_o[row][k][c] = row == 0 ? dxv : (row == 1 ? ddl : qs);
-          }
-        }
-        dDacc = fmaf(g, xv, dDacc);
-        const int rc = (lane % 16) / LPC;  // channel within the row
-        if constexpr (LPC == 4) {
-          // dB / dC over the row's 4 channels, whose parity alternates: an
-          // even channel's lanes add the dB terms of the channel one over
-          // (a row rotation by 4 lanes), an odd channel's lanes its dC terms.
-          // Either pair of windows covers the row once, so every lane stores
-          // one vector of SPL partials and no lane idles in a branch.
-          const bool odd = rc & 1;
-          float w[SPL];
-#pragma unroll
-          for (int j = 0; j < SPL; ++j) {
-            const float other = odd ? v[j] : v[SPL + j];
-            w[j] = (odd ? v[SPL + j] : v[j]) + dpp_f<kRowRor + 4>(other);
-          }
-          st_spl<SPL>(&s_red[(wave * 4 + lane / 16) * kSPR + rc / 2][k][(odd ? N : 0) + SPL * q], w);
-        } else {
-          // dB / dC: partial sums over the row's channels, written by the
-          // lanes of the row's channels 0 and R/2
-#pragma unroll
-          for (int i = 0; i < 2 * SPL; ++i) v[i] = row_half_sum<LPC>(v[i]);
-          if (rc % (kRowCh / kSPR) == 0) {
-            float *dst = &s_red[(wave * 4 + lane / 16) * kSPR + rc / (kRowCh / kSPR)][k][SPL * q];
-            st_spl<SPL>(dst, v);
-            st_spl<SPL>(dst + N, v + SPL);
-          }
+        for (int i = 0; i < kOS; ++i) {
+          const int row = q + i * LPC;
+          s_o[row][k][c] = row == 0 ? dxv : (row == 1 ? ddl : qs);
         }
       }
+      dDacc = fmaf(g, xv, dDacc);
+      const int rc = (lane % 16) / LPC;  // channel within the row
+      if constexpr (LPC == 4) {
+        // dB / dC over the row's 4 channels, whose parity alternates: an
+        // even channel's lanes add the dB terms of the channel one over
+        // (a row rotation by 4 lanes), an odd channel's lanes its dC terms.
+        // Either pair of windows covers the row once, so every lane stores
+        // one vector of SPL partials and no lane idles in a branch.
+        const bool odd = rc & 1;
+        float w[SPL];
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+          const float other = odd ? v[j] : v[SPL + j];
+          w[j] = (odd ? v[SPL + j] : v[j]) + dpp_f<kRowRor + 4>(other);
+        }
+        st_spl<SPL>(&s_red[(wave * 4 + lane / 16) * kSPR + rc / 2][k][(odd ? N : 0) + SPL * q], w);
+      } else {
+        // dB / dC: partial sums over the row's channels, written by the
+        // lanes of the row's channels 0 and R/2
+#pragma unroll
+        for (int i = 0; i < 2 * SPL; ++i) v[i] = row_half_sum<LPC>(v[i]);
+        if (rc % (kRowCh / kSPR) == 0) {
+          float *dst = &s_red[(wave * 4 + lane / 16) * kSPR + rc / (kRowCh / kSPR)][k][SPL * q];
+          st_spl<SPL>(dst, v);
+          st_spl<SPL>(dst + N, v + SPL);
+        }
+      }
+      // the scheduler may interleave two tokens; more overlap spills
+      if (k % 2 == 0) __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     for (int e = tid; e < nt * 2 * N; e += kBwdThreads) {
@@ -465,20 +467,32 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
   if (q == 0) PD[b * D + d] = dDacc;
 }
 
-// dB, dC: sum of the channel tiles' partials, tiles in order
+// dB, dC: sum of the channel tiles' partials.  A workgroup per (b, t)
+// row, whose partials (ntile, 2N) are contiguous: thread i reads entries i,
+// i + 256, ... (coalesced), all of column i % 2N since 2N divides 256, and
+// adds them in tile order; the 256 / 2N sums of a column are then added in
+// order, so the result does not depend on timing.
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(int64_t rows, int64_t N, int64_t ntile,
                                                             const float *P, float *dB, float *dC) {
-  const int64_t N2 = 2 * N;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= rows * N2) return;
-  const int64_t row = i / N2, j = i % N2;
-  const float *p = P + row * ntile * N2 + j;
-  float v = 0.f;
-  for (int64_t t = 0; t < ntile; ++t) v += p[t * N2];
-  if (j < N)
-    dB[row * N + j] = v;
-  else
-    dC[row * N + j - N] = v;
+  __shared__ float s_p[256];
+  const int64_t N2 = 2 * N, tot = ntile * N2;
+  const int tid = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const float *p = P + row * tot;
+    float v = 0.f;
+    for (int64_t e = tid; e < tot; e += 256) v += p[e];
+    __syncthreads();  // the previous row's sums are read
+    s_p[tid] = v;
+    __syncthreads();
+    if (tid < N2) {
+      float r = 0.f;
+      for (int m = tid; m < 256; m += static_cast<int>(N2)) r += s_p[m];
+      if (tid < N)
+        dB[row * N + tid] = r;
+      else
+        dC[row * N + tid - N] = r;
+    }
+  }
 }
 
 // dA, dD, dbias: sum of the sequences' partials, sequences in order
@@ -518,10 +532,13 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
     dim3 grid(static_cast<unsigned>(ntile), static_cast<unsigned>(a.B));
     scan_bwd_kernel<T, LPC, SPL><<<grid, kBwdThreads, 0, s>>>(a);
   }
-  const int64_t nbc = a.B * a.L * 2 * a.N;
-  if (nbc > 0)
-    bwd_reduce_bc_kernel<<<static_cast<unsigned>((nbc + 255) / 256), 256, 0, s>>>(a.B * a.L, a.N, ntile, P,
-                                                                              a.dB, a.dC);
+  // a workgroup per (b, t) row (grid-strided past 2^20 rows); 2N (8 .. 128)
+  // divides the 256 threads
+  static_assert(256 % (2 * LPC * SPL) == 0, "2N must divide the reduction's 256 threads");
+  const int64_t rows = a.B * a.L;
+  if (rows > 0)
+    bwd_reduce_bc_kernel<<<static_cast<unsigned>(rows < (1 << 20) ? rows : (1 << 20)), 256, 0, s>>>(
+        rows, a.N, ntile, P, a.dB, a.dC);
   const int64_t npar = a.D * a.N + 2 * a.D;
   if (npar > 0)
     bwd_reduce_param_kernel<<<static_cast<unsigned>((npar + 255) / 256), 256, 0, s>>>(
