@@ -245,9 +245,10 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
 #pragma unroll
       for (int e = 0; e < SegRegs<T, LPC, SPL, false, kP1>::kE; ++e) {
         const int k = k0 + e * LPC;
-        if (k < kP1) {
-          p_dl[k][cs] = step_size(r.f(r.d[e]), bias_s, a.delta_softplus);
-          p_x[k][cs] = r.f(r.x[e]);
+        if (k < kP1) {  // tokens past L: zeros, as in pass 2
+          const bool tok = t0 + k < L;
+          p_dl[k][cs] = tok ? step_size(r.f(r.d[e]), bias_s, a.delta_softplus) : 0.f;
+          p_x[k][cs] = tok ? r.f(r.x[e]) : 0.f;
         }
       }
 #pragma unroll
@@ -259,16 +260,14 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < kP1; ++k) {
-        if (k < nt) {
-          if (k % kSeg == 0 && active)  // the state entering segment (t0 + k) / kSeg
-            st_spl<SPL>(ck + ((b * nseg + (t0 + k) / kSeg) * D + d) * N + SPL * q, h);
-          const float dl = p_dl[k][c];
-          const float u = dl * p_x[k][c];
-          float bv[SPL];
-          ld_spl<SPL>(&p_B[k][SPL * q], bv);
+        if (k % kSeg == 0 && active && k < nt)  // the state entering segment (t0 + k) / kSeg
+          st_spl<SPL>(ck + ((b * nseg + (t0 + k) / kSeg) * D + d) * N + SPL * q, h);
+        const float dl = p_dl[k][c];
+        const float u = dl * p_x[k][c];
+        float bv[SPL];
+        ld_spl<SPL>(&p_B[k][SPL * q], bv);
 #pragma unroll
-          for (int j = 0; j < SPL; ++j) h[j] = fmaf(fast_exp2(dl * A2[j]), h[j], u * bv[j]);
-        }
+        for (int j = 0; j < SPL; ++j) h[j] = fmaf(fast_exp2(dl * A2[j]), h[j], u * bv[j]);
       }
     }
   }
