@@ -479,7 +479,15 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(int64_t rows, int64_
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const float *p = P + row * tot;
     float v = 0.f;
-    for (int64_t e = tid; e < tot; e += 256) v += p[e];
+    int64_t e = tid;
+    for (; e + 7 * 256 < tot; e += 8 * 256) {  // eight loads in flight, added in order
+      float t[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) t[m] = p[e + m * 256];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) v += t[m];
+    }
+    for (; e < tot; e += 256) v += p[e];
     __syncthreads();  // the previous row's sums are read
     s_p[tid] = v;
     __syncthreads();
