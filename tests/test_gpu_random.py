@@ -148,3 +148,59 @@ def test_random_ssd(oracle_mod, case):
                             None if w.z is None else w.z.f32, w.h0)
     assert_close(to_np(y), ry, "bf16", "y")
     assert_close(to_np(hf), rh, "bf16", "h_final")
+
+
+DEC_CASES = [dict(S=int(RNG.integers(1, 20)), D=int(RNG.choice([2, 31, 64, 100, 130, 320])),
+                  N=int(RNG.choice([1, 4, 5, 8, 16, 32, 64])), dtype=str(RNG.choice(["f32", "bf16"])),
+                  gate=bool(RNG.integers(0, 2)), softplus=bool(RNG.integers(0, 2)), seed=3500 + i)
+             for i in range(14)]
+
+
+@pytest.mark.parametrize("case", DEC_CASES, ids=lambda c: "S{S}D{D}N{N}{dtype}".format(**c))
+def test_random_state_update(oracle_mod, case):
+    """Three single-token steps in place against the oracle's own decode step
+    (step-size bias and softplus drawn too)."""
+    import mamba_selective_scan_ssm_amd as ssm
+    c = case
+    dec = gen.make_decode(c["S"], c["D"], c["N"], 3, dtype=c["dtype"], seed=c["seed"], gate=c["gate"])
+    delta, bias = dec.delta, None
+    if c["softplus"]:
+        delta = gen._store((dec.delta.f32 * 6.0 - 3.0).astype(np.float32), c["dtype"])
+        bias = np.random.default_rng(c["seed"]).normal(0.0, 1.0, c["D"]).astype(np.float32)
+    _say("random state_update", c)
+    st = to_dev(dec.state0)
+    xs, ds, bs, cs, zs = (to_dev(v) for v in (dec.x, delta, dec.Bm, dec.Cm, dec.z))
+    A, Ds = to_dev(dec.A), to_dev(dec.D_skip)
+    bias_d = None if bias is None else to_dev(bias)
+    rs = dec.state0.astype(np.float64).copy()
+    for t in range(3):
+        y = ssm.state_update(st, xs[t], ds[t], A, bs[t], cs[t], Ds, None if zs is None else zs[t],
+                             delta_bias=bias_d, delta_softplus=c["softplus"])
+        torch.cuda.synchronize()
+        ry = oracle_mod.state_update(rs, dec.x.f32[t], delta.f32[t], dec.A, dec.Bm.f32[t], dec.Cm.f32[t],
+                                     dec.D_skip, None if dec.z is None else dec.z.f32[t],
+                                     delta_bias=bias, delta_softplus=c["softplus"])
+        assert_close(to_np(y), ry, c["dtype"], f"y step {t}")
+    assert_close(to_np(st), rs, c["dtype"], "state")
+
+
+CONVU_CASES = [dict(S=int(RNG.integers(1, 20)), D=int(RNG.choice([1, 7, 256, 300])), K=int(RNG.integers(2, 9)),
+                    dtype=str(RNG.choice(["f32", "bf16"])), seed=3600 + i) for i in range(8)]
+
+
+@pytest.mark.parametrize("case", CONVU_CASES, ids=lambda c: "S{S}D{D}K{K}{dtype}".format(**c))
+def test_random_conv_update(oracle_mod, case):
+    """Three decode steps of the convolution in place against the oracle's."""
+    import mamba_selective_scan_ssm_amd as ssm
+    c = case
+    d = gen.make_conv_decode(c["S"], c["D"], c["K"], 3, dtype=c["dtype"], seed=c["seed"])
+    _say("random conv1d_update", c)
+    st, xs = to_dev(d.state0), to_dev(d.x)
+    wd, bd = to_dev(d.w), to_dev(d.bias)
+    rs = d.state0.astype(np.float64).copy()
+    for t in range(3):
+        y = ssm.conv1d_update(st, xs[t], wd, bd)
+        torch.cuda.synchronize()
+        ry = oracle_mod.conv1d_update(rs, d.x.f32[t], d.w, d.bias, act=True)
+        assert_close(to_np(y), ry, c["dtype"], f"y step {t}")
+    assert np.array_equal(to_np(st), rs)
