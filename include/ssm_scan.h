@@ -225,10 +225,11 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
  * dh_final, dh0 and the workspace 16-byte aligned.  N in {4, 8, 16, 32, 64}
  * (else SSM_ERR_UNSUPPORTED).  Outputs must not overlap inputs, the
  * workspace or each other.
- * workspace : at least ssm_scan_bwd_workspace_size() bytes: the states
- *             entering every 8-token segment (B * ceil(L/8) * D * N fp32,
- *             1.34 GB at B=8, L=4096, D=5120, N=16) plus per-channel-tile
- *             partial sums; contents on entry are ignored.
+ * workspace : at least ssm_scan_bwd_workspace_size_ex(B, L, D, N,
+ *             h_ckpt != NULL) bytes: the states entering every 8-token
+ *             segment (B * ceil(L/8) * D * N fp32, 1.34 GB at B=8, L=4096,
+ *             D=5120, N=16; left out when h_ckpt is given) plus
+ *             per-channel-tile partial sums; contents on entry are ignored.
  */
 ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
                         const void *x, const void *delta, const float *A,
@@ -240,8 +241,17 @@ ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
                         float *d_delta_bias, const ssm_delta_opts *dopts,
                         void *workspace, size_t workspace_bytes, void *stream);
 
-/* Device workspace ssm_scan_bwd needs (bytes; 0 for unsupported N). */
+/* Device workspace ssm_scan_bwd needs when it recomputes the segment states
+ * (h_ckpt == NULL); bytes, 0 for unsupported N.  Equal to
+ * ssm_scan_bwd_workspace_size_ex(B, L, D, N, 0). */
 size_t ssm_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N);
+
+/* Device workspace ssm_scan_bwd needs; saved_states = 1 when the call passes
+ * the forward's segment states (h_ckpt != NULL), which then take no
+ * workspace; 0 otherwise.  0 for unsupported N or a saved_states other than
+ * 0 or 1. */
+size_t ssm_scan_bwd_workspace_size_ex(int64_t B, int64_t L, int64_t D, int64_t N,
+                                      int32_t saved_states);
 
 /*
  * ssm_decode_steps -- T decode tokens for each of S sequences whose states
@@ -259,8 +269,10 @@ size_t ssm_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N);
  * state_pool : (pool_rows, D, N) fp32, in/out
  * slot_idx   : (S) int32 DEVICE array, or NULL for slot s = s (then
  *              pool_rows >= S).  Slots outside [0, pool_rows) skip the
- *              sequence (its y rows are not written).  Non-negative slots must
- *              be distinct: two sequences on one row race.
+ *              sequence (its y rows are not written); with pool_rows == 0
+ *              every sequence is skipped and nothing is enqueued.
+ *              Non-negative slots must be distinct: two sequences on one
+ *              row race.
  * x, delta, z, y : (S, T, D) dtype `dt`;  Bm, Cm : (S, T, N) dtype `dt`
  * A : (D, N) fp32;  D_skip : (D) or NULL;  z may be NULL;  dopts as
  * ssm_scan_fwd_ex.  y must not overlap the inputs or the pool; the pool must

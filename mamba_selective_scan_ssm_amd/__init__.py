@@ -82,6 +82,8 @@ def lib():
         L.ssm_scan_bwd.restype = ctypes.c_int
         L.ssm_scan_bwd_workspace_size.argtypes = [i64] * 4
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
+        L.ssm_scan_bwd_workspace_size_ex.argtypes = [i64] * 4 + [ctypes.c_int32]
+        L.ssm_scan_bwd_workspace_size_ex.restype = ctypes.c_size_t
         L.ssm_decode_steps.argtypes = [i64] * 4 + [ctypes.c_int, vp, i64, vp] + [vp] * 8 + [vp, vp]
         L.ssm_decode_steps.restype = ctypes.c_int
         L.ssm_conv1d_fwd.argtypes = [i64] * 4 + [ctypes.c_int] + [vp] * 4 + [ctypes.c_int32, vp, vp, vp]
@@ -340,8 +342,9 @@ def decode_steps(state_pool, x, delta, A, Bm, Cm, D_skip=None, z=None, *, slots=
     return y
 
 
-def scan_bwd_workspace_size(B, L, D, N) -> int:
-    return int(lib().ssm_scan_bwd_workspace_size(B, L, D, N))
+def scan_bwd_workspace_size(B, L, D, N, saved_states=False) -> int:
+    """Workspace bytes of scan_bwd; saved_states: the call passes h_ckpt."""
+    return int(lib().ssm_scan_bwd_workspace_size_ex(B, L, D, N, 1 if saved_states else 0))
 
 
 def scan_fwd_train(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, delta_bias=None,
@@ -403,7 +406,7 @@ def scan_bwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, dy=None, dh_fina
            "dD": torch.empty((D,), **f32) if D_skip is not None else None,
            "dh0": torch.empty((B, D, N), **f32) if want_dh0 else None,
            "dbias": torch.empty((D,), **f32) if want_dbias else None}
-    need = scan_bwd_workspace_size(B, L, D, N)
+    need = scan_bwd_workspace_size(B, L, D, N, saved_states=h_ckpt is not None)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()

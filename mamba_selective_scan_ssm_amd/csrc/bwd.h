@@ -26,12 +26,14 @@ struct BwdArgs {
   float *dB, *dC;            // (B, L, N)
   float *dD, *dbias;         // (D) or null
   float *dh0;                // (B, D, N) or null
-  float *ws;                 // scan_bwd_ws_floats(B, L, D, N) floats
+  float *ws;                 // scan_bwd_ws_floats(B, L, D, N, h_ckpt != null) floats
 };
 
 // Supported: N in {4, 8, 16, 32, 64}.
 bool scan_bwd_supported_n(int64_t N);
-int64_t scan_bwd_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N);
+// Workspace floats: the states entering every 8-token segment (unless the
+// forward saved them), the dB/dC tile partials and the parameter partials.
+int64_t scan_bwd_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, bool saved_states);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
 
 }  // namespace ssm

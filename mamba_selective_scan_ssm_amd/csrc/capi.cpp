@@ -337,6 +337,9 @@ ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtyp
   if (overlaps_any(Range{y, nX * es}, ins) || overlap(Range{y, nX * es}, pool))
     return SSM_ERR_INVALID_ARG;
   if (overlaps_any(pool, ins)) return SSM_ERR_INVALID_ARG;
+  // an empty pool: every slot lies outside it, so every sequence is skipped
+  // (and no kernel may read a state row)
+  if (slot_idx != nullptr && pool_rows == 0) return SSM_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T <= kDecodeLoopMaxT) {
     // the decode-step kernel, state carried in registers over the T tokens
@@ -367,8 +370,14 @@ ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtyp
 }
 
 size_t ssm_scan_bwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N) {
+  return ssm_scan_bwd_workspace_size_ex(B, L, D, N, 0);
+}
+
+size_t ssm_scan_bwd_workspace_size_ex(int64_t B, int64_t L, int64_t D, int64_t N,
+                                      int32_t saved_states) {
   if (B < 0 || L < 0 || D < 0 || N < 0 || !ssm::scan_bwd_supported_n(N)) return 0;
-  return static_cast<size_t>(ssm::scan_bwd_ws_floats(B, L, D, N)) * sizeof(float);
+  if (saved_states != 0 && saved_states != 1) return 0;
+  return static_cast<size_t>(ssm::scan_bwd_ws_floats(B, L, D, N, saved_states == 1)) * sizeof(float);
 }
 
 ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
@@ -391,7 +400,7 @@ ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
   if (!z && dz) return SSM_ERR_INVALID_ARG;
   auto a16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   if (!a16(A) || !a16(h0) || !a16(dh_final) || !a16(dh0) || !a16(h_ckpt)) return SSM_ERR_UNSUPPORTED;
-  const size_t need = ssm_scan_bwd_workspace_size(B, L, D, N);
+  const size_t need = ssm_scan_bwd_workspace_size_ex(B, L, D, N, h_ckpt != nullptr ? 1 : 0);
   if (need > 0 && (!workspace || workspace_bytes < need || !a16(workspace))) return SSM_ERR_WORKSPACE;
   const Range ins[] = {{x, nX * es},     {delta, nX * es},    {A, D * N * 4},
                        {Bm, nBC * es},   {Cm, nBC * es},      {D_skip, D * 4},

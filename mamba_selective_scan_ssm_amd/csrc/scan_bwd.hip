@@ -210,7 +210,9 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
 
   const int64_t nseg = bwd_nseg(L);
   float *ck = a.ws;                      // (B, nseg, D, N) entering states
-  float *P = ck + B * nseg * D * N;      // (B, L, ntile, 2N) dB|dC partials
+  // (B, L, ntile, 2N) dB|dC partials, after the entering states unless the
+  // forward saved them (then the workspace holds no states)
+  float *P = ck + (a.h_ckpt ? 0 : B * nseg * D * N);
   // the entering states: from the forward when it saved them, else pass 1
   const float *ckr = a.h_ckpt ? a.h_ckpt : ck;
   float *PA = P + B * L * ntile * 2 * N; // (B, D, N) dA partials
@@ -531,7 +533,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s) {
   const int64_t kCh = bwd_channels_per_block(a.N);
   const int64_t ntile = (a.D + kCh - 1) / kCh;
   const int64_t nseg = bwd_nseg(a.L);
-  float *P = a.ws + a.B * nseg * a.D * a.N;
+  float *P = a.ws + (a.h_ckpt ? 0 : a.B * nseg * a.D * a.N);
   float *PA = P + a.B * a.L * ntile * 2 * a.N;
   float *PD = PA + a.B * a.D * a.N;
   float *PB = PD + a.B * a.D;
@@ -569,11 +571,11 @@ hipError_t launch_bwd_dt(const BwdArgs &a, hipStream_t s) {
 
 bool scan_bwd_supported_n(int64_t N) { return N == 4 || N == 8 || N == 16 || N == 32 || N == 64; }
 
-int64_t scan_bwd_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N) {
+int64_t scan_bwd_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, bool saved_states) {
   if (!scan_bwd_supported_n(N)) return 0;
   const int64_t kCh = bwd_channels_per_block(N);
   const int64_t ntile = (D + kCh - 1) / kCh;
-  return B * bwd_nseg(L) * D * N + B * L * ntile * 2 * N + B * D * N + 2 * B * D;
+  return (saved_states ? 0 : B * bwd_nseg(L) * D * N) + B * L * ntile * 2 * N + B * D * N + 2 * B * D;
 }
 
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {

@@ -376,10 +376,6 @@ __device__ __forceinline__ float word_elem(const uint32_t *w, int e) {
   }
 }
 
-#ifndef SSM_LS_CYCLE
-#define SSM_LS_CYCLE 4
-#endif
-
 // CK: also write the state entering every 8-token segment to a.h_ckpt
 // (B, ceil(L/8), D, N) -- what a training step's backward recomputes
 // otherwise.  A block of this kernel is exactly one such segment.
@@ -394,7 +390,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   constexpr int kV = kN / 4;            // B or C values each lane converts per block
   constexpr int kWords = (kV * static_cast<int>(sizeof(T)) + 3) / 4;
   constexpr uint32_t kES = sizeof(T);
-  constexpr int kCyc = SSM_LS_CYCLE;    // blocks per load cycle
+  constexpr int kCyc = 4;               // blocks per load cycle
   static_assert(LPC == 1 || LPC == 2 || LPC == 4, "LPC must be 1, 2 or 4");
   static_assert(SPL % kV == 0, "a loader lane's values must fall in one lane's slice");
   static_assert(kPairs * 64 * 2 == TB * kCPW, "pair slots must tile the block");
@@ -762,10 +758,7 @@ struct SplitCfg {
 };
 
 // tokens per LDS stage / barrier (segment lengths are multiples of it)
-#ifndef SSM_SCAN_BLOCK_TOKENS
-#define SSM_SCAN_BLOCK_TOKENS 8
-#endif
-constexpr int kBlockTokens = SSM_SCAN_BLOCK_TOKENS;
+constexpr int kBlockTokens = 8;
 
 }  // namespace
 
@@ -849,14 +842,7 @@ hipError_t dispatch_lanesplit(const ScanArgs &a, hipStream_t s) {
   switch (a.N) {
     case 4: return launch_lanesplit_t<T, 1, 4>(a, s);
     case 8: return launch_lanesplit_t<T, 2, 4>(a, s);
-    case 16:
-#if defined(SSM_LS_N16_LPC) && SSM_LS_N16_LPC == 2
-      return launch_lanesplit_t<T, 2, 8>(a, s);
-#elif defined(SSM_LS_N16_LPC) && SSM_LS_N16_LPC == 1
-      return launch_lanesplit_t<T, 1, 16>(a, s);
-#else
-      return launch_lanesplit_t<T, 4, 4>(a, s);
-#endif
+    case 16: return launch_lanesplit_t<T, 4, 4>(a, s);
     case 32: return launch_lanesplit_t<T, 4, 8>(a, s);
     case 64: return launch_lanesplit_t<T, 4, 16>(a, s);
     default: return hipErrorNotSupported;

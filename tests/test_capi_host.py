@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     for n in ("ssm_scan_fwd", "ssm_scan_fwd_workspace_size", "ssm_state_update", "ssm_ssd_fwd",
               "ssm_ssd_fwd_workspace_size", "ssm_conv1d_fwd", "ssm_conv1d_update",
               "ssm_scan_fwd_ex", "ssm_state_update_ex", "ssm_ssd_fwd_ex", "ssm_decode_steps",
-              "ssm_scan_bwd", "ssm_scan_bwd_workspace_size", "ssm_scan_fwd_train",
+              "ssm_scan_bwd", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd_workspace_size_ex",
+              "ssm_scan_fwd_train",
               "ssm_status_string", "ssm_version"):
         assert n in names
 
@@ -239,6 +240,11 @@ def test_decode_steps_validation(lib):
     assert ds(y=P[1]) == INVALID                  # y on x
     assert ds(pool=8, y=P[0]) == INVALID          # y inside the pool
     assert ds(x=None) == INVALID
+    # an empty pool with slot indices: every slot is outside it, every
+    # sequence is skipped and nothing is launched (no state row may be read)
+    assert ds(pool=0, slots=P[9]) == OK
+    assert ds(pool=0, slots=P[9], T=1) == OK
+    assert ds(pool=0, slots=P[9], T=40) == OK
 
 
 Q = [ctypes.c_void_p(0x4000000 * (i + 1)) for i in range(24)]  # 64 MiB apart
@@ -268,6 +274,22 @@ def test_scan_bwd_workspace_size(lib):
     assert lib.ssm_scan_bwd_workspace_size(2, 8, 64, 16) == want
     # 8-token segments, 64-channel tiles at N = 16
     assert lib.ssm_scan_bwd_workspace_size(1, 17, 65, 16) == (3 * 2 * 65 * 16 // 2 + 17 * 2 * 32 + 65 * 16 + 2 * 65) * 4
+    # the _ex form: the same without saved states, no state region with them
+    assert lib.ssm_scan_bwd_workspace_size_ex(2, 8, 64, 16, 0) == want
+    assert lib.ssm_scan_bwd_workspace_size_ex(2, 8, 64, 16, 1) == want - 2 * 1 * 64 * 16 * 4
+    assert lib.ssm_scan_bwd_workspace_size_ex(2, 8, 64, 16, 2) == 0
+    assert lib.ssm_scan_bwd_workspace_size_ex(2, 8, 64, 12, 1) == 0
+
+
+def test_scan_bwd_saved_states_take_the_smaller_workspace(lib):
+    # with the forward's states a workspace of the _ex(.., 1) size is enough,
+    # so the call passes validation (it would launch: stop at the size check
+    # by giving one byte less, which must be rejected)
+    need1 = lib.ssm_scan_bwd_workspace_size_ex(2, 8, 64, 16, 1)
+    assert bwd(lib, h_ckpt=Q[10], ws_len=need1 - 1) == WORKSPACE
+    need0 = lib.ssm_scan_bwd_workspace_size_ex(2, 8, 64, 16, 0)
+    assert bwd(lib, ws_len=need1) == WORKSPACE                 # recomputing needs the larger one
+    assert need0 > need1
 
 
 def test_scan_bwd_validation(lib):
