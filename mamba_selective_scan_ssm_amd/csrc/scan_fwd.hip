@@ -379,7 +379,9 @@ __device__ __forceinline__ float word_elem(const uint32_t *w, int e) {
 // CK: also write the state entering every 8-token segment to a.h_ckpt
 // (B, ceil(L/8), D, N) -- what a training step's backward recomputes
 // otherwise.  A block of this kernel is exactly one such segment.
-template <typename T, int LPC, int SPL, bool HAS_Z, bool CK>
+// STEP: delta takes the per-channel bias and/or softplus; without it delta is
+// used as loaded (rows past L load as 0, which is what they must stage).
+template <typename T, int LPC, int SPL, bool HAS_Z, bool CK, bool STEP>
 __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   constexpr int TB = 8;                 // tokens per block
   constexpr int kCPW = kWave / LPC;     // channels per wave
@@ -448,8 +450,8 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
     vo_st[m] = on ? vo[m] : 0x80000000u;
     Dd[m][0] = a.D_skip ? a.D_skip[dpc] : 0.f;
     Dd[m][1] = a.D_skip ? a.D_skip[dpc + 1] : 0.f;
-    Db[m][0] = a.delta_bias ? a.delta_bias[dpc] : 0.f;
-    Db[m][1] = a.delta_bias ? a.delta_bias[dpc + 1] : 0.f;
+    Db[m][0] = (STEP && a.delta_bias) ? a.delta_bias[dpc] : 0.f;
+    Db[m][1] = (STEP && a.delta_bias) ? a.delta_bias[dpc + 1] : 0.f;
   }
   const bool dsoft = a.delta_softplus;
   auto rsrc = [&](const void *p, int64_t bytes) {
@@ -530,12 +532,12 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
       const uint32_t tb = static_cast<uint32_t>(cyc * kCyc + u) * TB;
 #pragma unroll
       for (int m = 0; m < kPairs; ++m) {
-        const bool ok = tb + rr[m] < ntok;
         float du[4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const float xv = word_elem<T>(w.x[u][m], hh);
-          const float dv = ok ? step_size(word_elem<T>(w.d[u][m], hh), Db[m][hh], dsoft) : 0.f;
+          float dv = word_elem<T>(w.d[u][m], hh);
+          if constexpr (STEP) dv = (tb + rr[m] < ntok) ? step_size(dv, Db[m][hh], dsoft) : 0.f;
           du[2 * hh] = dv;
           du[2 * hh + 1] = dv * xv;
         }
@@ -819,21 +821,29 @@ hipError_t dispatch_split(const ScanArgs &a, int spl_req, int64_t seg_len, float
   return hipErrorNotSupported;
 }
 
+template <typename T, int LPC, int SPL, bool STEP>
+void launch_lanesplit_s(const ScanArgs &a, dim3 grid, hipStream_t s) {
+  if (a.h_ckpt) {
+    if (a.z)
+      scan_lanesplit_kernel<T, LPC, SPL, true, true, STEP><<<grid, kWave * 4, 0, s>>>(a);
+    else
+      scan_lanesplit_kernel<T, LPC, SPL, false, true, STEP><<<grid, kWave * 4, 0, s>>>(a);
+  } else {
+    if (a.z)
+      scan_lanesplit_kernel<T, LPC, SPL, true, false, STEP><<<grid, kWave * 4, 0, s>>>(a);
+    else
+      scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP><<<grid, kWave * 4, 0, s>>>(a);
+  }
+}
+
 template <typename T, int LPC, int SPL>
 hipError_t launch_lanesplit_t(const ScanArgs &a, hipStream_t s) {
   constexpr int kChPerWG = 4 * (kWave / LPC);
   dim3 grid(static_cast<unsigned>((a.D + kChPerWG - 1) / kChPerWG), 1, static_cast<unsigned>(a.B));
-  if (a.h_ckpt) {
-    if (a.z)
-      scan_lanesplit_kernel<T, LPC, SPL, true, true><<<grid, kWave * 4, 0, s>>>(a);
-    else
-      scan_lanesplit_kernel<T, LPC, SPL, false, true><<<grid, kWave * 4, 0, s>>>(a);
-  } else {
-    if (a.z)
-      scan_lanesplit_kernel<T, LPC, SPL, true, false><<<grid, kWave * 4, 0, s>>>(a);
-    else
-      scan_lanesplit_kernel<T, LPC, SPL, false, false><<<grid, kWave * 4, 0, s>>>(a);
-  }
+  if (a.delta_bias != nullptr || a.delta_softplus)
+    launch_lanesplit_s<T, LPC, SPL, true>(a, grid, s);
+  else
+    launch_lanesplit_s<T, LPC, SPL, false>(a, grid, s);
   return hipGetLastError();
 }
 

@@ -82,29 +82,15 @@ def test_mamba130m_split_sequence(oracle_mod, variant, chunk):
     assert_close(to_np(h), rh, "f32", "h_final")
 
 
-def _sample_channels(B, D, k, seed):
-    rng = np.random.default_rng(seed)
-    ch = set(rng.integers(0, B * D, size=k).tolist())
-    for b in (0, B - 1):                # the edges of channel tiles and of D
-        for d in (0, 63, 64, D - 1):
-            ch.add(b * D + d)
-    return np.array(sorted(ch), dtype=np.int64)
-
-
-def test_mamba2p8b_prefill_bf16_sampled(oracle_mod):
-    """Full-size 2.8B-shaped prefill in the bench's launch configuration,
-    checked on sampled channels (each channel's whole sequence and state)."""
+def test_mamba2p8b_prefill_bf16_whole(oracle_mod):
+    """Full-size 2.8B-shaped prefill in the bench's launch configuration:
+    every y (B, L, D) and every h_final (B, D, N) against the oracle."""
     inp = gen.make_workload("mamba2p8b_prefill_bf16")
-    _say("mamba2p8b_prefill_bf16 full size, sampled channels")
+    _say("mamba2p8b_prefill_bf16 full size, whole tensors")
     y, hf = run_gpu(inp)
-    B, L, D, N = inp.B, inp.L, inp.D, inp.N
-    ch = _sample_channels(B, D, 96, 5)
-    ry, rh = run_oracle(oracle_mod, inp, channels=ch)
-    b, d = ch // D, ch % D
-    assert_close(y[b, :, d], ry, "bf16", "y")
-    assert_close(hf[b, d], rh, "bf16", "h_final")
-    # and the same channels as fp32-relative statistics, for the record
-    assert np.isfinite(y).all()
+    ry, rh = run_oracle(oracle_mod, inp)
+    assert_close(y, ry, "bf16", "y")
+    assert_close(hf, rh, "bf16", "h_final")
 
 
 SHAPES = [

@@ -128,27 +128,24 @@ def test_batch_invariance(T):
 
 
 @pytest.mark.parametrize("T", [1, 4, 16])
-def test_pool_decode_256x5120_sampled(oracle_mod, T):
+def test_pool_decode_256x5120_whole(oracle_mod, T):
     """The timed pool-decode workload (256 sequences on scattered rows of a
-    512-row pool, D=5120, N=16, bf16) at T = 1, 4 and 16 tokens per call; y and
-    the written rows checked on sampled channels, untouched rows whole."""
+    512-row pool, D=5120, N=16, bf16) at T = 1, 4 and 16 tokens per call: all
+    of y and every written pool row against the oracle, untouched rows
+    bitwise unchanged."""
     w = gen.make_workload("pool_decode_256x5120_bf16")
     cut = lambda t: gen.Tensor(np.ascontiguousarray(t.f32[:, :T]),
                                None if t.bf16 is None else np.ascontiguousarray(t.bf16[:, :T]))
     inp = dataclasses.replace(w.tokens, L=T, **{k: cut(getattr(w.tokens, k))
                                                 for k in ("x", "delta", "Bm", "Cm", "z")})
-    S, D, P = inp.B, inp.D, w.pool.shape[0]
+    P = w.pool.shape[0]
     slots, pool_np = w.slots, w.pool
     _say("pool_decode_256x5120_bf16", T)
     y, pool = _run(inp, pool_np, slots.tolist())
-    rng = np.random.default_rng(743)
-    ch = np.unique(np.concatenate([rng.integers(0, S * D, 160), [0, D - 1, S * D - 1]]))
     ry, rh = oracle_mod.scan(inp.x.f32, inp.delta.f32, inp.A, inp.Bm.f32, inp.Cm.f32, inp.D_skip,
-                             inp.z.f32, pool_np[slots], channels=ch)
-    s, d = ch // D, ch % D
-    yn = to_np(y)
-    assert_close(yn[s, :, d], ry, "bf16", "y")
+                             inp.z.f32, pool_np[slots])
+    assert_close(to_np(y), ry, "bf16", "y")
     pn = pool.cpu().numpy()
-    assert_close(pn[slots[s], d], rh, "bf16", "pool rows")
+    assert_close(pn[slots], rh, "bf16", "pool rows")
     untouched = np.setdiff1d(np.arange(P), slots)
     assert np.array_equal(pn[untouched], pool_np[untouched])
