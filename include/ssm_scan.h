@@ -157,6 +157,33 @@ ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype
                            void *stream);
 
 /*
+ * ssm_scan_fwd_noalloc -- ssm_scan_fwd_ex for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and schedule choice as
+ * ssm_scan_fwd_ex, bitwise, without the workspace: where the chosen schedule
+ * needs one (the chunked schedule's segment summaries), it uses a device
+ * scratch array that the library holds on every GPU it runs on, for the life
+ * of the process.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the caller still passes inputs and outputs.
+ *   limit : schedules needing more than 16 MiB of workspace
+ *           (ssm_scan_fwd_workspace_size > 16777216) return
+ *           SSM_ERR_WORKSPACE with nothing enqueued.
+ *   races : every call on one GPU shares that GPU's scratch, which keeps the
+ *           last call's contents (each call writes the entries it reads, so
+ *           nothing needs clearing); calls that overlap in time on one GPU
+ *           (other streams, other threads) race and must be serialised by the
+ *           caller.
+ * Errors as ssm_scan_fwd_ex; SSM_ERR_HIP if the scratch address cannot be
+ * looked up on the current device.
+ */
+ssm_status ssm_scan_fwd_noalloc(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                                const void *x, const void *delta, const float *A,
+                                const void *Bm, const void *Cm, const float *D_skip,
+                                const void *z, const float *h0, void *y, float *h_final,
+                                const ssm_tuning *tuning, const ssm_delta_opts *dopts,
+                                void *stream);
+
+/*
  * ssm_scan_fwd_train -- ssm_scan_fwd_ex for a training step: also writes
  * h_ckpt (B, ceil(L/8), D, N) fp32, the state entering every 8-token segment
  * (segment 0: h0), which ssm_scan_bwd then reads instead of recomputing

@@ -72,6 +72,8 @@ def lib():
         L.ssm_ssd_fwd_workspace_size.restype = sz
         L.ssm_scan_fwd_ex.argtypes = [i64, i64, i64, i64, ctypes.c_int] + [vp] * 10 + [vp, sz, vp, vp, vp]
         L.ssm_scan_fwd_ex.restype = ctypes.c_int
+        L.ssm_scan_fwd_noalloc.argtypes = [i64, i64, i64, i64, ctypes.c_int] + [vp] * 10 + [vp, vp, vp]
+        L.ssm_scan_fwd_noalloc.restype = ctypes.c_int
         L.ssm_state_update_ex.argtypes = [i64, i64, i64, ctypes.c_int] + [vp] * 9 + [vp, vp]
         L.ssm_state_update_ex.restype = ctypes.c_int
         L.ssm_ssd_fwd_ex.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 10 + [vp, sz, vp, vp]
@@ -175,6 +177,30 @@ def scan_fwd(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, y=None, h_fin
     _call("ssm_scan_fwd_ex", B, L, D, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
           _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(workspace), ws_len,
           ctypes.byref(tun), _dopts(delta_bias, delta_softplus), _stream(dev))
+    return y, h_final
+
+
+def scan_fwd_noalloc(x, delta, A, Bm, Cm, D_skip=None, z=None, h0=None, *, y, h_final=None,
+                     variant=0, chunk_len=0, states_per_lane=0, delta_bias=None, delta_softplus=False):
+    """scan_fwd through ssm_scan_fwd_noalloc: the outputs are the caller's
+    (y required, h_final optional) and the library's device scratch stands in
+    for the workspace, so the call allocates nothing.  Returns (y, h_final)."""
+    if x.dim() != 3 or Bm.dim() != 3:
+        raise ValueError("x must be (B, L, D) and Bm (B, L, N)")
+    B, L, D = x.shape
+    N = Bm.shape[2]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    for name, t, shp, tdt in (("x", x, (B, L, D), dt), ("delta", delta, (B, L, D), dt),
+                              ("z", z, (B, L, D), dt), ("Bm", Bm, (B, L, N), dt), ("Cm", Cm, (B, L, N), dt),
+                              ("A", A, (D, N), torch.float32), ("D_skip", D_skip, (D,), torch.float32),
+                              ("h0", h0, (B, D, N), torch.float32), ("delta_bias", delta_bias, (D,), torch.float32),
+                              ("y", y, (B, L, D), dt), ("h_final", h_final, (B, D, N), torch.float32)):
+        _check(name, t, shp, tdt, dev)
+    tun = Tuning(variant, chunk_len, states_per_lane)
+    _call("ssm_scan_fwd_noalloc", B, L, D, N, code, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+          _ptr(D_skip), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final), ctypes.byref(tun),
+          _dopts(delta_bias, delta_softplus), _stream(dev))
     return y, h_final
 
 

@@ -175,11 +175,19 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
                          workspace_bytes, tuning, nullptr, stream);
 }
 
-ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt, const void *x,
-                           const void *delta, const float *A, const void *Bm, const void *Cm,
-                           const float *D_skip, const void *z, const float *h0, void *y,
-                           float *h_final, void *workspace, size_t workspace_bytes,
-                           const ssm_tuning *tuning, const ssm_delta_opts *dopts, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// ssm_scan_fwd_ex, and ssm_scan_fwd_noalloc (own_scratch: the chunked
+// schedule's segment summaries go to the library's device scratch instead of
+// a caller workspace).
+ssm_status scan_fwd_impl(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt, const void *x,
+                         const void *delta, const float *A, const void *Bm, const void *Cm,
+                         const float *D_skip, const void *z, const float *h0, void *y,
+                         float *h_final, void *workspace, size_t workspace_bytes,
+                         const ssm_tuning *tuning, const ssm_delta_opts *dopts, void *stream,
+                         bool own_scratch) {
   if (B < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_INVALID_ARG;
   if (!valid_dtype(dt) || !tuning_ok(tuning) || !dopts_ok(dopts)) return SSM_ERR_INVALID_ARG;
   if (N > SSM_SCAN_MAX_N) return SSM_ERR_UNSUPPORTED;
@@ -213,11 +221,18 @@ ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype
   if (p.variant == 2) {
     if ((L + p.seg_len - 1) / p.seg_len > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
     const size_t need = static_cast<size_t>(scan_ws_floats(B, L, D, N, tuning)) * sizeof(float);
-    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
-    const Range wsr{workspace, static_cast<int64_t>(need)};
-    if (overlaps_any(wsr, ins) || overlap(wsr, Range{y, nBLD * es}) ||
-        overlap(wsr, Range{h_final, nBDN * 4}))
-      return SSM_ERR_INVALID_ARG;
+    if (own_scratch) {
+      if (need > ssm::kScratchBytes) return SSM_ERR_WORKSPACE;
+      const hipError_t e = ssm::scratch_device_ptr(&workspace);
+      if (e != hipSuccess) return SSM_ERR_HIP;
+      workspace_bytes = ssm::kScratchBytes;
+    } else {
+      if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+      const Range wsr{workspace, static_cast<int64_t>(need)};
+      if (overlaps_any(wsr, ins) || overlap(wsr, Range{y, nBLD * es}) ||
+          overlap(wsr, Range{h_final, nBDN * 4}))
+        return SSM_ERR_INVALID_ARG;
+    }
     return hip_status(ssm::launch_scan_chunked(a, spl_of(tuning), p.seg_len,
                                                static_cast<float *>(workspace), s));
   }
@@ -230,6 +245,28 @@ ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype
   if (auto_variant && spl_of(tuning) == 0 && lanesplit_ok)
     return hip_status(ssm::launch_scan_lanesplit(a, s));
   return hip_status(ssm::launch_scan_sequential(a, spl_of(tuning), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt, const void *x,
+                           const void *delta, const float *A, const void *Bm, const void *Cm,
+                           const float *D_skip, const void *z, const float *h0, void *y,
+                           float *h_final, void *workspace, size_t workspace_bytes,
+                           const ssm_tuning *tuning, const ssm_delta_opts *dopts, void *stream) {
+  return scan_fwd_impl(B, L, D, N, dt, x, delta, A, Bm, Cm, D_skip, z, h0, y, h_final, workspace,
+                       workspace_bytes, tuning, dopts, stream, false);
+}
+
+ssm_status ssm_scan_fwd_noalloc(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                                const void *x, const void *delta, const float *A, const void *Bm,
+                                const void *Cm, const float *D_skip, const void *z, const float *h0,
+                                void *y, float *h_final, const ssm_tuning *tuning,
+                                const ssm_delta_opts *dopts, void *stream) {
+  return scan_fwd_impl(B, L, D, N, dt, x, delta, A, Bm, Cm, D_skip, z, h0, y, h_final, nullptr, 0,
+                       tuning, dopts, stream, true);
 }
 
 ssm_status ssm_scan_fwd_train(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt,

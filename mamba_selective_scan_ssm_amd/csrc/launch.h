@@ -60,6 +60,12 @@ int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64
 hipError_t launch_scan_chunked(const ScanArgs &a, int spl_req, int64_t seg_len, float *ws,
                                hipStream_t s);
 
+// Library-owned device scratch (scratch.hip): kScratchBytes per device, for
+// entry points whose callers cannot allocate.  Sets *ptr to this device's
+// copy (the current device), looking its address up on first use.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+hipError_t scratch_device_ptr(void **ptr);
+
 // Workspace-free scan, one lane per channel holding all N states.  h0 and
 // h_final may alias (each lane reads its row before writing it).
 hipError_t launch_scan_lane(const ScanArgs &a, hipStream_t s);

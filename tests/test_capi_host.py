@@ -329,3 +329,25 @@ def test_scan_fwd_train_validation(lib):
     assert tr(h_ckpt=Q[9]) == INVALID                         # on h_final
     assert tr(y=Q[0]) == INVALID
     assert tr(N=65) == UNSUPPORTED
+
+
+def test_scan_noalloc_limit_and_validation(lib):
+    """ssm_scan_fwd_noalloc: a schedule needing more than the 16 MiB device
+    scratch is refused with SSM_ERR_WORKSPACE, and bad arguments as in
+    ssm_scan_fwd_ex -- all on the host, before any device call."""
+    def na(B=2, L=8, D=64, N=16, dt=F32, tun=None, **over):
+        p = dict(x=Q[0], delta=Q[1], A=Q[2], Bm=Q[3], Cm=Q[4], D_skip=Q[5], z=Q[6], h0=Q[7], y=Q[8],
+                 h_final=Q[9])
+        p.update(over)
+        return lib.ssm_scan_fwd_noalloc(B, L, D, N, dt, p["x"], p["delta"], p["A"], p["Bm"], p["Cm"],
+                                        p["D_skip"], p["z"], p["h0"], p["y"], p["h_final"],
+                                        None if tun is None else ctypes.byref(tun), None, None)
+    t = ssm.Tuning(2, 64)
+    big = dict(B=4, L=4096, D=256, N=64)         # 33.5 MB of segment summaries
+    assert lib.ssm_scan_fwd_workspace_size(*big.values(), ctypes.byref(t)) > 16 << 20
+    assert na(**big, tun=t) == WORKSPACE
+    assert na(B=-1) == INVALID
+    assert na(y=None) == INVALID
+    assert na(y=Q[0]) == INVALID                     # y on x
+    assert na(N=65) == UNSUPPORTED
+    assert na(tun=ssm.Tuning(4, 0)) == INVALID

@@ -1,0 +1,63 @@
+"""ssm_scan_fwd_noalloc (the entry point for callers that cannot allocate)
+against ssm_scan_fwd_ex on the same inputs: bitwise, on two calls in a row,
+the second smaller, both on the chunked schedule whose segment summaries now
+live in the library's device scratch; plus a schedule that needs no
+workspace, and the oracle at the parity bar."""
+
+import numpy as np
+import pytest
+import torch
+
+import ssm_inputs as gen
+from tests.helpers import assert_close, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _pair(inp, gate=True, bias=None, softplus=False):
+    import mamba_selective_scan_ssm_amd as ssm
+    args = [to_dev(getattr(inp, k)) for k in ("x", "delta", "A", "Bm", "Cm", "D_skip")]
+    args += [to_dev(inp.z) if gate else None, to_dev(inp.h0)]
+    kw = dict(delta_bias=None if bias is None else to_dev(bias), delta_softplus=softplus)
+    y_ref, h_ref = ssm.scan_fwd(*args, **kw)
+    y = torch.full_like(y_ref, float("nan"))
+    h = torch.full_like(h_ref, float("nan"))
+    ssm.scan_fwd_noalloc(*args, y=y, h_final=h, **kw)
+    torch.cuda.synchronize()
+    return y, h, y_ref, h_ref
+
+
+def test_noalloc_two_calls_second_smaller(oracle_mod):
+    import mamba_selective_scan_ssm_amd as ssm
+    first = gen.make_workload("mamba130m_fp32")                      # B=1 L=2048 D=1536 N=16
+    second = gen.make_scan(2, 600, 256, 16, dtype="bf16", seed=905)
+    for inp in (first, second):
+        assert ssm.scan_fwd_workspace_size(inp.B, inp.L, inp.D, inp.N) > 0   # chunked schedule
+    _say("noalloc first", first.B, first.L, first.D, first.N)
+    y, h, y_ref, h_ref = _pair(first)
+    assert torch.equal(y, y_ref) and torch.equal(h, h_ref)
+    ry, rh = oracle_mod.scan(first.x.f32, first.delta.f32, first.A, first.Bm.f32, first.Cm.f32,
+                             first.D_skip, first.z.f32, first.h0)
+    assert_close(to_np(y), ry, "f32", "y")
+    assert_close(to_np(h), rh, "f32", "h_final")
+    _say("noalloc second (smaller)", second.B, second.L, second.D, second.N)
+    bias = np.random.default_rng(906).normal(0.0, 0.5, second.D).astype(np.float32)
+    y, h, y_ref, h_ref = _pair(second, bias=bias, softplus=True)
+    assert torch.equal(y, y_ref) and torch.equal(h, h_ref)
+    ry, rh = oracle_mod.scan(second.x.f32, second.delta.f32, second.A, second.Bm.f32, second.Cm.f32,
+                             second.D_skip, second.z.f32, second.h0, delta_bias=bias, delta_softplus=True)
+    assert_close(to_np(y), ry, "bf16", "y")
+    assert_close(to_np(h), rh, "bf16", "h_final")
+
+
+def test_noalloc_without_workspace_schedule():
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(2, 70, 128, 16, dtype="bf16", seed=907)
+    assert ssm.scan_fwd_workspace_size(inp.B, inp.L, inp.D, inp.N) == 0
+    _say("noalloc lane-split", inp.B, inp.L, inp.D, inp.N)
+    y, h, y_ref, h_ref = _pair(inp, gate=False)
+    assert torch.equal(y, y_ref) and torch.equal(h, h_ref)
