@@ -7,23 +7,28 @@ h0, silu(z) gate on) with all inputs resident in HBM.  The headline value is
 selective-scan elements per second, B*L*D*N / step time, in Gelem/s.
 
 The JSON line also carries
-* roofline: the scan kernel against the ceiling that binds it (measured live
-  with HIP events on the launch stream), plus its algorithmic HBM bandwidth
-  against the 8 TB/s peak;
+* roofline: the scan kernel against the HBM roofline (algorithmic bytes per
+  launch / kernel time, measured live with HIP events on the launch stream,
+  against 8 TB/s), with the measured HBM traffic from rocprofv3 counters and,
+  under "alu", the issue-rate ceiling of the method's instruction mix and
+  the kernel's own mix from its VALU counters;
 * cpu_baseline: the fp64 CPU oracle (untuned, threads over channels) timed
-  on a bounded sample of the same workload, and on one core;
+  on the same workload, and on one core;
 * copy_GBs: a plain elementwise kernel reading and writing 1 GiB each, the
   practical ceiling the HBM-bound rates are also given against (copy_frac);
-* rows: the other hot-path entry points measured the same way -- the decode
-  step (S=256, D=5120, N=16, 128 steps), the Mamba-2 SSD chunked scan
-  (B=2, L=8192, H=80, P=64, N=128, G=8, chunk 256) and the width-4 causal
-  convolution ahead of the scan (B=8, L=4096, D=5120) with its decode step.
-  Launches of tens of microseconds (the decode steps, pool decode, the
-  convolution's decode step) are timed as HIP-graph replays of 32-64 calls,
-  since the host's per-call cost exceeds theirs; the eager per-call event
-  time and the host-driven wall time are given beside them.
+* rows: the other configurations and hot-path entry points measured the same
+  way -- the tiny scan (B=1, L=64, D=16, N=4, fp32) and the Mamba-130M-shaped
+  scan (B=1, L=2048, D=1536, N=16, fp32) under every schedule, the decode step
+  (S=256, D=5120, N=16, 128 steps), the Mamba-2 SSD chunked scan (B=2,
+  L=8192, H=80, P=64, N=128, G=8, chunk 256), the width-4 causal convolution
+  ahead of the scan (B=8, L=4096, D=5120) with its decode step, pool decode
+  and the backward.  Launches of tens of microseconds are timed as HIP-graph
+  replays, since the host's per-call cost exceeds theirs; the eager per-call
+  event time and the host-driven wall time are given beside them.  The rows
+  run before the headline steps, which therefore start on a warm device.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --summarize DIR   (rocprofv3 output -> profiles/)
 """
 
 from __future__ import annotations
@@ -41,20 +46,35 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# fp32 VALU lane rate from 157.3 TFLOP/s (FMA = 2 flops) and the
-# transcendental unit at a quarter of it (8 lanes/clk/SIMD * 1024 SIMDs * 2.4 GHz)
-VALU_LANE_OPS = 157.3e12 / 2
-TRANS_LANE_OPS = VALU_LANE_OPS / 4
+BF16_MFMA_PEAK = 2.5e15
+# gfx950 issue model: 256 CUs x 4 SIMDs, each SIMD issuing one wave64 fp32
+# VALU op per quad cycle (16 lanes x 4 cycles) at 2.4 GHz.  The VALU counters
+# of the kernels here charge v_exp_f32 two quad cycles (SQ_ACTIVE_INST_VALU
+# minus SQ_INSTS_VALU equals SQ_INSTS_VALU_TRANS_F32) and let two plain VALU
+# ops of different waves share one quad cycle (SQ_ACTIVE_INST_VALU2); a
+# transcendental never shares one.
+SIMDS, CLOCK_HZ = 1024, 2.4e9
 # per scan element: dA = exp2(delta*A2) -> 1 mul + 1 exp; u*B -> 1 mul;
-# h = dA*h + u*B -> 1 fma; y += C*h -> 1 fma.  6 flops + 1 transcendental.
-SCAN_VALU_PER_ELEM, SCAN_TRANS_PER_ELEM, SCAN_FLOPS_PER_ELEM = 4, 1, 6
-SCAN_ELEM_PEAK = 1.0 / (SCAN_VALU_PER_ELEM / VALU_LANE_OPS + SCAN_TRANS_PER_ELEM / TRANS_LANE_OPS)
+# h = dA*h + u*B -> 1 fma; y += C*h -> 1 fma.  4 VALU + 1 transcendental.
+SCAN_VALU_PER_ELEM, SCAN_TRANS_PER_ELEM = 4, 1
+
+
+def issue_ceiling(valu, trans, paired):
+    """Elements per second if every SIMD issued only this mix, back to back:
+    plain ops one quad cycle each (half when every one pairs), transcendentals
+    two."""
+    quads = valu / (2.0 if paired else 1.0) + 2.0 * trans
+    return SIMDS * CLOCK_HZ * 64 / (4.0 * quads)
+
+
+SCAN_ELEM_FLOOR = issue_ceiling(SCAN_VALU_PER_ELEM, SCAN_TRANS_PER_ELEM, False)   # 6.55 Telem/s
+SCAN_ELEM_PAIRED = issue_ceiling(SCAN_VALU_PER_ELEM, SCAN_TRANS_PER_ELEM, True)   # 9.83 Telem/s
 # backward, per element at least: the forward recurrence again (3 VALU) and
 # one exp(delta A); the adjoint g*C + lam (1), lam*u for dB (1), g*h for dC
 # (1), C*h for q (1), p = a*h_prev (1), ddelta += lam (A p + B x) (3),
 # dA += (lam delta) p (2), dx += lam B (1), lam *= a (1): 15 VALU + 1 exp
 BWD_VALU_PER_ELEM, BWD_TRANS_PER_ELEM = 15, 1
-BWD_ELEM_PEAK = 1.0 / (BWD_VALU_PER_ELEM / VALU_LANE_OPS + BWD_TRANS_PER_ELEM / TRANS_LANE_OPS)
+BWD_ELEM_PEAK = issue_ceiling(BWD_VALU_PER_ELEM, BWD_TRANS_PER_ELEM, False)
 
 
 # the kernel sources behind each measured entry point: counters taken on
@@ -70,6 +90,7 @@ KERNEL_SOURCES = {
     "decode_steps_T4": ["state_update.hip"] + _COMMON,
     "decode_steps_T16": ["state_update.hip"] + _COMMON,
     "scan_bwd": ["scan_bwd.hip", "bwd.h"] + _COMMON,
+    "scan_fwd_130m": ["scan_fwd.hip"] + _COMMON,
 }
 
 
@@ -83,20 +104,29 @@ def csrc_hash(entry: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(entry: str, field: str = "bytes_per_launch"):
-    """HBM bytes per launch (or per call) from the committed rocprofv3 --pmc
-    runs, if they were taken on the current kernel sources; else None."""
+def load_entry(entry: str):
+    """The committed rocprofv3 figures of an entry point (profiles/traffic.json),
+    if they were taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         with open(p) as f:
-            t = json.load(f)
-        e = t.get(entry)
-        if not e or e.get("csrc_hash") != csrc_hash(entry):
-            return None
-        return float(e[field])
-    except (OSError, ValueError, KeyError):
+            e = json.load(f).get(entry)
+    except (OSError, ValueError):
+        return None
+    if not e or e.get("csrc_hash") != csrc_hash(entry):
+        return None
+    return e
+
+
+def load_traffic(entry: str, field: str = "bytes_per_launch"):
+    """HBM bytes per launch (or per call) from the committed rocprofv3 --pmc
+    runs, if they were taken on the current kernel sources; else None."""
+    e = load_entry(entry)
+    try:
+        return None if e is None else float(e[field])
+    except (KeyError, TypeError, ValueError):
         return None
 
 
@@ -172,8 +202,14 @@ def upload(t, torch):
 
 
 def cpu_baseline(inp, n_seq: int):
+    """The fp64 oracle as it stands, on the first n_seq sequences of the
+    workload (all channels, whole L), threads over channels: as many threads as
+    the CPUs this process may run on, at most 16 -- the host share that goes
+    with one GPU on the machines this runs on (the count used is reported).
+    Then the same oracle on one core over 512 channels."""
     import oracle
-    threads = min(16, oracle.default_threads())
+    affinity = oracle.default_threads()
+    threads = min(16, affinity)
     D = inp.D
     ch = np.arange(n_seq * D, dtype=np.int64)          # every channel of the first n_seq sequences
     t0 = time.perf_counter()
@@ -189,7 +225,8 @@ def cpu_baseline(inp, n_seq: int):
     dt1 = time.perf_counter() - t1
     return {"value": elems / dt / 1e9, "unit": "Gelem/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_seq} of {inp.B} sequences (all {D} channels, L={inp.L}, N={inp.N}), "
-                      f"fp64 sequential recurrence, {dt:.2f} s wall",
+                      f"fp64 sequential recurrence, {dt:.2f} s wall, {dt * threads:.1f} thread-s",
+            "host_cpus": os.cpu_count(), "affinity_cpus": affinity,
             "one_core": {"value": len(ch1) * inp.L * inp.N / dt1 / 1e9, "unit": "Gelem/s",
                          "sample": f"512 channels of sequence 0, L={inp.L}, N={inp.N}, {dt1:.2f} s"}}
 
@@ -203,6 +240,63 @@ def copy_bandwidth(torch, nbytes=1 << 30):
     mean_ms, _, _ = time_calls(lambda: torch.mul(a, 1.5, out=b), 20, 5, torch)
     del a, b
     return 2 * nbytes / (mean_ms * 1e-3) / 1e9
+
+
+def scan_inputs(inp, torch):
+    t = {k: upload(getattr(inp, k), torch) for k in ("x", "delta", "z", "Bm", "Cm")}
+    return t, upload(inp.A, torch), upload(inp.D_skip, torch), upload(inp.h0, torch)
+
+
+def bench_tiny(torch, ssm, gen):
+    """The tiny fp32 scan (B=1, L=64, D=16, N=4, gate on): one launch, bound
+    by launch latency rather than by any unit of the chip."""
+    inp = gen.make_workload("tiny_fp32")
+    B, L, D, N = inp.B, inp.L, inp.D, inp.N
+    t, A, Ds, h0 = scan_inputs(inp, torch)
+    y = torch.empty((B, L, D), dtype=torch.float32, device="cuda")
+    hf = torch.empty((B, D, N), dtype=torch.float32, device="cuda")
+
+    def one():
+        ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, y=y, h_final=hf)
+
+    ev_ms, _, wall = time_calls(one, 64, 8, torch)
+    ms, _ = time_graph(one, 64, 8, torch)
+    alg = scan_alg_bytes(B, L, D, N, 4)
+    return {"workload": "tiny_fp32 (B=1, L=64, D=16, N=4, fp32, gate on, random h0)",
+            "kernel_us_per_call": ms * 1e3, "eager_event_us_per_call": ev_ms * 1e3,
+            "wall_us_per_call": wall * 1e3, "alg_bytes": alg, "bound": "launch"}
+
+
+def bench_130m(torch, ssm, gen, steps=50):
+    """The Mamba-130M-shaped fp32 scan (B=1, L=2048, D=1536, N=16, gate on,
+    random h0) under the automatic schedule and each schedule forced: at 24
+    channel tiles per sequence the choice between the channel-sequential
+    kernels and the chunked one is what this row measures."""
+    inp = gen.make_workload("mamba130m_fp32")
+    B, L, D, N = inp.B, inp.L, inp.D, inp.N
+    t, A, Ds, h0 = scan_inputs(inp, torch)
+    y = torch.empty((B, L, D), dtype=torch.float32, device="cuda")
+    hf = torch.empty((B, D, N), dtype=torch.float32, device="cuda")
+    alg = scan_alg_bytes(B, L, D, N, 4)
+    out = {"workload": "mamba130m_fp32 (B=1, L=2048, D=1536, N=16, fp32, gate on, random h0)",
+           "alg_bytes": alg, "traffic_bytes": load_traffic("scan_fwd_130m", "bytes_per_call")}
+    names = {0: "auto", 1: "workgroup", 2: "chunked", 3: "lanesplit"}
+    for v in (0, 1, 2, 3):
+        ws_n = ssm.scan_fwd_workspace_size(B, L, D, N, variant=v)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+        def one():
+            ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, y=y, h_final=hf,
+                         variant=v, workspace=ws)
+
+        ms, min_ms, _ = time_calls(one, steps, 10, torch)
+        gr_ms, _ = time_graph(one, 32, 8, torch)
+        out[names[v]] = {"kernel_ms": gr_ms, "eager_event_ms": ms, "eager_event_ms_min": min_ms,
+                         "Gelem_per_s": B * L * D * N / (gr_ms * 1e-3) / 1e9,
+                         "hbm_GBs": alg / (gr_ms * 1e-3) / 1e9,
+                         "hbm_frac": alg / (gr_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "workspace_bytes": ws_n}
+    return out
 
 
 def bench_decode(torch, ssm, gen, steps_meas=128):
@@ -268,13 +362,19 @@ def bench_ssd(torch, ssm, gen, steps=10):
     B, L, H, P, G, N = w.B, w.L, w.H, w.P, w.G, w.N
     alg = (B * L * H * P * 2 * 2 + B * L * H * 2 + 2 * B * L * G * N * 2 + H * 8
            + 2 * B * H * P * N * 4)
-    flops = 2.0 * B * L * (w.chunk * G * N + w.chunk * H * P + 2 * H * P * N)  # dense chunked GEMMs
+    Q = w.chunk
+    # the method's matrix work: C.B^T and (scores).X inside each chunk on
+    # their causal (lower) halves, the chunk states and the carried-in term
+    flops = 2.0 * B * L * (Q * G * N / 2 + Q * H * P / 2 + 2 * H * P * N)
+    e = load_entry("ssd_fwd") or {}
     return {"workload": "ssd_mamba2_bf16 (B=2, L=8192, H=80, P=64, N=128, G=8, chunk=256)",
             "ms": mean_ms, "Gelem_per_s": B * L * H * P * N / (mean_ms * 1e-3) / 1e9,
             "alg_bytes": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
             "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "dense_gemm_TFLOPs": flops / (mean_ms * 1e-3) / 1e12,
-            "mfma_frac_bf16": flops / (mean_ms * 1e-3) / 2.5e15, "workspace_bytes": ws_n,
+            "causal_matrix_GFLOP": flops / 1e9,
+            "matrix_TFLOPs": flops / (mean_ms * 1e-3) / 1e12,
+            "mfma_frac_bf16": flops / (mean_ms * 1e-3) / BF16_MFMA_PEAK,
+            "mfma_busy_counter": e.get("mfma_busy"), "workspace_bytes": ws_n,
             "traffic_bytes": load_traffic("ssd_fwd", "bytes_per_call")}
 
 
@@ -396,20 +496,286 @@ def bench_pool_decode(torch, ssm, gen, steps=128):
     return out
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> profiles/*.md and profiles/traffic.json
+# ---------------------------------------------------------------------------
+# Each entry was profiled from the repository root on the GPU machine (after
+# `cd /tmp && export TMPDIR=/tmp`) into <DIR>/<entry>/<pass>/ with
+#   kt: rocprofv3 --kernel-trace --stats --output-format csv -d <DIR>/<entry>/kt -o kt -- python3 bench.py --only <only> <timed args>
+#   f:  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/<entry>/f -o f -- python3 bench.py --only <only> <short args> --copy-calib
+#   w:  the same with --pmc WRITE_SIZE
+#   v:  --pmc VALU_COUNTERS (entries with "valu")
+#   m:  --pmc MFMA_COUNTERS (entries with "mfma")
+VALU_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VALU2",
+                 "SQ_INSTS_LDS", "SQ_WAVES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"]
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU",
+                 "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
+PROFILE_ENTRIES = {
+    # entry: (--only, timed args, short args, summary file, title, kernels of one call, elements
+    #         per call (for the per-element counter figures) or None, extra passes)
+    "scan_fwd": ("scan", "--steps 100 --warmup 30 --no-cpu", "--steps 2 --warmup 1 --no-cpu",
+                 "scan_lanesplit_mamba2p8b_prefill_bf16.md",
+                 "Mamba-1 prefill selective scan, B=8 L=4096 D=5120 N=16, bf16 inputs, fp32 state (ssm_scan_fwd)",
+                 ["scan_lanesplit_kernel"], 8 * 4096 * 5120 * 16, ["v"]),
+    "scan_fwd_130m": ("m130", "--steps 50", "--steps 2", "scan_mamba130m_fp32.md",
+                      "Mamba-1 scan, B=1 L=2048 D=1536 N=16, fp32, every schedule (ssm_scan_fwd)",
+                      ["scan_split_kernel", "scan_carry_kernel", "scan_lanesplit_kernel"], 2048 * 1536 * 16, []),
+    "state_update": ("decode", "", "", "state_update_decode_256x5120_bf16.md",
+                     "decode step, S=256 D=5120 N=16, bf16 inputs, fp32 state (ssm_state_update)",
+                     ["state_step"], None, []),
+    "ssd_fwd": ("ssd", "--steps 20", "--steps 2", "ssd_chunked_mamba2_bf16.md",
+                "Mamba-2 SSD chunked scan, B=2 L=8192 H=80 P=64 N=128 G=8 chunk 256, bf16 (ssm_ssd_fwd)",
+                ["ssd_"], None, ["m"]),
+    "conv1d_fwd": ("conv", "--steps 50", "--steps 2", "conv1d_mamba2p8b_bf16.md",
+                   "causal convolution K=4, B=8 L=4096 D=5120 bf16, and its decode step S=256 (ssm_conv1d_*)",
+                   ["conv1d_fwd"], None, []),
+    "decode_steps": ("pool", "--steps 64", "--steps 2", "decode_steps_pool_256x5120_bf16.md",
+                     "pool decode, 256 of 512 rows, D=5120 N=16, T = 1, 4, 16 (ssm_decode_steps)",
+                     ["state_"], None, []),
+    "scan_bwd": ("bwd", "--steps 10", "--steps 1", "scan_bwd_mamba2p8b_prefill_bf16.md",
+                 "selective-scan backward, B=8 L=4096 D=5120 N=16, bf16, all gradients (ssm_scan_bwd)",
+                 ["scan_bwd_kernel", "bwd_reduce"], 8 * 4096 * 5120 * 16, ["v"]),
+}
+
+
+# kernels of one call under the automatic schedule, where a profiled run
+# also times other schedules (short names, prefix match); default: all
+CALL_KERNELS = {
+    "scan_fwd_130m": ["scan_split_kernel<float, 4, 4, 8, 1,", "scan_carry_kernel",
+                      "scan_split_kernel<float, 4, 4, 8, 2,"],
+}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    if not os.path.isdir(dirpath):
+        return None
+    for root, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    return None
+
+
+def _counters(path):
+    """{dispatch id: (kernel name, {counter: value})} from a counter_collection.csv."""
+    out = {}
+    for r in _csv_rows(path):
+        d = int(r["Dispatch_Id"])
+        name = r["Kernel_Name"]
+        out.setdefault(d, (name, {}))[1][r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
+def _calibration(disp, counter):
+    """KiB the copy calibration kernel (torch's elementwise multiply: 1 GiB
+    read and 1 GiB written) reported."""
+    for name, c in disp.values():
+        if "MulFunctor" in name and counter in c:
+            return c[counter]
+    return None
+
+
+def _short(name, n=110):
+    """Kernel name without 'void', namespaces and the parameter list."""
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("ssm::", "")
+    if name.endswith(")") and "(" in name:
+        name = name[:name.rindex("(")]
+    return name if len(name) <= n else name[:n] + "..."
+
+
+def summarize_profiles(src):
+    prof_dir = os.path.join(ROOT, "profiles")
+    tj_path = os.path.join(prof_dir, "traffic.json")
+    traffic = json.load(open(tj_path)) if os.path.exists(tj_path) else {}
+    traffic["note"] = ("csrc_hash: sha256 over the entry's kernel sources (bench.KERNEL_SOURCES); "
+                       "bytes: FETCH_SIZE and WRITE_SIZE scaled by the copy calibration")
+    for entry, (only, targs, sargs, fname, title, kpat, elems, extra) in PROFILE_ENTRIES.items():
+        base = os.path.join(src, entry)
+        kt = _find(os.path.join(base, "kt"), "kernel_stats.csv")
+        if kt is None:
+            continue
+        stats = [r for r in _csv_rows(kt)]
+        trace_p = _find(os.path.join(base, "kt"), "kernel_trace.csv")
+        mins = {}
+        if trace_p:
+            for r in _csv_rows(trace_p):
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                k = r["Kernel_Name"]
+                mins[k] = min(mins.get(k, 1e30), dur)
+        fetch = _counters(_find(os.path.join(base, "f"), "counter_collection.csv") or "/dev/null") \
+            if _find(os.path.join(base, "f"), "counter_collection.csv") else {}
+        write = _counters(_find(os.path.join(base, "w"), "counter_collection.csv")) \
+            if _find(os.path.join(base, "w"), "counter_collection.csv") else {}
+        fcal, wcal = _calibration(fetch, "FETCH_SIZE"), _calibration(write, "WRITE_SIZE")
+        fs = (1 << 20) / fcal if fcal else None   # bytes per KiB of counter
+        ws_ = (1 << 20) / wcal if wcal else None
+        fs = fs * 1024 if fs else None
+        ws_ = ws_ * 1024 if ws_ else None
+
+        def per_kernel(disp, counter):
+            acc = {}
+            for name, c in disp.values():
+                if counter in c and any(p in name for p in kpat):
+                    acc.setdefault(name, []).append(c[counter])
+            return {k: sum(v) / len(v) for k, v in acc.items()}
+
+        f_k, w_k = per_kernel(fetch, "FETCH_SIZE"), per_kernel(write, "WRITE_SIZE")
+        hashes = {e: csrc_hash(e) for e in ([entry] if entry in KERNEL_SOURCES else [])}
+        lines = [f"# rocprofv3: {title}", ""]
+        lines.append("MI355X (gfx950).  Kernel source hash (sha256, first 16 hex digits, over "
+                     + ", ".join(KERNEL_SOURCES.get(entry, [])) + " in mamba_selective_scan_ssm_amd/csrc, "
+                     "as bench.py computes it): " + ", ".join(f"`{h}`" for h in hashes.values())
+                     + ".  Commands, from the repository root on the GPU machine after "
+                     "`cd /tmp && export TMPDIR=/tmp`:")
+        lines.append("")
+        lines.append(f"* kernel trace: `rocprofv3 --kernel-trace --stats --output-format csv -d <out>/kt -o kt "
+                     f"-- python3 bench.py --only {only} {targs}`".replace("  ", " "))
+        lines.append(f"* HBM reads: `rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/f -o f "
+                     f"-- python3 bench.py --only {only} {sargs} --copy-calib`".replace("  ", " "))
+        lines.append(f"* HBM writes: the same with `--pmc WRITE_SIZE`")
+        if "v" in extra:
+            lines.append(f"* VALU counters: `rocprofv3 --pmc {' '.join(VALU_COUNTERS)} --output-format csv "
+                         f"-d <out>/v -o v -- python3 bench.py --only {only} {sargs}`".replace("  ", " "))
+        if "m" in extra:
+            lines.append(f"* matrix-core counters: `rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv "
+                         f"-d <out>/m -o m -- python3 bench.py --only {only} {sargs}`".replace("  ", " "))
+        lines.append("")
+        if fcal and wcal:
+            lines.append(f"Counter calibration: `--copy-calib` runs one elementwise copy that reads 1 GiB and "
+                         f"writes 1 GiB; it read FETCH_SIZE {fcal:.0f} KiB and WRITE_SIZE {wcal:.0f} KiB, so "
+                         f"FETCH_SIZE is scaled by {1048576 / fcal:.3f} and WRITE_SIZE by {1048576 / wcal:.3f} "
+                         "to give bytes.")
+            lines.append("")
+        lines.append("| kernel | calls | avg us | min us | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch "
+                     "| HBM bytes/dispatch (scaled) |")
+        lines.append("|---|---|---|---|---|---|---|")
+        call_bytes, call_us = 0.0, 0.0
+        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+            name = r["Name"]
+            if not any(p in name for p in kpat):
+                continue
+            calls = int(r["Calls"])
+            avg = float(r["AverageNs"]) / 1e3
+            fk, wk = f_k.get(name), w_k.get(name)
+            hb = (fk * fs + wk * ws_) if (fk is not None and wk is not None and fs and ws_) else None
+            lines.append(f"| `{_short(name)}` | {calls} | {avg:.1f} | {mins.get(name, float('nan')):.1f} | "
+                         f"{'' if fk is None else f'{fk:.0f}'} | {'' if wk is None else f'{wk:.0f}'} | "
+                         f"{'' if hb is None else f'{hb / 1e6:.2f} MB'} |")
+        lines.append("")
+        rec = traffic.get(entry, {}) if isinstance(traffic.get(entry), dict) else {}
+        rec = {"csrc_hash": csrc_hash(entry)} if entry in KERNEL_SOURCES else {}
+        if "v" in extra:
+            vc = _find(os.path.join(base, "v"), "counter_collection.csv")
+            if vc:
+                disp = _counters(vc)
+                lines.append("VALU counters (summed over the dispatches of one call of the timed kernel; "
+                             "per wave64 element slot = per 64 elements):")
+                lines.append("")
+                lines.append("| kernel | VALU insts | of which v_exp etc. (TRANS_F32) | VALU quad cycles "
+                             "(ACTIVE_INST_VALU) | dual-issue quad cycles (ACTIVE_INST_VALU2) | LDS insts | waves "
+                             "| VALU busy (quad cycles x 4 / (1024 SIMDs x GUI cycles / 8 XCDs)) |")
+                lines.append("|---|---|---|---|---|---|---|---|")
+                last = {}
+                for d, (name, c) in sorted(disp.items()):
+                    if any(p in name for p in kpat) and "SQ_INSTS_VALU" in c:
+                        last[name] = c
+                for name, c in last.items():
+                    gui = c.get("GRBM_GUI_ACTIVE", 0) / 8
+                    busy = c["SQ_ACTIVE_INST_VALU"] * 4 / (1024 * gui) if gui else float("nan")
+                    ew = elems / 64 if elems else None
+                    lines.append(f"| `{_short(name, 70)}` | {c['SQ_INSTS_VALU']:.4g}"
+                                 + (f" ({c['SQ_INSTS_VALU'] / ew:.2f}/elem-wave)" if ew else "")
+                                 + f" | {c['SQ_INSTS_VALU_TRANS_F32']:.4g}"
+                                 + (f" ({c['SQ_INSTS_VALU_TRANS_F32'] / ew:.3f})" if ew else "")
+                                 + f" | {c['SQ_ACTIVE_INST_VALU']:.4g} | {c['SQ_ACTIVE_INST_VALU2']:.4g}"
+                                 + f" ({2 * c['SQ_ACTIVE_INST_VALU2'] / c['SQ_INSTS_VALU']:.2f} of VALU insts paired)"
+                                 + f" | {c['SQ_INSTS_LDS']:.4g} | {c['SQ_WAVES']:.0f} | {busy:.2f} |")
+                    if ew and entry == "scan_fwd":
+                        rec["valu"] = {"valu_per_elem_wave": c["SQ_INSTS_VALU"] / ew,
+                                       "trans_per_elem_wave": c["SQ_INSTS_VALU_TRANS_F32"] / ew,
+                                       "paired_quads_per_elem_wave": c["SQ_ACTIVE_INST_VALU2"] / ew,
+                                       "valu_busy": busy}
+                lines.append("")
+        if "m" in extra:
+            mc = _find(os.path.join(base, "m"), "counter_collection.csv")
+            if mc:
+                disp = _counters(mc)
+                last = {}
+                for d, (name, c) in sorted(disp.items()):
+                    if any(p in name for p in kpat) and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                        last[name] = c
+                lines.append("Matrix-core counters (last dispatch of each kernel):")
+                lines.append("")
+                lines.append("| kernel | MFMA busy cycles | MFMA busy (/ (1024 SIMDs x GUI cycles / 8)) "
+                             "| bf16 MFMA MOPs (x512 flops) | VALU insts | LDS insts | waves |")
+                lines.append("|---|---|---|---|---|---|---|")
+                tot_busy, tot_gui = 0.0, 0.0
+                for name, c in last.items():
+                    gui = c.get("GRBM_GUI_ACTIVE", 0) / 8
+                    mb = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * gui) if gui else float("nan")
+                    tot_busy += c["SQ_VALU_MFMA_BUSY_CYCLES"]
+                    tot_gui += gui
+                    lines.append(f"| `{_short(name, 70)}` | {c['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | {mb:.3f} | "
+                                 f"{c['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4g} ({c['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.1f} GFLOP) | "
+                                 f"{c['SQ_INSTS_VALU']:.4g} | {c['SQ_INSTS_LDS']:.4g} | {c['SQ_WAVES']:.0f} |")
+                if tot_gui:
+                    rec["mfma_busy"] = tot_busy / (1024 * tot_gui)
+                    lines.append("")
+                    lines.append(f"Over the call's kernels: matrix cores busy {100 * rec['mfma_busy']:.1f}% "
+                                 "of SIMD-cycles.")
+                lines.append("")
+        # HBM bytes per call: each of the call's kernels once
+        per_call = 0.0
+        ok = True
+        for name in set(f_k) | set(w_k):
+            if entry in CALL_KERNELS and not any(_short(name).startswith(k) for k in CALL_KERNELS[entry]):
+                continue
+            if name in f_k and name in w_k and fs and ws_:
+                per_call += f_k[name] * fs + w_k[name] * ws_
+            else:
+                ok = False
+        if ok and (f_k or w_k) and entry in KERNEL_SOURCES:
+            rec["bytes_per_call"] = per_call
+            rec["bytes_per_launch"] = per_call
+            which = (" under the automatic schedule (" + ", ".join(CALL_KERNELS[entry]) + ")"
+                     if entry in CALL_KERNELS else "")
+            lines.append(f"HBM traffic of one call{which} (each of its kernels once): {per_call / 1e6:.2f} MB.")
+            lines.append("")
+        if rec:
+            traffic[entry] = rec
+        with open(os.path.join(prof_dir, fname), "w") as f:
+            f.write("\n".join(lines))
+        print("wrote", fname)
+    with open(tj_path, "w") as f:
+        json.dump(traffic, f, indent=1)
+    print("wrote traffic.json")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--no-rows", action="store_true", help="skip the decode and SSD rows")
+    ap.add_argument("--no-rows", action="store_true", help="skip the other configurations and entry points")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=8)
-    ap.add_argument("--only", choices=["scan", "decode", "ssd", "conv", "pool", "bwd"], default=None,
-                    help="time one hot-path entry point only (for profiling); prints its row")
+    ap.add_argument("--only", choices=["scan", "tiny", "m130", "decode", "ssd", "conv", "pool", "bwd"],
+                    default=None, help="time one hot-path entry point only (for profiling); prints its row")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) so a "
                          "counter run can scale FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="turn the rocprofv3 output under DIR into profiles/*.md and traffic.json")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(channels and sequences are independent; see the sharding notes).", file=sys.stderr)
@@ -426,27 +792,37 @@ def main():
         torch.mul(src, 1.0, out=dst)   # elementwise copy kernel: 1 GiB read + 1 GiB written
         torch.cuda.synchronize()
         del src, dst
-    if args.only == "decode":
-        print(json.dumps({"decode": bench_decode(torch, ssm, gen)}))
+    single = {"tiny": ("tiny_fp32", lambda: bench_tiny(torch, ssm, gen)),
+              "m130": ("mamba130m_fp32", lambda: bench_130m(torch, ssm, gen, steps=args.steps)),
+              "decode": ("decode", lambda: bench_decode(torch, ssm, gen)),
+              "ssd": ("ssd", lambda: bench_ssd(torch, ssm, gen, steps=args.steps)),
+              "bwd": ("bwd", lambda: bench_bwd(torch, ssm, gen, steps=args.steps)),
+              "pool": ("pool_decode", lambda: bench_pool_decode(torch, ssm, gen, steps=args.steps)),
+              "conv": ("conv", lambda: bench_conv(torch, ssm, gen, steps=args.steps))}
+    if args.only in single:
+        key, fn = single[args.only]
+        print(json.dumps({key: fn()}))
         return
-    if args.only == "ssd":
-        print(json.dumps({"ssd": bench_ssd(torch, ssm, gen, steps=args.steps)}))
-        return
-    if args.only == "bwd":
-        print(json.dumps({"bwd": bench_bwd(torch, ssm, gen, steps=args.steps)}))
-        return
-    if args.only == "pool":
-        print(json.dumps({"pool_decode": bench_pool_decode(torch, ssm, gen, steps=args.steps)}))
-        return
-    if args.only == "conv":
-        print(json.dumps({"conv": bench_conv(torch, ssm, gen, steps=args.steps)}))
-        return
+
+    # the other configurations and entry points first: besides their own
+    # figures they leave the device warm for the headline steps
+    rows, copy_gbs = None, None
+    if not args.no_rows and args.only is None:
+        copy_gbs = copy_bandwidth(torch)
+        rows = {"tiny_fp32": bench_tiny(torch, ssm, gen), "mamba130m_fp32": bench_130m(torch, ssm, gen),
+                "decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen, steps=20),
+                "conv": bench_conv(torch, ssm, gen), "pool_decode": bench_pool_decode(torch, ssm, gen),
+                "bwd": bench_bwd(torch, ssm, gen)}
+        for row in rows.values():  # HBM rates also as a fraction of the copy
+            for r in [row] + [v for v in row.values() if isinstance(v, dict)]:
+                if "hbm_GBs" in r:
+                    r["copy_frac"] = r["hbm_GBs"] / copy_gbs
+        torch.cuda.empty_cache()
 
     name = "mamba2p8b_prefill_bf16"
     inp = gen.make_workload(name)
     B, L, D, N = inp.B, inp.L, inp.D, inp.N
-    t = {k: upload(getattr(inp, k), torch) for k in ("x", "delta", "z", "Bm", "Cm")}
-    A, Ds, h0 = upload(inp.A, torch), upload(inp.D_skip, torch), upload(inp.h0, torch)
+    t, A, Ds, h0 = scan_inputs(inp, torch)
     y = torch.empty((B, L, D), dtype=torch.bfloat16, device="cuda")
     hf = torch.empty((B, D, N), dtype=torch.float32, device="cuda")
     ws_n = ssm.scan_fwd_workspace_size(B, L, D, N)
@@ -463,21 +839,30 @@ def main():
     kern_s = mean_ms * 1e-3
     hbm_gbs = alg / kern_s / 1e9
     elem_rate = elems / kern_s
-    traffic = load_traffic("scan_fwd")
+    e = load_entry("scan_fwd") or {}
+    mix = e.get("valu")
+    alu = {"achieved_Telem_s": elem_rate / 1e12,
+           "method_floor_Telem_s": SCAN_ELEM_FLOOR / 1e12,
+           "method_floor_paired_Telem_s": SCAN_ELEM_PAIRED / 1e12,
+           "frac_of_floor": elem_rate / SCAN_ELEM_FLOOR,
+           "kernel_mix": mix,
+           "note": "4 fp32 VALU + 1 v_exp_f32 per element; one VALU op per SIMD quad cycle, "
+                   "v_exp_f32 two, at 2.4 GHz on 1024 SIMDs; 'paired': every plain op dual-issued"}
+    if mix:
+        quads = mix["valu_per_elem_wave"] - mix["trans_per_elem_wave"] + 2 * mix["trans_per_elem_wave"] \
+            - mix["paired_quads_per_elem_wave"]
+        alu["kernel_mix_ceiling_Telem_s"] = SIMDS * CLOCK_HZ * 64 / (4 * quads) / 1e12
     roofline = {
-        "bound": "alu",
-        "achieved": elem_rate * SCAN_FLOPS_PER_ELEM / 1e12,
-        "peak": SCAN_ELEM_PEAK * SCAN_FLOPS_PER_ELEM / 1e12,
-        "unit": "TFLOP/s",
-        "frac": elem_rate / SCAN_ELEM_PEAK,
-        "traffic": traffic,
+        "bound": "hbm",
+        "achieved": hbm_gbs,
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": hbm_gbs / HBM_PEAK_GBS,
+        "traffic": e.get("bytes_per_launch"),
+        "alg_bytes_per_launch": alg,
         "kernel_ms": mean_ms,
         "kernel_ms_min": min_ms,
-        "hbm": {"achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": hbm_gbs / HBM_PEAK_GBS, "alg_bytes_per_launch": alg},
-        "note": "per element 4 fp32 VALU ops + 1 v_exp_f32; ALU ceiling "
-                f"{SCAN_ELEM_PEAK / 1e12:.2f} Telem/s is below the HBM ceiling "
-                f"{HBM_PEAK_GBS * 1e9 / (alg / elems) / 1e12:.2f} Telem/s",
+        "alu": alu,
     }
     out = {
         "metric": "selective-scan Gelem/s (B*L*D*N) + achieved HBM GB/s vs peak on 1 MI355X",
@@ -490,17 +875,10 @@ def main():
         "hbm_GBs": hbm_gbs, "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
         "roofline": roofline,
     }
-    if not args.no_rows and args.only is None:
-        copy_gbs = copy_bandwidth(torch)
+    if rows is not None:
         out["copy_GBs"] = copy_gbs
-        out["roofline"]["hbm"]["frac_of_copy"] = hbm_gbs / copy_gbs
-        out["rows"] = {"decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen, steps=20),
-                       "conv": bench_conv(torch, ssm, gen), "pool_decode": bench_pool_decode(torch, ssm, gen),
-                       "bwd": bench_bwd(torch, ssm, gen)}
-        for row in out["rows"].values():  # HBM rates also as a fraction of the copy
-            for r in [row] + [v for v in row.values() if isinstance(v, dict)]:
-                if "hbm_GBs" in r:
-                    r["copy_frac"] = r["hbm_GBs"] / copy_gbs
+        out["roofline"]["frac_of_copy"] = hbm_gbs / copy_gbs
+        out["rows"] = rows
     if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
     print(json.dumps(out))
