@@ -105,7 +105,7 @@ typedef struct {
 
 /* Largest N the Mamba-1 kernels (scan and decode) are built for. */
 #define SSM_SCAN_MAX_N 64
-/* Largest N the SSD kernels are built for, and the supported head dim P. */
+/* Largest N the SSD kernels are built for. */
 #define SSM_SSD_MAX_N 256
 
 /*
@@ -322,16 +322,22 @@ ssm_status ssm_decode_steps(int64_t S, int64_t T, int64_t D, int64_t N, ssm_dtyp
  *   h_t[p,n] = dA_t * h_{t-1}[p,n] + dt[b,t,h] * Bm[b,t,g,n] * x[b,t,h,p]
  *   y[b,t,h,p] = (sum_n Cm[b,t,g,n] h_t[p,n] + D_skip[h] x[b,t,h,p])
  *                * silu(z[b,t,h,p])
- * computed chunk by chunk (`chunk` tokens): intra-chunk products on the
- * matrix cores, chunk states passed sequentially in fp32, seeded by h0.
- *
+ * Two paths, chosen from the shape alone:
+ *  - matrix cores: bf16 inputs, P == 64, N a multiple of 32 (32 .. 256),
+ *    chunk in {64, 128, 256}, and x, Bm, Cm, h0, h_final and the workspace
+ *    16-byte aligned.  Computed chunk by chunk (`chunk` tokens):
+ *    intra-chunk products on the matrix cores with computed operands split
+ *    into bf16 hi + lo, chunk states passed sequentially in fp32 from h0.
+ *    Needs ssm_ssd_fwd_workspace_size() bytes of workspace.
+ *  - every other shape with N <= SSM_SSD_MAX_N (fp32 inputs, any P, any
+ *    N, any chunk >= 1, any alignment): the recurrence token by token on
+ *    the vector ALU in fp32; the result does not depend on `chunk`; no
+ *    workspace (workspace may be NULL).
  * x, z, y   : (B, L, H, P) dtype `dt`;  dt_in : (B, L, H) dtype `dt`
  * Bm, Cm    : (B, L, G, N) dtype `dt`;  A, D_skip : (H) fp32 (D_skip may be NULL)
  * h0, h_final : (B, H, P, N) fp32 or NULL.  z may be NULL.
- * Supported: dt == SSM_BF16; P == 64; N a multiple of 32 with
- * N <= SSM_SSD_MAX_N; chunk in {64, 128, 256}; H % G == 0; x, Bm, Cm,
- * h0, h_final and workspace 16-byte aligned.  Other sizes return
- * SSM_ERR_UNSUPPORTED.  Any L >= 0 (a ragged last chunk is handled).
+ * SSM_ERR_UNSUPPORTED: N > SSM_SSD_MAX_N, chunk < 1, H % G != 0.  Any
+ * L >= 0 (a ragged last chunk is handled).
  */
 ssm_status ssm_ssd_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                        int64_t N, int64_t chunk, ssm_dtype dt, const void *x,
@@ -349,6 +355,8 @@ ssm_status ssm_ssd_fwd_ex(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                           void *workspace, size_t workspace_bytes,
                           const ssm_delta_opts *dopts, void *stream);
 
+/* Workspace of the matrix-core path for these sizes (bytes); 0 where that
+ * path does not apply (the token-by-token path needs none). */
 size_t ssm_ssd_fwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P,
                                   int64_t G, int64_t N, int64_t chunk);
 

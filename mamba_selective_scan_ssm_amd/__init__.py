@@ -238,7 +238,7 @@ def ssd_fwd(x, dt, A, Bm, Cm, D_skip=None, z=None, h0=None, *, chunk=256, y=None
             return_final=True, workspace=None, dt_bias=None, dt_softplus=False):
     """Mamba-2 SSD chunked scan (ssm_ssd_fwd).
 
-    x, z: (B, L, H, P); dt: (B, L, H); Bm, Cm: (B, L, G, N) bfloat16;
+    x, z: (B, L, H, P); dt: (B, L, H); Bm, Cm: (B, L, G, N), all bfloat16 or all float32;
     A, D_skip: (H,) float32; h0: (B, H, P, N) float32.  dt_bias: (H,)
     float32 added to dt, then softplus if dt_softplus.  Returns (y, h_final).
     """

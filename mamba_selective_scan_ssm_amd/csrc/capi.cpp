@@ -87,6 +87,12 @@ Plan plan_scan(int64_t L, int64_t D, const ssm_tuning *t) {
 
 ssm_status hip_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
 
+// shapes the matrix-core SSD kernels are built for
+bool ssd_mfma_applies(ssm_dtype dt, int64_t P, int64_t N, int64_t chunk) {
+  return dt == SSM_BF16 && P == 64 && N % 32 == 0 && N >= 32 && N <= SSM_SSD_MAX_N &&
+         (chunk == 64 || chunk == 128 || chunk == 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,6 +474,9 @@ ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype dt
 size_t ssm_ssd_fwd_workspace_size(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                                   int64_t N, int64_t chunk) {
   if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || G <= 0 || N <= 0 || chunk <= 0) return 0;
+  // what the matrix-core path needs (bf16 inputs); the token-by-token path
+  // needs none
+  if (!ssd_mfma_applies(SSM_BF16, P, N, chunk)) return 0;
   return static_cast<size_t>(ssm::ssd_ws_bytes(B, L, H, P, G, N, chunk));
 }
 
@@ -488,22 +497,19 @@ ssm_status ssm_ssd_fwd_ex(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
   if (B < 0 || L < 0 || H < 0 || P < 0 || G < 0 || N < 0 || chunk < 0 || !valid_dtype(dt) ||
       !dopts_ok(dopts))
     return SSM_ERR_INVALID_ARG;
-  if (dt != SSM_BF16) return SSM_ERR_UNSUPPORTED;
-  if (P != 64 || N % 32 != 0 || N > SSM_SSD_MAX_N || N == 0) return SSM_ERR_UNSUPPORTED;
-  if (chunk != 64 && chunk != 128 && chunk != 256) return SSM_ERR_UNSUPPORTED;
+  if (N > SSM_SSD_MAX_N || chunk < 1) return SSM_ERR_UNSUPPORTED;
   if (G <= 0 || H % G != 0) return SSM_ERR_UNSUPPORTED;
-  {
-    // x, B, C are read and the states moved in 16-byte pieces
-    auto a16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-    if (!a16(x) || !a16(Bm) || !a16(Cm) || !a16(h0) || !a16(h_final) || !a16(workspace))
-      return SSM_ERR_UNSUPPORTED;
-  }
-  if (B == 0 || H == 0) return SSM_OK;
+  // the matrix-core kernels where they apply (x, B, C read and the states
+  // moved in 16-byte pieces); the token-by-token kernel otherwise
+  auto a16 = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const bool mfma_path = ssd_mfma_applies(dt, P, N, chunk) && a16(x) && a16(Bm) && a16(Cm) && a16(h0) &&
+                         a16(h_final) && a16(workspace);
+  if (B == 0 || H == 0 || P == 0) return SSM_OK;
   const int64_t nc = (L + chunk - 1) / chunk;
   if (B > kMaxGridYZ || H > kMaxGridYZ) return SSM_ERR_UNSUPPORTED;
   if (L > 0 && (!x || !dt_in || !Bm || !Cm || !y)) return SSM_ERR_INVALID_ARG;
   if (!A) return SSM_ERR_INVALID_ARG;
-  const int64_t es = 2;
+  const int64_t es = esize(dt);
   const int64_t nX = B * L * H * P, nB = B * L * G * N, nS = B * H * P * N;
   const Range ins[] = {{x, nX * es},  {dt_in, B * L * H * es}, {A, H * 4},  {Bm, nB * es},
                        {Cm, nB * es}, {D_skip, H * 4},         {z, nX * es}, {h0, nS * 4},
@@ -511,7 +517,7 @@ ssm_status ssm_ssd_fwd_ex(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
   if (overlaps_any(Range{y, nX * es}, ins)) return SSM_ERR_INVALID_ARG;
   if (overlaps_any(Range{h_final, nS * 4}, ins)) return SSM_ERR_INVALID_ARG;
   if (overlap(Range{y, nX * es}, Range{h_final, nS * 4})) return SSM_ERR_INVALID_ARG;
-  const int64_t need = ssm::ssd_ws_bytes(B, L, H, P, G, N, chunk);
+  const int64_t need = mfma_path ? ssm::ssd_ws_bytes(B, L, H, P, G, N, chunk) : 0;
   if (need > 0 && (!workspace || static_cast<int64_t>(workspace_bytes) < need))
     return SSM_ERR_WORKSPACE;
   if (need > 0 && (overlaps_any(Range{workspace, need}, ins) ||
@@ -522,9 +528,11 @@ ssm_status ssm_ssd_fwd_ex(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
 
   ssm::SSDArgs a{};
   a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N; a.chunk = chunk;
+  a.dt_type = dt == SSM_BF16 ? DType::BF16 : DType::F32;
   a.x = x; a.dt = dt_in; a.A = A; a.Bm = Bm; a.Cm = Cm; a.D_skip = D_skip; a.z = z;
   a.h0 = h0; a.y = y; a.h_final = h_final;
   a.dt_bias = dbias_of(dopts); a.dt_softplus = dsoft_of(dopts);
+  if (!mfma_path) return hip_status(ssm::launch_ssd_seq(a, static_cast<hipStream_t>(stream)));
   return hip_status(ssm::launch_ssd(a, workspace, static_cast<hipStream_t>(stream)));
 }
 

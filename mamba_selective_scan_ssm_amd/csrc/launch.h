@@ -92,6 +92,7 @@ hipError_t launch_state_update(const StepArgs &a, hipStream_t s);
 
 struct SSDArgs {
   int64_t B, L, H, P, G, N, chunk;
+  DType dt_type;  // storage type of x, dt, Bm, Cm, z and y
   const void *x, *dt;
   const float *A;
   const void *Bm, *Cm;
@@ -121,7 +122,12 @@ struct ConvArgs {
 hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t s);
 hipError_t launch_conv1d_update(const ConvArgs &a, hipStream_t s);
 
+// SSD on the matrix cores (ssd.hip): bf16, P = 64, N a multiple of 32 up to
+// 256, chunk 64, 128 or 256; workspace ssd_ws_bytes.
 int64_t ssd_ws_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t chunk);
 hipError_t launch_ssd(const SSDArgs &a, void *ws, hipStream_t s);
+// SSD token by token on the vector ALU (ssd_seq.hip): any dtype, P, N <= 256,
+// no workspace.
+hipError_t launch_ssd_seq(const SSDArgs &a, hipStream_t s);
 
 }  // namespace ssm

@@ -146,18 +146,23 @@ def ssd(lib, B=1, L=512, H=8, P_=64, G=2, N=128, chunk=256, dt=BF16, ws=None, ws
 
 
 def test_ssd_validation(lib):
+    # every call here is refused on the host, before any launch
     assert ssd(lib, B=-1) == INVALID
-    assert ssd(lib, dt=F32) == UNSUPPORTED
-    assert ssd(lib, P_=48) == UNSUPPORTED
-    assert ssd(lib, N=100) == UNSUPPORTED
-    assert ssd(lib, chunk=100) == UNSUPPORTED
+    assert ssd(lib, dt=7) == INVALID
+    assert ssd(lib, N=300) == UNSUPPORTED                   # above SSM_SSD_MAX_N
+    assert ssd(lib, chunk=0) == UNSUPPORTED
     assert ssd(lib, H=8, G=3) == UNSUPPORTED
     assert ssd(lib, y=P[0]) == INVALID
+    assert ssd(lib, dt=F32, y=P[0]) == INVALID              # fp32 takes the token-by-token path,
+    assert ssd(lib, P_=48, h_final=P[7]) == INVALID         # P != 64 too: same argument checks
+    assert ssd(lib, A=None) == INVALID
     assert ssd(lib, B=0) == OK
-    for k in ("x", "Bm", "Cm", "h0", "h_final"):   # 16-byte pieces
-        assert ssd(lib, **{k: ctypes.c_void_p(P[["x", "dtv", "A", "Bm", "Cm", "D_skip", "z", "h0", "y",
-                                                  "h_final"].index(k)].value + 4)}) == UNSUPPORTED, k
-    assert ssd(lib, ws=ctypes.c_void_p(P[12].value + 8), ws_len=1 << 40) == UNSUPPORTED
+    assert ssd(lib, P_=0) == OK
+    # the matrix-core path needs its workspace; the other path needs none
+    assert ssd(lib) == WORKSPACE
+    assert lib.ssm_ssd_fwd_workspace_size(1, 512, 8, 64, 2, 128, 256) > 0
+    for shape in ((1, 512, 8, 48, 2, 128, 256), (1, 512, 8, 64, 2, 100, 256), (1, 512, 8, 64, 2, 128, 100)):
+        assert lib.ssm_ssd_fwd_workspace_size(*shape) == 0, shape
 
 
 def test_scan_lanesplit_variant_limits(lib):

@@ -122,3 +122,57 @@ def test_ssd_determinism():
     a = ssm.ssd_fwd(*args)
     b = ssm.ssd_fwd(*args)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# Shapes the matrix-core kernels are not built for take the token-by-token
+# kernel (ssd_seq.hip): fp32 inputs, head dims other than 64, N not a
+# multiple of 32, other chunk lengths, x not 16-byte aligned.
+@pytest.mark.parametrize("B,L,H,P,G,N,chunk,dtype,gate", [
+    (1, 200, 4, 64, 2, 64, 64, "f32", False),     # fp32, at the fp32 bar
+    (2, 300, 6, 32, 3, 128, 256, "f32", True),    # fp32, P 32, gate
+    (1, 130, 3, 16, 1, 48, 128, "f32", False),    # P 16 (four heads per 64 channels), N 48
+    (2, 257, 4, 128, 2, 128, 256, "bf16", True),  # P 128
+    (1, 99, 5, 24, 5, 16, 256, "bf16", False),    # P 24 (workgroups span heads), N 16, G = H
+    (1, 300, 4, 64, 2, 128, 100, "bf16", False),  # chunk 100
+    (1, 0, 2, 32, 1, 32, 64, "f32", False),       # empty sequence
+])
+def test_ssd_token_path(oracle_mod, B, L, H, P, G, N, chunk, dtype, gate):
+    w = gen.make_ssd(B, L, H, P, G, N, chunk=chunk, dtype=dtype, seed=450 + L + P + N, gate=gate)
+    _say("ssd token path", B, L, H, P, G, N, chunk, dtype, gate)
+    y, hf = run_gpu(w)
+    ry, rh = run_oracle(oracle_mod, w)
+    assert y.shape == (B, L, H, P)
+    assert_close(y, ry, dtype, "y")
+    assert_close(hf, rh, dtype, "h_final")
+
+
+def test_ssd_unaligned_x_takes_token_path(oracle_mod):
+    """x one element off 16-byte alignment: the token-by-token kernel, same results."""
+    import mamba_selective_scan_ssm_amd as ssm
+    w = gen.make_ssd(1, 300, 4, 64, 2, 128, chunk=256, dtype="bf16", seed=470)
+    _say("ssd unaligned x")
+    xs = to_dev(w.x)
+    buf = torch.empty(xs.numel() + 1, dtype=xs.dtype, device="cuda")
+    x_off = buf[1:].view_as(xs)
+    x_off.copy_(xs)
+    y, hf = ssm.ssd_fwd(x_off, to_dev(w.dt), to_dev(w.A), to_dev(w.Bm), to_dev(w.Cm), to_dev(w.D_skip),
+                        None, to_dev(w.h0), chunk=w.chunk)
+    torch.cuda.synchronize()
+    ry, rh = run_oracle(oracle_mod, w)
+    assert_close(to_np(y), ry, "bf16", "y")
+    assert_close(to_np(hf), rh, "bf16", "h_final")
+
+
+def test_ssd_token_path_dt_transform(oracle_mod):
+    """dt bias per head and softplus on the token-by-token path (fp32)."""
+    import mamba_selective_scan_ssm_amd as ssm
+    w = gen.make_ssd(2, 150, 4, 32, 2, 64, chunk=64, dtype="f32", seed=471)
+    bias = np.random.default_rng(472).normal(0.0, 0.5, 4).astype(np.float32)
+    _say("ssd token path dt transform")
+    y, hf = ssm.ssd_fwd(to_dev(w.x), to_dev(w.dt), to_dev(w.A), to_dev(w.Bm), to_dev(w.Cm), to_dev(w.D_skip),
+                        None, to_dev(w.h0), chunk=w.chunk, dt_bias=to_dev(bias), dt_softplus=True)
+    torch.cuda.synchronize()
+    ry, rh = oracle_mod.ssd(w.x.f32, w.dt.f32, w.A, w.Bm.f32, w.Cm.f32, w.D_skip, None, w.h0,
+                            dt_bias=bias, dt_softplus=True)
+    assert_close(to_np(y), ry, "f32", "y")
+    assert_close(to_np(hf), rh, "f32", "h_final")
