@@ -464,9 +464,9 @@ def bench_bwd(torch, ssm, gen, steps=10):
                                   "saved_state_bytes": ck.numel() * 4}}
 
 
-def bench_pool_decode(torch, ssm, gen, steps=128):
+def bench_pool_decode(torch, ssm, gen, steps=128, only_tokens=None):
     """Decode from a state pool (ssm_decode_steps): 256 sequences on scattered
-    rows of a 512-row pool; 1, 4 and 16 tokens per call."""
+    rows of a 512-row pool; 1, 4 and 16 tokens per call (or only_tokens)."""
     w = gen.make_workload("pool_decode_256x5120_bf16")
     tk = w.tokens
     S, T, D, N = tk.B, tk.L, tk.D, tk.N
@@ -476,7 +476,7 @@ def bench_pool_decode(torch, ssm, gen, steps=128):
     A, Ds = upload(tk.A, torch), upload(tk.D_skip, torch)
     out = {"workload": f"pool_decode_256x5120_bf16 (S={S}, D={D}, N={N}, pool {w.pool.shape[0]} rows, "
                        "scattered slots, bf16, fp32 state)"}
-    for tt in (1, 4, T):
+    for tt in (1, 4, T) if only_tokens is None else (only_tokens,):
         tok = {k: v[:, :tt].contiguous() for k, v in t.items()}
         y = torch.empty((S, tt, D), dtype=torch.bfloat16, device="cuda")
 
@@ -511,30 +511,44 @@ VALU_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_VAL
 MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU",
                  "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
 PROFILE_ENTRIES = {
-    # entry: (--only, timed args, short args, summary file, title, kernels of one call, elements
-    #         per call (for the per-element counter figures) or None, extra passes)
-    "scan_fwd": ("scan", "--steps 100 --warmup 30 --no-cpu", "--steps 2 --warmup 1 --no-cpu",
-                 "scan_lanesplit_mamba2p8b_prefill_bf16.md",
-                 "Mamba-1 prefill selective scan, B=8 L=4096 D=5120 N=16, bf16 inputs, fp32 state (ssm_scan_fwd)",
-                 ["scan_lanesplit_kernel"], 8 * 4096 * 5120 * 16, ["v"]),
-    "scan_fwd_130m": ("m130", "--steps 50", "--steps 2", "scan_mamba130m_fp32.md",
-                      "Mamba-1 scan, B=1 L=2048 D=1536 N=16, fp32, every schedule (ssm_scan_fwd)",
-                      ["scan_split_kernel", "scan_carry_kernel", "scan_lanesplit_kernel"], 2048 * 1536 * 16, []),
-    "state_update": ("decode", "", "", "state_update_decode_256x5120_bf16.md",
-                     "decode step, S=256 D=5120 N=16, bf16 inputs, fp32 state (ssm_state_update)",
-                     ["state_step"], None, []),
-    "ssd_fwd": ("ssd", "--steps 20", "--steps 2", "ssd_chunked_mamba2_bf16.md",
-                "Mamba-2 SSD chunked scan, B=2 L=8192 H=80 P=64 N=128 G=8 chunk 256, bf16 (ssm_ssd_fwd)",
-                ["ssd_"], None, ["m"]),
-    "conv1d_fwd": ("conv", "--steps 50", "--steps 2", "conv1d_mamba2p8b_bf16.md",
-                   "causal convolution K=4, B=8 L=4096 D=5120 bf16, and its decode step S=256 (ssm_conv1d_*)",
-                   ["conv1d_fwd"], None, []),
-    "decode_steps": ("pool", "--steps 64", "--steps 2", "decode_steps_pool_256x5120_bf16.md",
-                     "pool decode, 256 of 512 rows, D=5120 N=16, T = 1, 4, 16 (ssm_decode_steps)",
-                     ["state_"], None, []),
-    "scan_bwd": ("bwd", "--steps 10", "--steps 1", "scan_bwd_mamba2p8b_prefill_bf16.md",
-                 "selective-scan backward, B=8 L=4096 D=5120 N=16, bf16, all gradients (ssm_scan_bwd)",
-                 ["scan_bwd_kernel", "bwd_reduce"], 8 * 4096 * 5120 * 16, ["v"]),
+    # entry: dict(only=--only, t=timed args, s=short args, file=summary file, title, k=kernel name
+    #   patterns of one call, elems=elements per call (per-element counter figures), extra=extra
+    #   passes, run=directory of the profiled run when another entry's run also covers this one)
+    "scan_fwd": dict(only="scan", t="--steps 100 --warmup 30 --no-cpu", s="--steps 2 --warmup 1 --no-cpu",
+                     file="scan_lanesplit_mamba2p8b_prefill_bf16.md",
+                     title="Mamba-1 prefill selective scan, B=8 L=4096 D=5120 N=16, bf16 inputs, fp32 state "
+                           "(ssm_scan_fwd)",
+                     k=["scan_lanesplit_kernel"], elems=8 * 4096 * 5120 * 16, extra="v"),
+    "scan_fwd_130m": dict(only="m130", t="--steps 50", s="--steps 2", file="scan_mamba130m_fp32.md",
+                          title="Mamba-1 scan, B=1 L=2048 D=1536 N=16, fp32, every schedule (ssm_scan_fwd)",
+                          k=["scan_split_kernel", "scan_carry_kernel", "scan_lanesplit_kernel"],
+                          elems=2048 * 1536 * 16),
+    "state_update": dict(only="decode", t="", s="", file="state_update_decode_256x5120_bf16.md",
+                         title="decode step, S=256 D=5120 N=16, bf16 inputs, fp32 state (ssm_state_update)",
+                         k=["state_step"]),
+    "ssd_fwd": dict(only="ssd", t="--steps 20", s="--steps 2", file="ssd_chunked_mamba2_bf16.md",
+                    title="Mamba-2 SSD chunked scan, B=2 L=8192 H=80 P=64 N=128 G=8 chunk 256, bf16 "
+                          "(ssm_ssd_fwd)",
+                    k=["ssd_"], extra="m"),
+    "conv1d_fwd": dict(only="conv", t="--steps 50", s="--steps 2", file="conv1d_mamba2p8b_bf16.md",
+                       title="causal convolution K=4, B=8 L=4096 D=5120 bf16 (ssm_conv1d_fwd)",
+                       k=["conv1d_fwd_kernel", "conv1d_state_kernel"]),
+    "conv1d_update": dict(only="conv", t="--steps 50", s="--steps 2", file="conv1d_mamba2p8b_bf16.md",
+                          title="convolution decode step K=4, S=256 D=5120 bf16 (ssm_conv1d_update)",
+                          k=["conv1d_update_kernel"], run="conv1d_fwd"),
+    "decode_steps_T1": dict(only="pool", t="--steps 64 --pool-tokens 1", s="--steps 2 --pool-tokens 1",
+                            file="decode_steps_pool_256x5120_bf16.md",
+                            title="pool decode, 256 of 512 rows, D=5120 N=16 bf16, T=1 token per call "
+                                  "(ssm_decode_steps)", k=["state_"]),
+    "decode_steps_T4": dict(only="pool", t="--steps 64 --pool-tokens 4", s="--steps 2 --pool-tokens 4",
+                            file="decode_steps_pool_256x5120_bf16.md",
+                            title="pool decode, T=4 tokens per call (ssm_decode_steps)", k=["state_"]),
+    "decode_steps_T16": dict(only="pool", t="--steps 64 --pool-tokens 16", s="--steps 2 --pool-tokens 16",
+                             file="decode_steps_pool_256x5120_bf16.md",
+                             title="pool decode, T=16 tokens per call (ssm_decode_steps)", k=["state_"]),
+    "scan_bwd": dict(only="bwd", t="--steps 10", s="--steps 1", file="scan_bwd_mamba2p8b_prefill_bf16.md",
+                     title="selective-scan backward, B=8 L=4096 D=5120 N=16, bf16, all gradients (ssm_scan_bwd)",
+                     k=["scan_bwd_kernel", "bwd_reduce"], elems=8 * 4096 * 5120 * 16, extra="v"),
 }
 
 
@@ -565,6 +579,8 @@ def _find(dirpath, suffix):
 def _counters(path):
     """{dispatch id: (kernel name, {counter: value})} from a counter_collection.csv."""
     out = {}
+    if path is None:
+        return out
     for r in _csv_rows(path):
         d = int(r["Dispatch_Id"])
         name = r["Kernel_Name"]
@@ -589,168 +605,160 @@ def _short(name, n=110):
     return name if len(name) <= n else name[:n] + "..."
 
 
+def _entry_section(src, entry, p, rec):
+    """Markdown lines for one profiled entry; fills rec (its traffic.json record)."""
+    base = os.path.join(src, p.get("run", entry))
+    kpat, extra, elems, only = p["k"], p.get("extra", ""), p.get("elems"), p["only"]
+    match = lambda name: any(k in name for k in kpat)
+    trace_p = _find(os.path.join(base, "kt"), "kernel_trace.csv")
+    durs = {}
+    for r in _csv_rows(trace_p):
+        if match(r["Kernel_Name"]):
+            durs.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    fetch = _counters(_find(os.path.join(base, "f"), "counter_collection.csv"))
+    write = _counters(_find(os.path.join(base, "w"), "counter_collection.csv"))
+    fcal, wcal = _calibration(fetch, "FETCH_SIZE"), _calibration(write, "WRITE_SIZE")
+    fs = (1 << 30) / fcal if fcal else None   # bytes per KiB of counter
+    ws_ = (1 << 30) / wcal if wcal else None
+
+    def per_kernel(disp, counter):
+        acc = {}
+        for name, c in disp.values():
+            if counter in c and match(name):
+                acc.setdefault(name, []).append(c[counter])
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    f_k, w_k = per_kernel(fetch, "FETCH_SIZE"), per_kernel(write, "WRITE_SIZE")
+    lines = [f"# rocprofv3: {p['title']}", ""]
+    lines.append("MI355X (gfx950).  Kernel source hash (sha256, first 16 hex digits, over "
+                 + ", ".join(KERNEL_SOURCES[entry]) + " in mamba_selective_scan_ssm_amd/csrc, "
+                 f"as bench.py computes it): `{csrc_hash(entry)}`.  Commands, from the repository root on "
+                 "the GPU machine after `cd /tmp && export TMPDIR=/tmp`:")
+    lines.append("")
+    cmd = lambda c: "`" + " ".join(c.split()) + "`"
+    lines.append("* kernel trace: " + cmd(f"rocprofv3 --kernel-trace --stats --output-format csv -d <out>/kt "
+                                          f"-o kt -- python3 bench.py --only {only} {p['t']}"))
+    lines.append(f"* HBM reads: `rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/f -o f "
+                 f"-- python3 bench.py --only {only} {p['s']} --copy-calib`".replace("  ", " "))
+    lines.append("* HBM writes: the same with `--pmc WRITE_SIZE`")
+    if "v" in extra:
+        lines.append(f"* VALU counters: `rocprofv3 --pmc {' '.join(VALU_COUNTERS)} --output-format csv "
+                     f"-d <out>/v -o v -- python3 bench.py --only {only} {p['s']}`".replace("  ", " "))
+    if "m" in extra:
+        lines.append(f"* matrix-core counters: `rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv "
+                     f"-d <out>/m -o m -- python3 bench.py --only {only} {p['s']}`".replace("  ", " "))
+    lines.append("")
+    if fcal and wcal:
+        lines.append(f"Counter calibration: `--copy-calib` runs one elementwise copy that reads 1 GiB and "
+                     f"writes 1 GiB; it read FETCH_SIZE {fcal:.0f} KiB and WRITE_SIZE {wcal:.0f} KiB, so "
+                     f"FETCH_SIZE is scaled by {1048576 / fcal:.3f} and WRITE_SIZE by {1048576 / wcal:.3f} "
+                     "to give bytes.")
+        lines.append("")
+    lines.append("| kernel | calls | avg us | min us | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch "
+                 "| HBM bytes/dispatch (scaled) |")
+    lines.append("|---|---|---|---|---|---|---|")
+    for name, d in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        fk, wk = f_k.get(name), w_k.get(name)
+        hb = (fk * fs + wk * ws_) if (fk is not None and wk is not None and fs and ws_) else None
+        lines.append(f"| `{_short(name)}` | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | "
+                     f"{'' if fk is None else f'{fk:.0f}'} | {'' if wk is None else f'{wk:.0f}'} | "
+                     f"{'' if hb is None else f'{hb / 1e6:.2f} MB'} |")
+    lines.append("")
+    if "v" in extra:
+        disp = _counters(_find(os.path.join(base, "v"), "counter_collection.csv"))
+        last = {}
+        for d, (name, c) in sorted(disp.items()):
+            if match(name) and "SQ_INSTS_VALU" in c:
+                last[name] = c
+        if last:
+            lines.append("VALU counters (the last dispatch of each kernel; per wave64 element slot = per 64 "
+                         "elements):")
+            lines.append("")
+            lines.append("| kernel | VALU insts | of which v_exp etc. (TRANS_F32) | VALU quad cycles "
+                         "(ACTIVE_INST_VALU) | dual-issue quad cycles (ACTIVE_INST_VALU2) | LDS insts | waves "
+                         "| VALU busy (quad cycles x 4 / (1024 SIMDs x GUI cycles / 8 XCDs)) |")
+            lines.append("|---|---|---|---|---|---|---|---|")
+        for name, c in last.items():
+            gui = c.get("GRBM_GUI_ACTIVE", 0) / 8
+            busy = c["SQ_ACTIVE_INST_VALU"] * 4 / (1024 * gui) if gui else float("nan")
+            ew = elems / 64 if elems else None
+            lines.append(f"| `{_short(name, 70)}` | {c['SQ_INSTS_VALU']:.4g}"
+                         + (f" ({c['SQ_INSTS_VALU'] / ew:.2f}/elem-wave)" if ew else "")
+                         + f" | {c['SQ_INSTS_VALU_TRANS_F32']:.4g}"
+                         + (f" ({c['SQ_INSTS_VALU_TRANS_F32'] / ew:.3f})" if ew else "")
+                         + f" | {c['SQ_ACTIVE_INST_VALU']:.4g} | {c['SQ_ACTIVE_INST_VALU2']:.4g}"
+                         + f" ({2 * c['SQ_ACTIVE_INST_VALU2'] / c['SQ_INSTS_VALU']:.2f} of VALU insts paired)"
+                         + f" | {c['SQ_INSTS_LDS']:.4g} | {c['SQ_WAVES']:.0f} | {busy:.2f} |")
+            if ew and entry == "scan_fwd":
+                rec["valu"] = {"valu_per_elem_wave": c["SQ_INSTS_VALU"] / ew,
+                               "trans_per_elem_wave": c["SQ_INSTS_VALU_TRANS_F32"] / ew,
+                               "paired_quads_per_elem_wave": c["SQ_ACTIVE_INST_VALU2"] / ew,
+                               "valu_busy": busy}
+        lines.append("")
+    if "m" in extra:
+        disp = _counters(_find(os.path.join(base, "m"), "counter_collection.csv"))
+        last = {}
+        for d, (name, c) in sorted(disp.items()):
+            if match(name) and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                last[name] = c
+        if last:
+            lines.append("Matrix-core counters (last dispatch of each kernel):")
+            lines.append("")
+            lines.append("| kernel | MFMA busy cycles | MFMA busy (/ (1024 SIMDs x GUI cycles / 8)) "
+                         "| bf16 MFMA MOPs (x512 flops) | VALU insts | LDS insts | waves |")
+            lines.append("|---|---|---|---|---|---|---|")
+        tot_busy, tot_gui = 0.0, 0.0
+        for name, c in last.items():
+            gui = c.get("GRBM_GUI_ACTIVE", 0) / 8
+            mb = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * gui) if gui else float("nan")
+            tot_busy += c["SQ_VALU_MFMA_BUSY_CYCLES"]
+            tot_gui += gui
+            lines.append(f"| `{_short(name, 70)}` | {c['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | {mb:.3f} | "
+                         f"{c['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4g} "
+                         f"({c['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.1f} GFLOP) | "
+                         f"{c['SQ_INSTS_VALU']:.4g} | {c['SQ_INSTS_LDS']:.4g} | {c['SQ_WAVES']:.0f} |")
+        if tot_gui:
+            rec["mfma_busy"] = tot_busy / (1024 * tot_gui)
+            lines.append("")
+            lines.append(f"Over the call's kernels: matrix cores busy {100 * rec['mfma_busy']:.1f}% "
+                         "of SIMD-cycles.")
+        lines.append("")
+    # HBM bytes per call: each of the call's kernels once
+    per_call, ok = 0.0, bool(f_k or w_k)
+    for name in set(f_k) | set(w_k):
+        if entry in CALL_KERNELS and not any(_short(name).startswith(k) for k in CALL_KERNELS[entry]):
+            continue
+        if name in f_k and name in w_k and fs and ws_:
+            per_call += f_k[name] * fs + w_k[name] * ws_
+        else:
+            ok = False
+    if ok:
+        rec["bytes_per_call"] = per_call
+        rec["bytes_per_launch"] = per_call
+        which = (" under the automatic schedule (" + ", ".join(CALL_KERNELS[entry]) + ")"
+                 if entry in CALL_KERNELS else "")
+        lines.append(f"HBM traffic of one call{which} (each of its kernels once): {per_call / 1e6:.2f} MB.")
+        lines.append("")
+    return lines
+
+
 def summarize_profiles(src):
     prof_dir = os.path.join(ROOT, "profiles")
     tj_path = os.path.join(prof_dir, "traffic.json")
     traffic = json.load(open(tj_path)) if os.path.exists(tj_path) else {}
     traffic["note"] = ("csrc_hash: sha256 over the entry's kernel sources (bench.KERNEL_SOURCES); "
                        "bytes: FETCH_SIZE and WRITE_SIZE scaled by the copy calibration")
-    for entry, (only, targs, sargs, fname, title, kpat, elems, extra) in PROFILE_ENTRIES.items():
-        base = os.path.join(src, entry)
-        kt = _find(os.path.join(base, "kt"), "kernel_stats.csv")
-        if kt is None:
+    files = {}
+    for entry, p in PROFILE_ENTRIES.items():
+        if _find(os.path.join(src, p.get("run", entry), "kt"), "kernel_trace.csv") is None:
             continue
-        stats = [r for r in _csv_rows(kt)]
-        trace_p = _find(os.path.join(base, "kt"), "kernel_trace.csv")
-        mins = {}
-        if trace_p:
-            for r in _csv_rows(trace_p):
-                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-                k = r["Kernel_Name"]
-                mins[k] = min(mins.get(k, 1e30), dur)
-        fetch = _counters(_find(os.path.join(base, "f"), "counter_collection.csv") or "/dev/null") \
-            if _find(os.path.join(base, "f"), "counter_collection.csv") else {}
-        write = _counters(_find(os.path.join(base, "w"), "counter_collection.csv")) \
-            if _find(os.path.join(base, "w"), "counter_collection.csv") else {}
-        fcal, wcal = _calibration(fetch, "FETCH_SIZE"), _calibration(write, "WRITE_SIZE")
-        fs = (1 << 20) / fcal if fcal else None   # bytes per KiB of counter
-        ws_ = (1 << 20) / wcal if wcal else None
-        fs = fs * 1024 if fs else None
-        ws_ = ws_ * 1024 if ws_ else None
-
-        def per_kernel(disp, counter):
-            acc = {}
-            for name, c in disp.values():
-                if counter in c and any(p in name for p in kpat):
-                    acc.setdefault(name, []).append(c[counter])
-            return {k: sum(v) / len(v) for k, v in acc.items()}
-
-        f_k, w_k = per_kernel(fetch, "FETCH_SIZE"), per_kernel(write, "WRITE_SIZE")
-        hashes = {e: csrc_hash(e) for e in ([entry] if entry in KERNEL_SOURCES else [])}
-        lines = [f"# rocprofv3: {title}", ""]
-        lines.append("MI355X (gfx950).  Kernel source hash (sha256, first 16 hex digits, over "
-                     + ", ".join(KERNEL_SOURCES.get(entry, [])) + " in mamba_selective_scan_ssm_amd/csrc, "
-                     "as bench.py computes it): " + ", ".join(f"`{h}`" for h in hashes.values())
-                     + ".  Commands, from the repository root on the GPU machine after "
-                     "`cd /tmp && export TMPDIR=/tmp`:")
-        lines.append("")
-        lines.append(f"* kernel trace: `rocprofv3 --kernel-trace --stats --output-format csv -d <out>/kt -o kt "
-                     f"-- python3 bench.py --only {only} {targs}`".replace("  ", " "))
-        lines.append(f"* HBM reads: `rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/f -o f "
-                     f"-- python3 bench.py --only {only} {sargs} --copy-calib`".replace("  ", " "))
-        lines.append(f"* HBM writes: the same with `--pmc WRITE_SIZE`")
-        if "v" in extra:
-            lines.append(f"* VALU counters: `rocprofv3 --pmc {' '.join(VALU_COUNTERS)} --output-format csv "
-                         f"-d <out>/v -o v -- python3 bench.py --only {only} {sargs}`".replace("  ", " "))
-        if "m" in extra:
-            lines.append(f"* matrix-core counters: `rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv "
-                         f"-d <out>/m -o m -- python3 bench.py --only {only} {sargs}`".replace("  ", " "))
-        lines.append("")
-        if fcal and wcal:
-            lines.append(f"Counter calibration: `--copy-calib` runs one elementwise copy that reads 1 GiB and "
-                         f"writes 1 GiB; it read FETCH_SIZE {fcal:.0f} KiB and WRITE_SIZE {wcal:.0f} KiB, so "
-                         f"FETCH_SIZE is scaled by {1048576 / fcal:.3f} and WRITE_SIZE by {1048576 / wcal:.3f} "
-                         "to give bytes.")
-            lines.append("")
-        lines.append("| kernel | calls | avg us | min us | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch "
-                     "| HBM bytes/dispatch (scaled) |")
-        lines.append("|---|---|---|---|---|---|---|")
-        call_bytes, call_us = 0.0, 0.0
-        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-            name = r["Name"]
-            if not any(p in name for p in kpat):
-                continue
-            calls = int(r["Calls"])
-            avg = float(r["AverageNs"]) / 1e3
-            fk, wk = f_k.get(name), w_k.get(name)
-            hb = (fk * fs + wk * ws_) if (fk is not None and wk is not None and fs and ws_) else None
-            lines.append(f"| `{_short(name)}` | {calls} | {avg:.1f} | {mins.get(name, float('nan')):.1f} | "
-                         f"{'' if fk is None else f'{fk:.0f}'} | {'' if wk is None else f'{wk:.0f}'} | "
-                         f"{'' if hb is None else f'{hb / 1e6:.2f} MB'} |")
-        lines.append("")
-        rec = traffic.get(entry, {}) if isinstance(traffic.get(entry), dict) else {}
-        rec = {"csrc_hash": csrc_hash(entry)} if entry in KERNEL_SOURCES else {}
-        if "v" in extra:
-            vc = _find(os.path.join(base, "v"), "counter_collection.csv")
-            if vc:
-                disp = _counters(vc)
-                lines.append("VALU counters (summed over the dispatches of one call of the timed kernel; "
-                             "per wave64 element slot = per 64 elements):")
-                lines.append("")
-                lines.append("| kernel | VALU insts | of which v_exp etc. (TRANS_F32) | VALU quad cycles "
-                             "(ACTIVE_INST_VALU) | dual-issue quad cycles (ACTIVE_INST_VALU2) | LDS insts | waves "
-                             "| VALU busy (quad cycles x 4 / (1024 SIMDs x GUI cycles / 8 XCDs)) |")
-                lines.append("|---|---|---|---|---|---|---|---|")
-                last = {}
-                for d, (name, c) in sorted(disp.items()):
-                    if any(p in name for p in kpat) and "SQ_INSTS_VALU" in c:
-                        last[name] = c
-                for name, c in last.items():
-                    gui = c.get("GRBM_GUI_ACTIVE", 0) / 8
-                    busy = c["SQ_ACTIVE_INST_VALU"] * 4 / (1024 * gui) if gui else float("nan")
-                    ew = elems / 64 if elems else None
-                    lines.append(f"| `{_short(name, 70)}` | {c['SQ_INSTS_VALU']:.4g}"
-                                 + (f" ({c['SQ_INSTS_VALU'] / ew:.2f}/elem-wave)" if ew else "")
-                                 + f" | {c['SQ_INSTS_VALU_TRANS_F32']:.4g}"
-                                 + (f" ({c['SQ_INSTS_VALU_TRANS_F32'] / ew:.3f})" if ew else "")
-                                 + f" | {c['SQ_ACTIVE_INST_VALU']:.4g} | {c['SQ_ACTIVE_INST_VALU2']:.4g}"
-                                 + f" ({2 * c['SQ_ACTIVE_INST_VALU2'] / c['SQ_INSTS_VALU']:.2f} of VALU insts paired)"
-                                 + f" | {c['SQ_INSTS_LDS']:.4g} | {c['SQ_WAVES']:.0f} | {busy:.2f} |")
-                    if ew and entry == "scan_fwd":
-                        rec["valu"] = {"valu_per_elem_wave": c["SQ_INSTS_VALU"] / ew,
-                                       "trans_per_elem_wave": c["SQ_INSTS_VALU_TRANS_F32"] / ew,
-                                       "paired_quads_per_elem_wave": c["SQ_ACTIVE_INST_VALU2"] / ew,
-                                       "valu_busy": busy}
-                lines.append("")
-        if "m" in extra:
-            mc = _find(os.path.join(base, "m"), "counter_collection.csv")
-            if mc:
-                disp = _counters(mc)
-                last = {}
-                for d, (name, c) in sorted(disp.items()):
-                    if any(p in name for p in kpat) and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
-                        last[name] = c
-                lines.append("Matrix-core counters (last dispatch of each kernel):")
-                lines.append("")
-                lines.append("| kernel | MFMA busy cycles | MFMA busy (/ (1024 SIMDs x GUI cycles / 8)) "
-                             "| bf16 MFMA MOPs (x512 flops) | VALU insts | LDS insts | waves |")
-                lines.append("|---|---|---|---|---|---|---|")
-                tot_busy, tot_gui = 0.0, 0.0
-                for name, c in last.items():
-                    gui = c.get("GRBM_GUI_ACTIVE", 0) / 8
-                    mb = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * gui) if gui else float("nan")
-                    tot_busy += c["SQ_VALU_MFMA_BUSY_CYCLES"]
-                    tot_gui += gui
-                    lines.append(f"| `{_short(name, 70)}` | {c['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | {mb:.3f} | "
-                                 f"{c['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4g} ({c['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.1f} GFLOP) | "
-                                 f"{c['SQ_INSTS_VALU']:.4g} | {c['SQ_INSTS_LDS']:.4g} | {c['SQ_WAVES']:.0f} |")
-                if tot_gui:
-                    rec["mfma_busy"] = tot_busy / (1024 * tot_gui)
-                    lines.append("")
-                    lines.append(f"Over the call's kernels: matrix cores busy {100 * rec['mfma_busy']:.1f}% "
-                                 "of SIMD-cycles.")
-                lines.append("")
-        # HBM bytes per call: each of the call's kernels once
-        per_call = 0.0
-        ok = True
-        for name in set(f_k) | set(w_k):
-            if entry in CALL_KERNELS and not any(_short(name).startswith(k) for k in CALL_KERNELS[entry]):
-                continue
-            if name in f_k and name in w_k and fs and ws_:
-                per_call += f_k[name] * fs + w_k[name] * ws_
-            else:
-                ok = False
-        if ok and (f_k or w_k) and entry in KERNEL_SOURCES:
-            rec["bytes_per_call"] = per_call
-            rec["bytes_per_launch"] = per_call
-            which = (" under the automatic schedule (" + ", ".join(CALL_KERNELS[entry]) + ")"
-                     if entry in CALL_KERNELS else "")
-            lines.append(f"HBM traffic of one call{which} (each of its kernels once): {per_call / 1e6:.2f} MB.")
-            lines.append("")
-        if rec:
-            traffic[entry] = rec
+        rec = {"csrc_hash": csrc_hash(entry)}
+        files.setdefault(p["file"], []).append(_entry_section(src, entry, p, rec))
+        traffic[entry] = rec
+    for fname, sections in files.items():
         with open(os.path.join(prof_dir, fname), "w") as f:
-            f.write("\n".join(lines))
+            f.write("\n".join(l for s in sections for l in s))
         print("wrote", fname)
     with open(tj_path, "w") as f:
         json.dump(traffic, f, indent=1)
@@ -767,6 +775,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--only", choices=["scan", "tiny", "m130", "decode", "ssd", "conv", "pool", "bwd"],
                     default=None, help="time one hot-path entry point only (for profiling); prints its row")
+    ap.add_argument("--pool-tokens", type=int, choices=[1, 4, 16], default=None,
+                    help="with --only pool: time this many tokens per call only (for profiling)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) so a "
                          "counter run can scale FETCH_SIZE/WRITE_SIZE")
@@ -797,7 +807,8 @@ def main():
               "decode": ("decode", lambda: bench_decode(torch, ssm, gen)),
               "ssd": ("ssd", lambda: bench_ssd(torch, ssm, gen, steps=args.steps)),
               "bwd": ("bwd", lambda: bench_bwd(torch, ssm, gen, steps=args.steps)),
-              "pool": ("pool_decode", lambda: bench_pool_decode(torch, ssm, gen, steps=args.steps)),
+              "pool": ("pool_decode", lambda: bench_pool_decode(torch, ssm, gen, steps=args.steps,
+                                                                 only_tokens=args.pool_tokens)),
               "conv": ("conv", lambda: bench_conv(torch, ssm, gen, steps=args.steps))}
     if args.only in single:
         key, fn = single[args.only]
