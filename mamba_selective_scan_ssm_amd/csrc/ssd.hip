@@ -40,6 +40,8 @@
 // MFMA used: v_mfma_f32_32x32x16_bf16.  Operand layout (lane l, e = 0..7):
 // A[i = l%32][k = 8*(l/32) + e], B[k = 8*(l/32) + e][j = l%32]; result
 // register r holds D[8*(r/4) + 4*(l/32) + r%4][l%32].
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -75,15 +77,30 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, bf16x2 &hi, bf16x
                                bf16x2);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts
+// by 1, 2, 4, 8 within rows of 16 lanes (lanes without a source add 0), then
+// the last lane of row 0 added to row 1 and of row 2 to row 3, then that of
+// row 1 to rows 2 and 3.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  auto shr = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, true));
+  };
+  v += shr(v, std::integral_constant<int, 0x111>{});  // row_shr:1
+  v += shr(v, std::integral_constant<int, 0x112>{});  // row_shr:2
+  v += shr(v, std::integral_constant<int, 0x114>{});  // row_shr:4
+  v += shr(v, std::integral_constant<int, 0x118>{});  // row_shr:8
+  // row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3; other
+  // rows keep the 0 passed as the old value
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+
 // Inclusive prefix sum over the Q <= 256 values v (one per thread, threads
-// >= Q pass 0) into s_out[0..Q).  Uses wave shuffles and one LDS round.
+// >= Q pass 0) into s_out[0..Q).  Uses DPP moves and one LDS round.
 __device__ void block_inclusive_scan(float v, float *s_out, float *s_wave, int Q) {
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+  v = wave_inclusive_scan(v);
   if (lane == 63) s_wave[wave] = v;
   __syncthreads();
   float add = 0.f;
@@ -628,12 +645,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void ssd_chunk_scan_kernel(SSDArgs
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = pdt[e] * A2 + (e > 0 ? v[e - 1] : 0.f);
-      float run = v[3];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(run, off, 64);
-        if (lane >= off) run += o;
-      }
+      const float run = wave_inclusive_scan(v[3]);
       const float excl = run - v[3];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

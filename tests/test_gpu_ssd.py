@@ -40,6 +40,9 @@ def run_oracle(oracle_mod, w, h0=True, channels=None):
     (1, 333, 2, 1, 32, 128, False),      # N 32
     (1, 270, 2, 2, 256, 256, False),     # N 256
     (2, 7, 4, 2, 128, 256, True),        # fewer tokens than a chunk
+    (1, 600, 4, 2, 64, 256, True),       # chunk 256 at N 64, gate on
+    (2, 530, 4, 4, 32, 256, False),      # chunk 256 at N 32, one head per group
+    (1, 300, 6, 2, 96, 256, False),      # chunk 256 at N 96
 ])
 def test_ssd_small(oracle_mod, B, L, H, G, N, chunk, gate):
     w = gen.make_ssd(B, L, H, 64, G, N, chunk=chunk, dtype="bf16", seed=400 + L + N, gate=gate)
