@@ -88,7 +88,7 @@ KERNEL_SOURCES = {
     "conv1d_update": ["conv1d.hip"] + _COMMON,
     "decode_steps_T1": ["state_update.hip"] + _COMMON,
     "decode_steps_T4": ["state_update.hip"] + _COMMON,
-    "decode_steps_T16": ["state_update.hip"] + _COMMON,
+    "decode_steps_T16": ["scan_fwd.hip"] + _COMMON,
     "scan_bwd": ["scan_bwd.hip", "bwd.h"] + _COMMON,
     "scan_fwd_130m": ["scan_fwd.hip"] + _COMMON,
 }
@@ -545,7 +545,8 @@ PROFILE_ENTRIES = {
                             title="pool decode, T=4 tokens per call (ssm_decode_steps)", k=["state_"]),
     "decode_steps_T16": dict(only="pool", t="--steps 64 --pool-tokens 16", s="--steps 2 --pool-tokens 16",
                              file="decode_steps_pool_256x5120_bf16.md",
-                             title="pool decode, T=16 tokens per call (ssm_decode_steps)", k=["state_"]),
+                             title="pool decode, T=16 tokens per call (ssm_decode_steps; the lane-split scan "
+                                   "kernel)", k=["scan_lanesplit"]),
     "scan_bwd": dict(only="bwd", t="--steps 10", s="--steps 1", file="scan_bwd_mamba2p8b_prefill_bf16.md",
                      title="selective-scan backward, B=8 L=4096 D=5120 N=16, bf16, all gradients (ssm_scan_bwd)",
                      k=["scan_bwd_kernel", "bwd_reduce"], elems=8 * 4096 * 5120 * 16, extra="v"),

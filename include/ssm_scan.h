@@ -288,7 +288,7 @@ size_t ssm_scan_bwd_workspace_size_ex(int64_t B, int64_t L, int64_t D, int64_t N
  * slot_idx[s] of state_pool IN PLACE; its T tokens go through the decode
  * step in order with the state kept on chip between them, so T = 1 is one
  * decode step and T > 1 reads and writes the state once for T tokens.  For
- * T <= 16 the results are bitwise those of T successive ssm_state_update
+ * T <= 4 the results are bitwise those of T successive ssm_state_update
  * calls; longer calls run the prefill scan's kernels (bitwise ssm_scan_fwd
  * with tuning variant 1 and h0 = h_final = the gathered rows).  A sequence's
  * results do not depend on which other sequences share the call.

@@ -381,7 +381,7 @@ __device__ __forceinline__ float word_elem(const uint32_t *w, int e) {
 // otherwise.  A block of this kernel is exactly one such segment.
 // STEP: delta takes the per-channel bias and/or softplus; without it delta is
 // used as loaded (rows past L load as 0, which is what they must stage).
-template <typename T, int LPC, int SPL, bool HAS_Z, bool CK, bool STEP>
+template <typename T, int LPC, int SPL, bool HAS_Z, bool CK, bool STEP, int CYC = 4>
 __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   constexpr int TB = 8;                 // tokens per block
   constexpr int kCPW = kWave / LPC;     // channels per wave
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   constexpr int kV = kN / 4;            // B or C values each lane converts per block
   constexpr int kWords = (kV * static_cast<int>(sizeof(T)) + 3) / 4;
   constexpr uint32_t kES = sizeof(T);
-  constexpr int kCyc = 4;               // blocks per load cycle
+  constexpr int kCyc = CYC;             // blocks per load cycle
   static_assert(LPC == 1 || LPC == 2 || LPC == 4, "LPC must be 1, 2 or 4");
   static_assert(SPL % kV == 0, "a loader lane's values must fall in one lane's slice");
   static_assert(kPairs * 64 * 2 == TB * kCPW, "pair slots must tile the block");
@@ -630,17 +630,22 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   // cycle's y, issue the next cycle's loads, then compute.  Loads and stores
   // share one counter whose waits cannot skip a pending store, so no store is
   // issued between a load and the wait for it except a whole cycle earlier.
-  auto cycle = [&](Raw &cur, Raw &nxt, int64_t cyc) {
+  // nb: blocks of the cycle that hold tokens (the last cycle may have
+  // fewer; its blocks past the end are neither computed nor finished -- their
+  // y stores fall past the plane and the state is already final)
+  auto cycle = [&](Raw &cur, Raw &nxt, int64_t cyc, int nb) {
     stage(cur, cyc);
     if (cyc > 0) store_cycle(cyc - 1);
     issue(nxt, cyc + 1);
     wave_sync_lds();
 #pragma unroll
     for (int u = 0; u < kCyc; ++u) {
-      run_block(u);
-      wave_sync_lds();
-      finish_block(cur, u);
-      wave_sync_lds();
+      if (u < nb) {
+        run_block(u);
+        wave_sync_lds();
+        finish_block(cur, u);
+        wave_sync_lds();
+      }
     }
   };
 
@@ -648,11 +653,11 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   issue(r0, 0);
   int64_t cyc = 0;
   for (; cyc + 1 < ncyc; cyc += 2) {
-    cycle(r0, r1, cyc);
-    cycle(r1, r0, cyc + 1);
+    cycle(r0, r1, cyc, kCyc);
+    cycle(r1, r0, cyc + 1, kCyc);
   }
   if (cyc < ncyc) {
-    cycle(r0, r1, cyc);
+    cycle(r0, r1, cyc, static_cast<int>(nblk - cyc * kCyc));
     ++cyc;
   }
   if (ncyc > 0) store_cycle(cyc - 1);
@@ -823,6 +828,16 @@ hipError_t dispatch_split(const ScanArgs &a, int spl_req, int64_t seg_len, float
 
 template <typename T, int LPC, int SPL, bool STEP>
 void launch_lanesplit_s(const ScanArgs &a, dim3 grid, hipStream_t s) {
+  if (a.L <= 16 && a.h_ckpt == nullptr) {
+    // short runs (multi-token decode): cycles of two blocks halve the LDS and
+    // the registers of the input sets, so more waves stay resident to cover
+    // the latency of each wave's state load and store
+    if (a.z)
+      scan_lanesplit_kernel<T, LPC, SPL, true, false, STEP, 2><<<grid, kWave * 4, 0, s>>>(a);
+    else
+      scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP, 2><<<grid, kWave * 4, 0, s>>>(a);
+    return;
+  }
   if (a.h_ckpt) {
     if (a.z)
       scan_lanesplit_kernel<T, LPC, SPL, true, true, STEP><<<grid, kWave * 4, 0, s>>>(a);

@@ -83,9 +83,9 @@ def test_slots_with_delta_transform(oracle_mod, T):
                           delta_softplus=True)
 
 
-@pytest.mark.parametrize("T,N", [(1, 16), (12, 16), (16, 5), (40, 16), (40, 5)])
+@pytest.mark.parametrize("T,N", [(1, 16), (4, 16), (4, 5), (5, 16), (12, 16), (16, 5), (40, 16), (40, 5)])
 def test_identity_slots_match_single_call_kernels(T, N):
-    """slot_idx = NULL: up to 16 tokens the results are bitwise those of T
+    """slot_idx = NULL: up to 4 tokens the results are bitwise those of T
     successive ssm_state_update calls; longer calls bitwise ssm_scan_fwd
     (variant 1) with h0 = h_final = the state."""
     import mamba_selective_scan_ssm_amd as ssm
@@ -97,7 +97,7 @@ def test_identity_slots_match_single_call_kernels(T, N):
     st = to_dev(pool_np)
     x, dl, Bm, Cm, z = (to_dev(getattr(inp, k)) for k in ("x", "delta", "Bm", "Cm", "z"))
     A, Ds = to_dev(inp.A), to_dev(inp.D_skip)
-    if T <= 16:
+    if T <= 4:
         ry = torch.stack([ssm.state_update(st, x[:, t].contiguous(), dl[:, t].contiguous(), A,
                                            Bm[:, t].contiguous(), Cm[:, t].contiguous(), Ds,
                                            z[:, t].contiguous()) for t in range(T)], 1)
