@@ -175,3 +175,48 @@ def test_saved_segment_states(oracle_mod, L, N, dtype):
     for k in g0:
         if g0[k] is not None:
             assert torch.equal(g0[k], g1[k]), k
+
+
+def test_bwd_max_plane_size(oracle_mod):
+    """One sequence whose (L, D) planes are just under the 2 GiB the boundary
+    accepts (L = 209600, D = 5120, bf16).  dy is nonzero on sampled channels
+    only (the last one included) and dh_final is zero, so every other
+    channel's gradient is exactly zero and dB, dC sum over the sampled
+    channels: all of them are compared with the oracle over the whole
+    sequence, and the other channels' dx, ddelta, dz checked to be zero on a
+    band of channels.  Inputs drawn on the GPU (seeded); A, D, h0 from the
+    input generator."""
+    import mamba_selective_scan_ssm_amd as ssm
+    L, D, N = 209600, 5120, 16
+    assert (L + 64) * D * 2 < 2 ** 31
+    small = gen.make_scan(1, 1, D, N, dtype="bf16", seed=484)
+    _say("bwd max plane size", L, D, N)
+    g = torch.Generator(device="cuda").manual_seed(485)
+
+    def normal(shape):
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    x, z = normal((1, L, D)), normal((1, L, D))
+    dl = torch.nn.functional.softplus(
+        0.5 * torch.randn((1, L, D), generator=g, device="cuda", dtype=torch.float32) - 1.0).to(torch.bfloat16)
+    Bm, Cm = normal((1, L, N)), normal((1, L, N))
+    sel = [0, 77, 2048, 5119]
+    idx = torch.tensor(sel, device="cuda")
+    dy = torch.zeros((1, L, D), dtype=torch.bfloat16, device="cuda")
+    dy[:, :, idx] = normal((1, L, len(sel)))
+    A, Ds, h0 = to_dev(small.A), to_dev(small.D_skip), to_dev(small.h0)
+    out = ssm.scan_bwd(x, dl, A, Bm, Cm, Ds, z, h0, dy, None, want_dh0=True)
+    torch.cuda.synchronize()
+    take = lambda t: t.index_select(2, idx).float().cpu().numpy()
+    r = oracle_mod.scan_bwd(take(x), take(dl), small.A[sel], Bm.float().cpu().numpy(), Cm.float().cpu().numpy(),
+                            small.D_skip[sel], take(z), small.h0[:, sel], take(dy), None)
+    for k in ("dx", "ddelta", "dz"):
+        assert_close(to_np(out[k].index_select(2, idx)), r[k], "bf16", k)
+    assert_close(to_np(out["dh0"][:, idx]), r["dh0"], "bf16", "dh0")
+    assert_close(to_np(out["dA"][idx]), r["dA"], "bf16", "dA")
+    assert_close(to_np(out["dD"][idx]), r["dD"], "bf16", "dD")
+    assert_close(to_np(out["dB"]), r["dB"], "bf16", "dB")
+    assert_close(to_np(out["dC"]), r["dC"], "bf16", "dC")
+    band = slice(100, 164)  # channels without gradient
+    for k in ("dx", "ddelta", "dz"):
+        assert not (out[k][:, :, band] != 0).any(), k

@@ -118,3 +118,26 @@ def test_conv_rejects_bad_arguments():
         ssm.conv1d_fwd(x, to_dev(c.w), None, None, y=x)      # y on x
     with pytest.raises(ValueError):
         ssm.conv1d_fwd(torch.randn(1, 16, 128, device="cuda")[..., :64], to_dev(c.w))
+
+
+def test_conv_max_plane_size(oracle_mod):
+    """One sequence whose (L, D) planes are just under the 2 GiB the boundary
+    accepts (L = 209600, D = 5120, bf16), against the oracle on sampled
+    channels over the whole sequence (the last channel's last token sits at
+    the largest offset); the new state of those channels too.  x is drawn on
+    the GPU (seeded); w, bias and the state come from the input generator."""
+    import mamba_selective_scan_ssm_amd as ssm
+    L, D, K = 209600, 5120, 4
+    assert (L + 64) * D * 2 < 2 ** 31
+    c = gen.make_conv(1, 1, D, K, dtype="bf16", seed=482)
+    _say("conv max plane size", L, D, K)
+    g = torch.Generator(device="cuda").manual_seed(483)
+    x = torch.randn((1, L, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    sel = [0, 1, 255, 256, 3000, 5119]
+    idx = torch.tensor(sel, device="cuda")
+    ry, rs = oracle_mod.conv1d(x.index_select(2, idx).float().cpu().numpy(), c.w[sel], c.bias[sel],
+                               c.state0[:, sel], act=True)
+    y, st = ssm.conv1d_fwd(x, to_dev(c.w), to_dev(c.bias), to_dev(c.state0), activation="silu")
+    torch.cuda.synchronize()
+    assert_close(to_np(y.index_select(2, idx)), ry, "bf16", "y")
+    assert_close(to_np(st[:, idx]), rs, "bf16", "state")

@@ -276,3 +276,40 @@ def test_unaligned_bc_falls_back_bitwise():
     assert torch.equal(ya, yu) and torch.equal(ha, hu)
     with pytest.raises(ssm.SSMError):
         ssm.scan_fwd(t["x"], t["delta"], A, bu, cu, Ds, t["z"], h0, variant=3)
+
+
+def test_max_plane_size(oracle_mod):
+    """One sequence whose (L, D) planes are just under the 2 GiB the boundary
+    accepts (L = 209600, D = 5120, bf16: the largest buffer offsets the
+    kernels form), through the automatic (lane-split) and the chunked
+    schedules, against the oracle on sampled channels over the whole
+    sequence -- the last channel included, whose last token sits at the
+    largest offset.  The inputs are drawn on the GPU (seeded) with the laws of
+    the other workloads; A, D and h0 come from the input generator."""
+    import mamba_selective_scan_ssm_amd as ssm
+    L, D, N = 209600, 5120, 16
+    assert (L + 64) * D * 2 < 2 ** 31
+    small = gen.make_scan(1, 1, D, N, dtype="bf16", seed=480)
+    _say("max plane size", L, D, N)
+    g = torch.Generator(device="cuda").manual_seed(481)
+
+    def normal(shape):
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    x, z = normal((1, L, D)), normal((1, L, D))
+    dl = torch.nn.functional.softplus(
+        0.5 * torch.randn((1, L, D), generator=g, device="cuda", dtype=torch.float32) - 1.0).to(torch.bfloat16)
+    Bm, Cm = normal((1, L, N)), normal((1, L, N))
+    A, Ds, h0 = to_dev(small.A), to_dev(small.D_skip), to_dev(small.h0)
+    sel = [0, 1, 63, 64, 2047, 4000, 5118, 5119]
+    idx = torch.tensor(sel, device="cuda")
+    take = lambda t: t.index_select(2, idx).float().cpu().numpy()
+    ry, rh = oracle_mod.scan(take(x), take(dl), small.A[sel], Bm.float().cpu().numpy(),
+                             Cm.float().cpu().numpy(), small.D_skip[sel], take(z), small.h0[:, sel])
+    for variant in (0, 2):
+        _say("max plane size, variant", variant)
+        y, hf = ssm.scan_fwd(x, dl, A, Bm, Cm, Ds, z, h0, variant=variant)
+        torch.cuda.synchronize()
+        assert_close(to_np(y.index_select(2, idx)), ry, "bf16", f"y variant {variant}")
+        assert_close(to_np(hf[:, idx]), rh, "bf16", f"h_final variant {variant}")
+        del y, hf
