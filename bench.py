@@ -375,7 +375,32 @@ def bench_ssd(torch, ssm, gen, steps=10):
             "matrix_TFLOPs": flops / (mean_ms * 1e-3) / 1e12,
             "mfma_frac_bf16": flops / (mean_ms * 1e-3) / BF16_MFMA_PEAK,
             "mfma_busy_counter": e.get("mfma_busy"), "workspace_bytes": ws_n,
-            "traffic_bytes": load_traffic("ssd_fwd", "bytes_per_call")}
+            "traffic_bytes": load_traffic("ssd_fwd", "bytes_per_call"),
+            "fp32_token_path": bench_ssd_f32(torch, ssm, w)}
+
+
+def bench_ssd_f32(torch, ssm, w, steps=5):
+    """The same SSD workload in fp32 (the bf16 values widened), which runs the
+    token-by-token VALU kernel: one multiply and two FMAs per element."""
+    f = {k: torch.from_numpy(getattr(w, k).f32).cuda() for k in ("x", "dt", "Bm", "Cm")}
+    A, Ds, h0 = upload(w.A, torch), upload(w.D_skip, torch), upload(w.h0, torch)
+    y = torch.empty((w.B, w.L, w.H, w.P), dtype=torch.float32, device="cuda")
+    hf = torch.empty((w.B, w.H, w.P, w.N), dtype=torch.float32, device="cuda")
+
+    def one():
+        ssm.ssd_fwd(f["x"], f["dt"], A, f["Bm"], f["Cm"], Ds, None, h0, chunk=w.chunk, y=y, h_final=hf)
+
+    mean_ms, min_ms, _ = time_calls(one, steps, 2, torch)
+    B, L, H, P, G, N = w.B, w.L, w.H, w.P, w.G, w.N
+    elems = B * L * H * P * N
+    alg = B * L * H * P * 4 * 2 + B * L * H * 4 + 2 * B * L * G * N * 4 + 2 * B * H * P * N * 4
+    floor = SIMDS * CLOCK_HZ / 4 / 3 * 64  # 3 plain VALU ops per element, one per quad cycle
+    del f, y, hf
+    return {"workload": "ssd_mamba2 in fp32 (B=2, L=8192, H=80, P=64, N=128, G=8)",
+            "ms": mean_ms, "ms_min": min_ms, "Gelem_per_s": elems / (mean_ms * 1e-3) / 1e9,
+            "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
+            "issue_floor_Telem_s": floor / 1e12,
+            "frac_of_issue_floor": elems / (mean_ms * 1e-3) / floor}
 
 
 def bench_conv(torch, ssm, gen, steps=50):

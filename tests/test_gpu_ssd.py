@@ -128,8 +128,10 @@ def test_ssd_determinism():
 
 
 # Shapes the matrix-core kernels are not built for take the token-by-token
-# kernel (ssd_seq.hip): fp32 inputs, head dims other than 64, N not a
-# multiple of 32, other chunk lengths, x not 16-byte aligned.
+# kernels (ssd_seq.hip): fp32 inputs, head dims other than 64, N not a
+# multiple of 32, other chunk lengths, x not 16-byte aligned.  Where every
+# 64-channel block lies in one group ((H / G) P a multiple of 64) the staged
+# kernel runs, otherwise (P 16 with 3 heads per group, P 24) the plain one.
 @pytest.mark.parametrize("B,L,H,P,G,N,chunk,dtype,gate", [
     (1, 200, 4, 64, 2, 64, 64, "f32", False),     # fp32, at the fp32 bar
     (2, 300, 6, 32, 3, 128, 256, "f32", True),    # fp32, P 32, gate
@@ -138,6 +140,8 @@ def test_ssd_determinism():
     (1, 99, 5, 24, 5, 16, 256, "bf16", False),    # P 24 (workgroups span heads), N 16, G = H
     (1, 300, 4, 64, 2, 128, 100, "bf16", False),  # chunk 100
     (1, 0, 2, 32, 1, 32, 64, "f32", False),       # empty sequence
+    (1, 150, 2, 64, 1, 256, 64, "f32", True),     # N 256: 16 waves per workgroup
+    (2, 77, 4, 32, 2, 48, 64, "f32", False),      # N 48 (3 waves), ragged 16-token block
 ])
 def test_ssd_token_path(oracle_mod, B, L, H, P, G, N, chunk, dtype, gate):
     w = gen.make_ssd(B, L, H, P, G, N, chunk=chunk, dtype=dtype, seed=450 + L + P + N, gate=gate)
