@@ -204,3 +204,38 @@ def test_random_conv_update(oracle_mod, case):
         ry = oracle_mod.conv1d_update(rs, d.x.f32[t], d.w, d.bias, act=True)
         assert_close(to_np(y), ry, c["dtype"], f"y step {t}")
     assert np.array_equal(to_np(st), rs)
+
+
+def _ssd_token_case(i):
+    G = int(RNG.choice([1, 2]))
+    return dict(B=int(RNG.integers(1, 3)), L=int(RNG.choice([1, 15, 16, 17, 100, 257])), G=G,
+                H=G * int(RNG.integers(1, 5)), P=int(RNG.choice([8, 16, 24, 32, 48, 64, 96, 128])),
+                N=int(RNG.choice([1, 5, 16, 33, 64, 128, 200])), chunk=int(RNG.choice([37, 64, 100])),
+                dtype=str(RNG.choice(["f32", "bf16"])), gate=bool(RNG.integers(0, 2)),
+                softplus=bool(RNG.integers(0, 2)), seed=3700 + i)
+
+
+SSD_TOKEN_CASES = [_ssd_token_case(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("case", SSD_TOKEN_CASES,
+                         ids=lambda c: "B{B}L{L}H{H}P{P}G{G}N{N}c{chunk}{dtype}".format(**c))
+def test_random_ssd_token_path(oracle_mod, case):
+    """SSD shapes and dtypes the matrix-core kernels are not built for (any P,
+    any N, fp32, odd chunk lengths), with and without the dt bias + softplus:
+    the token-by-token kernels, staged or plain by the group alignment."""
+    import mamba_selective_scan_ssm_amd as ssm
+    c = case
+    w = gen.make_ssd(c["B"], c["L"], c["H"], c["P"], c["G"], c["N"], chunk=c["chunk"], dtype=c["dtype"],
+                     seed=c["seed"], gate=c["gate"])
+    bias = np.random.default_rng(c["seed"] + 1).normal(0.0, 0.5, c["H"]).astype(np.float32) \
+        if c["softplus"] else None
+    _say("random ssd token path", c)
+    y, hf = ssm.ssd_fwd(to_dev(w.x), to_dev(w.dt), to_dev(w.A), to_dev(w.Bm), to_dev(w.Cm), to_dev(w.D_skip),
+                        to_dev(w.z), to_dev(w.h0), chunk=c["chunk"],
+                        dt_bias=None if bias is None else to_dev(bias), dt_softplus=c["softplus"])
+    torch.cuda.synchronize()
+    ry, rh = oracle_mod.ssd(w.x.f32, w.dt.f32, w.A, w.Bm.f32, w.Cm.f32, w.D_skip,
+                            None if w.z is None else w.z.f32, w.h0, dt_bias=bias, dt_softplus=c["softplus"])
+    assert_close(to_np(y), ry, c["dtype"], "y")
+    assert_close(to_np(hf), rh, c["dtype"], "h_final")
