@@ -7,7 +7,7 @@
 // layout is chosen for the state stream: a channel's N states are N/4 lanes
 // holding four consecutive states each, so one 16-byte load per lane covers
 // the state tensor contiguously across the wave.  The y contraction over n is
-// finished with a butterfly over those N/4 lanes.  The single-token step
+// finished with DPP sums over those N/4 lanes.  The single-token step
 // gives each thread one channel of two sequences: the channel's A row (read
 // by every sequence) is loaded once for both, and all loads of the thread
 // are issued before any is used, so a wave keeps twice the state bytes in
@@ -46,6 +46,22 @@ __device__ __forceinline__ void load4(const T *p, float *v) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = to_f32(p[j]);
   }
+}
+
+// Sum over the LPC adjacent lanes of a channel, every lane getting it, with
+// DPP moves on the VALU (quad permutations, then mirrors within half rows
+// and rows) rather than lane shuffles through the LDS unit.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+template <int LPC>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  if constexpr (LPC >= 2) v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if constexpr (LPC >= 4) v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if constexpr (LPC >= 8) v += dpp_mov<0x141>(v);  // lane i <- 7 - i of the half row
+  if constexpr (LPC >= 16) v += dpp_mov<0x140>(v); // lane i <- 15 - i of the row
+  return v;
 }
 
 // LPC = lanes per channel (N / 4).  TT = tokens whose inputs are loaded
@@ -111,8 +127,7 @@ __global__ __launch_bounds__(kBlock) void state_update_kernel(StepArgs a) {
         h[j] = fmaf(dA, h[j], u * bv[k][j]);
         acc = fmaf(cv[k][j], h[j], acc);
       }
-#pragma unroll
-      for (int off = LPC / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPC);
+      acc = lane_group_sum<LPC>(acc);
       if (active && q == 0) {
         float v = acc;
         if (a.D_skip) v = fmaf(skp, xv[k], v);
@@ -181,8 +196,7 @@ __global__ __launch_bounds__(kBlock) void state_step_seq_kernel(StepArgs a) {
       h[j] = fmaf(dA, h[j], u * Bv[k][j]);
       acc = fmaf(Cv[k][j], h[j], acc);
     }
-#pragma unroll
-    for (int off = LPC / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPC);
+    acc = lane_group_sum<LPC>(acc);
     hv[k] = make_float4(h[0], h[1], h[2], h[3]);
     if (act && ok[k] && q == 0) {
       float v = acc;
