@@ -54,6 +54,7 @@ BF16_MFMA_PEAK = 2.5e15
 # ops of different waves share one quad cycle (SQ_ACTIVE_INST_VALU2); a
 # transcendental never shares one.
 SIMDS, CLOCK_HZ = 1024, 2.4e9
+CLOCK_WARMUP_S = 0.5  # untimed headline steps before the warm-up steps (clock ramp)
 # per scan element: dA = exp2(delta*A2) -> 1 mul + 1 exp; u*B -> 1 mul;
 # h = dA*h + u*B -> 1 fma; y += C*h -> 1 fma.  4 VALU + 1 transcendental.
 SCAN_VALU_PER_ELEM, SCAN_TRANS_PER_ELEM = 4, 1
@@ -141,7 +142,14 @@ def scan_alg_bytes(B, L, D, N, es, gate=True, h0=True, hf=True):
 
 
 def time_calls(fn, steps, warmup, torch):
-    """Mean time of `fn` (ms) with HIP events on the current stream, bracketed by syncs."""
+    """Mean and min time of `fn` (ms) with HIP events on the current stream,
+    bracketed by syncs, and the wall-clock time per call."""
+    mean, mn, _, wall = time_calls_full(fn, steps, warmup, torch)
+    return mean, mn, wall
+
+
+def time_calls_full(fn, steps, warmup, torch):
+    """time_calls with the median too: (mean, min, median, wall) in ms."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -157,7 +165,7 @@ def time_calls(fn, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     per = [a.elapsed_time(b) for a, b in ev]
-    return float(np.mean(per)), float(np.min(per)), wall
+    return float(np.mean(per)), float(np.min(per)), float(np.median(per)), wall
 
 
 def time_graph(fn, calls, replays, torch):
@@ -358,7 +366,7 @@ def bench_ssd(torch, ssm, gen, steps=10):
         one()
     except Exception as e:  # not built for this configuration
         return {"workload": "ssd_mamba2_bf16", "error": str(e)}
-    mean_ms, min_ms, wall_ms = time_calls(one, steps, 10, torch)
+    mean_ms, min_ms, med_ms, wall_ms = time_calls_full(one, steps, 10, torch)
     B, L, H, P, G, N = w.B, w.L, w.H, w.P, w.G, w.N
     alg = (B * L * H * P * 2 * 2 + B * L * H * 2 + 2 * B * L * G * N * 2 + H * 8
            + 2 * B * H * P * N * 4)
@@ -368,7 +376,8 @@ def bench_ssd(torch, ssm, gen, steps=10):
     flops = 2.0 * B * L * (Q * G * N / 2 + Q * H * P / 2 + 2 * H * P * N)
     e = load_entry("ssd_fwd") or {}
     return {"workload": "ssd_mamba2_bf16 (B=2, L=8192, H=80, P=64, N=128, G=8, chunk=256)",
-            "ms": mean_ms, "Gelem_per_s": B * L * H * P * N / (mean_ms * 1e-3) / 1e9,
+            "ms": mean_ms, "ms_min": min_ms, "ms_median": med_ms,
+            "Gelem_per_s": B * L * H * P * N / (mean_ms * 1e-3) / 1e9,
             "alg_bytes": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
             "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "causal_matrix_GFLOP": flops / 1e9,
@@ -403,6 +412,26 @@ def bench_ssd_f32(torch, ssm, w, steps=5):
             "frac_of_issue_floor": elems / (mean_ms * 1e-3) / floor}
 
 
+def bench_ppl_context(torch, ssm, gen):
+    """Context shape, not a target: the perplexity run on the llama.cpp page
+    as one scan call (4 sequences of 512 tokens, d_inner 1536, d_state 16,
+    fp32 as ggml computes it), timed as graph replays."""
+    inp = gen.make_scan(4, 512, 1536, 16, dtype="f32", seed=1100)
+    t, A, Ds, h0 = scan_inputs(inp, torch)
+    y = torch.empty((4, 512, 1536), dtype=torch.float32, device="cuda")
+    hf = torch.empty((4, 1536, 16), dtype=torch.float32, device="cuda")
+
+    def one():
+        ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, y=y, h_final=hf)
+
+    ms, min_ms = time_graph(one, 16, 8, torch)
+    elems = 4 * 512 * 1536 * 16
+    alg = scan_alg_bytes(4, 512, 1536, 16, 4)
+    return {"workload": "ppl_ctx (B=4, L=512, D=1536, N=16, fp32, gate on)", "kernel_ms": ms,
+            "kernel_ms_min": min_ms, "Gelem_per_s": elems / (ms * 1e-3) / 1e9,
+            "hbm_GBs": alg / (ms * 1e-3) / 1e9, "tokens_per_s": 4 * 512 / (ms * 1e-3)}
+
+
 def bench_conv(torch, ssm, gen, steps=50):
     """Width-4 causal convolution ahead of the 2.8B-shaped scan (prefill) and
     its decode step; both HBM-bound."""
@@ -415,10 +444,11 @@ def bench_conv(torch, ssm, gen, steps=50):
     def one():
         ssm.conv1d_fwd(x, w, bias, s0, y=y, state_out=st)
 
-    mean_ms, min_ms, _ = time_calls(one, steps, 10, torch)
+    mean_ms, min_ms, med_ms, _ = time_calls_full(one, steps, 10, torch)
     alg = B * L * D * 2 * 2 + D * K * 4 + D * 4 + 2 * B * D * (K - 1) * 4
     out = {"workload": "conv_mamba2p8b_bf16 (B=8, L=4096, D=5120, K=4, bf16, SiLU)",
-           "ms": mean_ms, "alg_bytes": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
+           "ms": mean_ms, "ms_min": min_ms, "ms_median": med_ms,
+           "alg_bytes": alg, "hbm_GBs": alg / (mean_ms * 1e-3) / 1e9,
            "hbm_frac": alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "traffic_bytes": load_traffic("conv1d_fwd", "bytes_per_call")}
     d = gen.make_workload("conv_decode_256x5120_bf16")
@@ -461,7 +491,7 @@ def bench_bwd(torch, ssm, gen, steps=10):
     def one():
         ssm.scan_bwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, dy, dhf, workspace=ws)
 
-    ms, min_ms, wall = time_calls(one, steps, 3, torch)
+    ms, min_ms, med_ms, wall = time_calls_full(one, steps, 3, torch)
     elems = B * L * D * N
     io = B * L * D * 2 * 7 + B * L * N * (2 * 2 + 4 * 2) + D * N * 4 * 2 + D * 4 * 2 + B * D * N * 4 * 3
     rate = elems / (ms * 1e-3)
@@ -480,7 +510,7 @@ def bench_bwd(torch, ssm, gen, steps=10):
 
     bms, _, _ = time_calls(bwd_saved, steps, 3, torch)
     return {"workload": "mamba2p8b_prefill_bf16 backward (B=8, L=4096, D=5120, N=16, bf16, all gradients)",
-            "ms": ms, "ms_min": min_ms, "Gelem_per_s": rate / 1e9, "alg_bytes": io,
+            "ms": ms, "ms_min": min_ms, "ms_median": med_ms, "Gelem_per_s": rate / 1e9, "alg_bytes": io,
             "hbm_GBs": io / (ms * 1e-3) / 1e9, "hbm_frac": io / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "alu_frac": rate / BWD_ELEM_PEAK, "alu_peak_Telem_s": BWD_ELEM_PEAK / 1e12,
             "workspace_bytes": ws.numel(), "traffic_bytes": load_traffic("scan_bwd", "bytes_per_call"),
@@ -849,7 +879,7 @@ def main():
         rows = {"tiny_fp32": bench_tiny(torch, ssm, gen), "mamba130m_fp32": bench_130m(torch, ssm, gen),
                 "decode": bench_decode(torch, ssm, gen), "ssd": bench_ssd(torch, ssm, gen, steps=20),
                 "conv": bench_conv(torch, ssm, gen), "pool_decode": bench_pool_decode(torch, ssm, gen),
-                "bwd": bench_bwd(torch, ssm, gen)}
+                "bwd": bench_bwd(torch, ssm, gen), "ppl_context": bench_ppl_context(torch, ssm, gen)}
         for row in rows.values():  # HBM rates also as a fraction of the copy
             for r in [row] + [v for v in row.values() if isinstance(v, dict)]:
                 if "hbm_GBs" in r:
@@ -869,7 +899,17 @@ def main():
         ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, y=y, h_final=hf,
                      workspace=ws)
 
-    mean_ms, min_ms, wall_ms = time_calls(step, args.steps, args.warmup, torch)
+    # The GPU clock ramps up under sustained load (from ~1.9 to ~2.37 GHz over
+    # the first few dozen launches after an idle spell, such as the host-side
+    # input generation above; profiles/scan_lanesplit_clock_*.md): run the
+    # step untimed for CLOCK_WARMUP_S first, so the W warm-up and K timed
+    # steps see the steady clock whatever W is.
+    t_end = time.perf_counter() + CLOCK_WARMUP_S
+    while time.perf_counter() < t_end:
+        for _ in range(16):
+            step()
+        torch.cuda.synchronize()
+    mean_ms, min_ms, med_ms, wall_ms = time_calls_full(step, args.steps, args.warmup, torch)
     elems = B * L * D * N
     value = elems / (wall_ms * 1e-3) / 1e9
     alg = scan_alg_bytes(B, L, D, N, 2)
@@ -899,11 +939,13 @@ def main():
         "alg_bytes_per_launch": alg,
         "kernel_ms": mean_ms,
         "kernel_ms_min": min_ms,
+        "kernel_ms_median": med_ms,
         "alu": alu,
     }
     out = {
         "metric": "selective-scan Gelem/s (B*L*D*N) + achieved HBM GB/s vs peak on 1 MI355X",
         "value": value, "unit": "Gelem/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "clock_warmup_s": CLOCK_WARMUP_S,
         "ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "mamba-2.8B-shaped prefill selective scan", "B": B, "L": L, "D": D,
