@@ -23,7 +23,7 @@ namespace {
 
 constexpr int kConvThreads = 256;   // channels per workgroup
 constexpr int kConvSeg = 64;        // tokens per segment
-constexpr int kConvBatch = 8;       // token rows loaded ahead
+constexpr int kConvBatch = 16;      // token rows loaded ahead
 
 template <typename T>
 __device__ __forceinline__ float conv_ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
