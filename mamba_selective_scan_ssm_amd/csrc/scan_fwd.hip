@@ -671,7 +671,12 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
 // Carry pass: one thread per (b, d, n); walks the segments in order,
 // replacing each segment's summary state with the state entering it, and
 // writes h_final.  carry <- a_seg * carry + h_seg composes the segment's
-// affine map after the carry (seed (1, h0)).
+// affine map after the carry (seed (1, h0)).  The summaries of kCarryBatch
+// segments are loaded before any carry is stored, so that many loads are in
+// flight per thread (a load of segment s + 1 would otherwise wait for the
+// store to segment s).
+constexpr int kCarryBatch = 8;
+
 __global__ __launch_bounds__(256) void scan_carry_kernel(int64_t B, int64_t D, int64_t N,
                                                           int64_t nseg, const float *h0,
                                                           const float *seg_a, float *seg_h,
@@ -682,12 +687,23 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(int64_t B, int64_t D, i
   const int64_t b = i / DN;
   const int64_t dn = i - b * DN;
   float carry = h0 ? h0[i] : 0.f;
-  for (int64_t s = 0; s < nseg; ++s) {
-    const int64_t k = (b * nseg + s) * DN + dn;
-    const float av = seg_a[k];
-    const float hv = seg_h[k];
-    seg_h[k] = carry;
-    carry = fmaf(av, carry, hv);
+  for (int64_t s0 = 0; s0 < nseg; s0 += kCarryBatch) {
+    float av[kCarryBatch], hv[kCarryBatch];
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k) {
+      if (s0 + k < nseg) {
+        const int64_t idx = (b * nseg + s0 + k) * DN + dn;
+        av[k] = seg_a[idx];
+        hv[k] = seg_h[idx];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kCarryBatch; ++k) {
+      if (s0 + k < nseg) {
+        seg_h[(b * nseg + s0 + k) * DN + dn] = carry;
+        carry = fmaf(av[k], carry, hv[k]);
+      }
+    }
   }
   if (h_final) h_final[i] = carry;
 }
