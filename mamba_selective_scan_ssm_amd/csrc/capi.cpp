@@ -63,7 +63,8 @@ bool dsoft_of(const ssm_delta_opts *o) { return o && o->softplus == 1; }
 // Variant choice: a function of (L, D, N) only, so a sequence's result does
 // not depend on the batch it is in.  Sequential when one sequence already
 // brings enough 64-channel waves or L is short; otherwise chunked with
-// segments sized so one sequence yields ~2048 waves.
+// segments sized so one sequence yields ~2048 waves, a multiple of 32 tokens
+// (whole load cycles of the lane-split kernel).
 struct Plan {
   int variant;  // 1 sequential (waves split N), 2 chunked, 3 sequential (lanes split N)
   int64_t seg_len;
@@ -78,7 +79,7 @@ Plan plan_scan(int64_t L, int64_t D, const ssm_tuning *t) {
     int64_t nseg = 512 / (wps > 0 ? wps : 1);  // ~512 tiles x segments per sequence
     if (nseg < 1) nseg = 1;
     seg = (L + nseg - 1) / nseg;
-    seg = (seg + 7) / 8 * 8;
+    seg = seg / 32 * 32;
     if (seg < 64) seg = 64;
   }
   if (variant == 2 && seg <= 0) seg = 64;

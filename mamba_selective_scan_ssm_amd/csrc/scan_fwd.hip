@@ -381,8 +381,15 @@ __device__ __forceinline__ float word_elem(const uint32_t *w, int e) {
 // otherwise.  A block of this kernel is exactly one such segment.
 // STEP: delta takes the per-channel bias and/or softplus; without it delta is
 // used as loaded (rows past L load as 0, which is what they must stage).
-template <typename T, int LPC, int SPL, bool HAS_Z, bool CK, bool STEP, int CYC = 4>
-__global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
+// MODE (grid y = segment of seg_len tokens, as the split kernel's modes):
+// kFull runs all of L from h0; kSummary runs its segment from 0 and writes
+// seg_a = exp(A sum delta) and seg_h = the state reached, without outputs;
+// kOutput runs its segment from seg_h (the state entering it) and writes y.
+// seg_len is a multiple of the 32-token load cycle (TB * CYC), so only the
+// last segment has a partial cycle and its rows past L lie past the plane.
+template <typename T, int LPC, int SPL, bool HAS_Z, bool CK, bool STEP, int CYC = 4, int MODE = kFull>
+__global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, int64_t seg_len, float *seg_a,
+                                                                   float *seg_h) {
   constexpr int TB = 8;                 // tokens per block
   constexpr int kCPW = kWave / LPC;     // channels per wave
   constexpr int kN = LPC * SPL;         // = N
@@ -396,6 +403,8 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   static_assert(LPC == 1 || LPC == 2 || LPC == 4, "LPC must be 1, 2 or 4");
   static_assert(SPL % kV == 0, "a loader lane's values must fall in one lane's slice");
   static_assert(kPairs * 64 * 2 == TB * kCPW, "pair slots must tile the block");
+  static_assert(!CK || MODE == kFull, "segment states are saved by full runs only");
+  constexpr bool kY = MODE != kSummary;
 
   // per wave and block of the cycle: B/C [token][q][B|C][SPL] and
   // (delta, u) [token][channel]; per wave: partial sums [token][channel *
@@ -413,20 +422,28 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   const int64_t b = blockIdx.z;
   int64_t hrow;  // state row of sequence b
   if (!scan_state_row(a, b, hrow)) return;
+  const int64_t seg = blockIdx.y, nseg = gridDim.y;
+  const int64_t tok0 = seg * seg_len;                                // first token of the segment
+  const int64_t Ls = (L - tok0) < seg_len ? (L - tok0) : seg_len;    // its tokens
+  const uint32_t tok0_u = static_cast<uint32_t>(tok0);
 
   // compute role: channel c, state slice q
   const int c = lane / LPC, q = lane % LPC;
   const int64_t dc = (d0 + c < D) ? d0 + c : D - 1;
+  const int64_t ws_row = ((b * nseg + seg) * D + dc) * kN + q * SPL;  // segment summaries
   float A2[SPL], h[SPL];
   {
     const float *Ap = a.A + dc * kN + q * SPL;
-    const float *hp = a.h0 ? a.h0 + (hrow * D + dc) * kN + q * SPL : nullptr;
+    const float *hp = MODE == kOutput ? seg_h + ws_row
+                      : (MODE == kFull && a.h0) ? a.h0 + (hrow * D + dc) * kN + q * SPL
+                                                : nullptr;
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
       A2[s] = Ap[s] * kLog2e;
       h[s] = hp ? hp[s] : 0.f;
     }
   }
+  float dsum = 0.f;  // sum of the segment's delta (kSummary)
 
   // load/finish role: slot m covers token row rr[m] of a block and the
   // channel pair pp[m] (wave-local channels 2pp, 2pp+1; D is even, so a pair
@@ -476,7 +493,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   const uint32_t ld_vo = static_cast<uint32_t>(kV * ld) * kES;
 
   const uint32_t ntok = static_cast<uint32_t>(L);
-  const int64_t nblk = (L + TB - 1) / TB;
+  const int64_t nblk = (Ls + TB - 1) / TB;
   const int64_t ncyc = (nblk + kCyc - 1) / kCyc;
 
   // segment states: the state after each block of a cycle, stored with the
@@ -509,16 +526,16 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
 #pragma unroll
     for (int u = 0; u < kCyc; ++u) {
       const uint32_t blk = static_cast<uint32_t>(cyc * kCyc + u);
-      const uint32_t so = __builtin_amdgcn_readfirstlane(blk * TB * row_bytes);
+      const uint32_t so = __builtin_amdgcn_readfirstlane((tok0_u + blk * TB) * row_bytes);
 #pragma unroll
       for (int m = 0; m < kPairs; ++m) {
         load_words<2 * kES>(rx, vo[m], so, w.x[u][m]);
         load_words<2 * kES>(rd, vo[m], so, w.d[u][m]);
-        if (HAS_Z) load_words<2 * kES>(rz, vo[m], so, w.z[u][m]);
+        if (HAS_Z && kY) load_words<2 * kES>(rz, vo[m], so, w.z[u][m]);
       }
       // buffer resources must be wave-uniform: every lane loads its slice
       // of both B and C and converts one of them when the cycle is staged
-      const uint32_t bso = __builtin_amdgcn_readfirstlane(blk * TB * kN * kES);
+      const uint32_t bso = __builtin_amdgcn_readfirstlane((tok0_u + blk * TB) * kN * kES);
       load_words<kV * kES>(rb, ld_vo, bso, w.b[u]);
       load_words<kV * kES>(rc, ld_vo, bso, w.c[u]);
     }
@@ -529,7 +546,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   auto stage = [&](const Raw &w, int64_t cyc) {
 #pragma unroll
     for (int u = 0; u < kCyc; ++u) {
-      const uint32_t tb = static_cast<uint32_t>(cyc * kCyc + u) * TB;
+      const uint32_t tb = tok0_u + static_cast<uint32_t>(cyc * kCyc + u) * TB;
 #pragma unroll
       for (int m = 0; m < kPairs; ++m) {
         float du[4];
@@ -568,9 +585,10 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
       for (int s = 0; s < SPL; ++s) {
         const float dA = fast_exp2(du.x * A2[s]);
         h[s] = fmaf(dA, h[s], du.y * Bv[s]);
-        acc = fmaf(Cv[s], h[s], acc);
+        if (kY) acc = fmaf(Cv[s], h[s], acc);
       }
-      s_y[wave][j][c * LPC + q] = acc;
+      if (kY) s_y[wave][j][c * LPC + q] = acc;
+      if (MODE == kSummary) dsum += du.x;
     }
     if constexpr (CK) {
 #pragma unroll
@@ -606,7 +624,8 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   auto store_cycle = [&](int64_t cyc) {
 #pragma unroll
     for (int u = 0; u < kCyc; ++u) {
-      const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(cyc * kCyc + u) * TB * row_bytes);
+      const uint32_t so =
+          __builtin_amdgcn_readfirstlane((tok0_u + static_cast<uint32_t>(cyc * kCyc + u) * TB) * row_bytes);
 #pragma unroll
       for (int m = 0; m < kPairs; ++m) {
         const int vov = static_cast<int>(vo_st[m]), sov = static_cast<int>(so);
@@ -635,7 +654,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
   // y stores fall past the plane and the state is already final)
   auto cycle = [&](Raw &cur, Raw &nxt, int64_t cyc, int nb) {
     stage(cur, cyc);
-    if (cyc > 0) store_cycle(cyc - 1);
+    if (kY && cyc > 0) store_cycle(cyc - 1);
     issue(nxt, cyc + 1);
     wave_sync_lds();
 #pragma unroll
@@ -643,8 +662,10 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
       if (u < nb) {
         run_block(u);
         wave_sync_lds();
-        finish_block(cur, u);
-        wave_sync_lds();
+        if (kY) {
+          finish_block(cur, u);
+          wave_sync_lds();
+        }
       }
     }
   };
@@ -660,9 +681,17 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a) {
     cycle(r0, r1, cyc, static_cast<int>(nblk - cyc * kCyc));
     ++cyc;
   }
-  if (ncyc > 0) store_cycle(cyc - 1);
+  if (kY && ncyc > 0) store_cycle(cyc - 1);
 
-  if (d0 + c >= D || a.h_final == nullptr) return;
+  if (d0 + c >= D) return;
+  if (MODE == kSummary) {
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) {
+      seg_a[ws_row + s] = fast_exp2(A2[s] * dsum);
+      seg_h[ws_row + s] = h[s];
+    }
+  }
+  if (MODE != kFull || a.h_final == nullptr) return;
   float *hf = a.h_final + (hrow * D + dc) * kN + q * SPL;
 #pragma unroll
   for (int s = 0; s < SPL; ++s) hf[s] = h[s];
@@ -849,21 +878,21 @@ void launch_lanesplit_s(const ScanArgs &a, dim3 grid, hipStream_t s) {
     // the registers of the input sets, so more waves stay resident to cover
     // the latency of each wave's state load and store
     if (a.z)
-      scan_lanesplit_kernel<T, LPC, SPL, true, false, STEP, 2><<<grid, kWave * 4, 0, s>>>(a);
+      scan_lanesplit_kernel<T, LPC, SPL, true, false, STEP, 2><<<grid, kWave * 4, 0, s>>>(a, a.L, nullptr, nullptr);
     else
-      scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP, 2><<<grid, kWave * 4, 0, s>>>(a);
+      scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP, 2><<<grid, kWave * 4, 0, s>>>(a, a.L, nullptr, nullptr);
     return;
   }
   if (a.h_ckpt) {
     if (a.z)
-      scan_lanesplit_kernel<T, LPC, SPL, true, true, STEP><<<grid, kWave * 4, 0, s>>>(a);
+      scan_lanesplit_kernel<T, LPC, SPL, true, true, STEP><<<grid, kWave * 4, 0, s>>>(a, a.L, nullptr, nullptr);
     else
-      scan_lanesplit_kernel<T, LPC, SPL, false, true, STEP><<<grid, kWave * 4, 0, s>>>(a);
+      scan_lanesplit_kernel<T, LPC, SPL, false, true, STEP><<<grid, kWave * 4, 0, s>>>(a, a.L, nullptr, nullptr);
   } else {
     if (a.z)
-      scan_lanesplit_kernel<T, LPC, SPL, true, false, STEP><<<grid, kWave * 4, 0, s>>>(a);
+      scan_lanesplit_kernel<T, LPC, SPL, true, false, STEP><<<grid, kWave * 4, 0, s>>>(a, a.L, nullptr, nullptr);
     else
-      scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP><<<grid, kWave * 4, 0, s>>>(a);
+      scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP><<<grid, kWave * 4, 0, s>>>(a, a.L, nullptr, nullptr);
   }
 }
 
@@ -876,6 +905,51 @@ hipError_t launch_lanesplit_t(const ScanArgs &a, hipStream_t s) {
   else
     launch_lanesplit_s<T, LPC, SPL, false>(a, grid, s);
   return hipGetLastError();
+}
+
+// Chunked schedule on the lane-split kernel: segment summaries, the carry
+// pass, then each segment's outputs from the state entering it.
+template <typename T, int LPC, int SPL, bool STEP>
+void launch_lanesplit_chunked_s(const ScanArgs &a, int64_t seg_len, float *seg_a, float *seg_h,
+                                hipStream_t s) {
+  constexpr int kChPerWG = 4 * (kWave / LPC);
+  const int64_t nseg = (a.L + seg_len - 1) / seg_len;
+  dim3 grid(static_cast<unsigned>((a.D + kChPerWG - 1) / kChPerWG), static_cast<unsigned>(nseg),
+            static_cast<unsigned>(a.B));
+  scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP, 4, kSummary><<<grid, kWave * 4, 0, s>>>(a, seg_len, seg_a,
+                                                                                                 seg_h);
+  const int64_t total = a.B * a.D * a.N;
+  scan_carry_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, s>>>(a.B, a.D, a.N, nseg, a.h0, seg_a,
+                                                                              seg_h, a.h_final);
+  if (a.z)
+    scan_lanesplit_kernel<T, LPC, SPL, true, false, STEP, 4, kOutput><<<grid, kWave * 4, 0, s>>>(a, seg_len, seg_a,
+                                                                                               seg_h);
+  else
+    scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP, 4, kOutput><<<grid, kWave * 4, 0, s>>>(a, seg_len, seg_a,
+                                                                                                seg_h);
+}
+
+template <typename T, int LPC, int SPL>
+hipError_t launch_lanesplit_chunked_t(const ScanArgs &a, int64_t seg_len, float *seg_a, float *seg_h,
+                                      hipStream_t s) {
+  if (a.delta_bias != nullptr || a.delta_softplus)
+    launch_lanesplit_chunked_s<T, LPC, SPL, true>(a, seg_len, seg_a, seg_h, s);
+  else
+    launch_lanesplit_chunked_s<T, LPC, SPL, false>(a, seg_len, seg_a, seg_h, s);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_lanesplit_chunked(const ScanArgs &a, int64_t seg_len, float *seg_a, float *seg_h,
+                                      hipStream_t s) {
+  switch (a.N) {
+    case 4: return launch_lanesplit_chunked_t<T, 1, 4>(a, seg_len, seg_a, seg_h, s);
+    case 8: return launch_lanesplit_chunked_t<T, 2, 4>(a, seg_len, seg_a, seg_h, s);
+    case 16: return launch_lanesplit_chunked_t<T, 4, 4>(a, seg_len, seg_a, seg_h, s);
+    case 32: return launch_lanesplit_chunked_t<T, 4, 8>(a, seg_len, seg_a, seg_h, s);
+    case 64: return launch_lanesplit_chunked_t<T, 4, 16>(a, seg_len, seg_a, seg_h, s);
+    default: return hipErrorNotSupported;
+  }
 }
 
 template <typename T>
@@ -941,6 +1015,12 @@ hipError_t launch_scan_chunked(const ScanArgs &a, int spl_req, int64_t seg_len, 
   const int64_t nseg = (a.L + seg_len - 1) / seg_len;
   float *seg_a = ws;
   float *seg_h = ws + a.B * nseg * a.D * a.N;
+  // the lane-split kernel takes segments of whole 32-token load cycles
+  if (spl_req == 0 && seg_len % 32 == 0 && a.slots == nullptr && a.h_ckpt == nullptr &&
+      scan_lanesplit_supported(a)) {
+    if (a.dt == DType::BF16) return dispatch_lanesplit_chunked<bf16_t>(a, seg_len, seg_a, seg_h, s);
+    return dispatch_lanesplit_chunked<float>(a, seg_len, seg_a, seg_h, s);
+  }
   if (a.dt == DType::BF16) return dispatch_split<bf16_t>(a, spl_req, seg_len, seg_a, seg_h, s);
   return dispatch_split<float>(a, spl_req, seg_len, seg_a, seg_h, s);
 }

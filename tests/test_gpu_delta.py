@@ -23,7 +23,7 @@ def _raw_and_bias(inp_delta, n, seed):
     return raw, bias
 
 
-@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 16), (3, 0)])
+@pytest.mark.parametrize("variant,chunk", [(0, 0), (1, 0), (2, 16), (2, 64), (3, 0)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("softplus", [False, True])
 def test_scan_delta_transform(oracle_mod, variant, chunk, dtype, softplus):

@@ -255,6 +255,48 @@ def test_lanesplit_matches_wavesplit_bitwise(B, L, D, N, dtype, gate):
     assert torch.equal(y1, y3) and torch.equal(h1, h3)
 
 
+# Chunked schedule with segments of whole 32-token cycles: its summary and
+# output passes run on the lane-split kernel (N in LANESPLIT_N, aligned rows).
+CHUNKED_LANESPLIT_SHAPES = [
+    (1, 1000, 192, 16, "f32", 96),    # ragged last segment
+    (2, 333, 130, 8, "bf16", 32),     # D not a multiple of 64
+    (1, 257, 64, 4, "f32", 64),       # one token in the last segment
+    (1, 300, 96, 32, "bf16", 128),
+    (1, 200, 64, 64, "f32", 32),
+    (3, 96, 128, 16, "bf16", 96),     # a single segment
+]
+
+
+@pytest.mark.parametrize("B,L,D,N,dtype,chunk", CHUNKED_LANESPLIT_SHAPES)
+@pytest.mark.parametrize("gate,h0", [(True, True), (False, False)])
+def test_chunked_lanesplit_shapes(oracle_mod, B, L, D, N, dtype, chunk, gate, h0):
+    inp = gen.make_scan(B, L, D, N, dtype=dtype, seed=700 + L + N + chunk)
+    _say("chunked lane-split", B, L, D, N, dtype, chunk, gate, h0)
+    y, hf = run_gpu(inp, gate, h0, variant=2, chunk_len=chunk)
+    ry, rh = run_oracle(oracle_mod, inp, gate, h0)
+    assert_close(y, ry, dtype, "y")
+    assert_close(hf, rh, dtype, "h_final")
+
+
+@pytest.mark.parametrize("B,L,D,N,dtype,chunk", CHUNKED_LANESPLIT_SHAPES)
+def test_chunked_lanesplit_matches_wavesplit_bitwise(B, L, D, N, dtype, chunk):
+    """The chunked schedule gives the same bits whether its passes run on the
+    lane-split kernel (automatic) or on the wave-split kernel (asked for with
+    an explicit states-per-lane): both do the same fp32 operations in the
+    same order, segment by segment."""
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(B, L, D, N, dtype=dtype, seed=750 + L + N)
+    _say("chunked lane-split vs wave-split", B, L, D, N, dtype, chunk)
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds, h0 = to_dev(inp.A), to_dev(inp.D_skip), to_dev(inp.h0)
+    spl = 4 if N <= 16 else N // 4  # the lane-split kernel's states per lane
+    y1, h1 = ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, variant=2,
+                          chunk_len=chunk)
+    y2, h2 = ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, t["z"], h0, variant=2,
+                          chunk_len=chunk, states_per_lane=spl)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
 def test_unaligned_bc_falls_back_bitwise():
     """B/C views that are not 16-byte aligned take the wave-split kernel and
     give the same bits as aligned copies (which take the lane-split one)."""
