@@ -611,8 +611,8 @@ PROFILE_ENTRIES = {
 # kernels of one call under the automatic schedule, where a profiled run
 # also times other schedules (short names, prefix match); default: all
 CALL_KERNELS = {
-    "scan_fwd_130m": ["scan_split_kernel<float, 4, 4, 8, 1,", "scan_carry_kernel",
-                      "scan_split_kernel<float, 4, 4, 8, 2,"],
+    "scan_fwd_130m": ["scan_lanesplit_kernel<float, 4, 4, false, false, false, 4, 1>", "scan_carry_kernel",
+                      "scan_lanesplit_kernel<float, 4, 4, true, false, false, 4, 2>"],
 }
 
 
