@@ -537,7 +537,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
       // of both B and C and converts one of them when the cycle is staged
       const uint32_t bso = __builtin_amdgcn_readfirstlane((tok0_u + blk * TB) * kN * kES);
       load_words<kV * kES>(rb, ld_vo, bso, w.b[u]);
-      load_words<kV * kES>(rc, ld_vo, bso, w.c[u]);
+      if (kY) load_words<kV * kES>(rc, ld_vo, bso, w.c[u]);  // (kSummary: no outputs, no C)
     }
   };
 
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
       }
       uint32_t bc[kWords];
 #pragma unroll
-      for (int k = 0; k < kWords; ++k) bc[k] = ld_c ? w.c[u][k] : w.b[u][k];
+      for (int k = 0; k < kWords; ++k) bc[k] = (kY && ld_c) ? w.c[u][k] : w.b[u][k];
       float *dst = &s_bc[wave][u][ld_j][ld_n / SPL][ld_c ? 1 : 0][ld_n % SPL];
 #pragma unroll
       for (int e = 0; e < kV; ++e) dst[e] = word_elem<T>(bc, e);
@@ -705,8 +705,9 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
 // flight per thread (a load of segment s + 1 would otherwise wait for the
 // store to segment s).
 constexpr int kCarryBatch = 8;
+constexpr int kCarryThreads = 256;
 
-__global__ __launch_bounds__(256) void scan_carry_kernel(int64_t B, int64_t D, int64_t N,
+__global__ __launch_bounds__(kCarryThreads) void scan_carry_kernel(int64_t B, int64_t D, int64_t N,
                                                           int64_t nseg, const float *h0,
                                                           const float *seg_a, float *seg_h,
                                                           float *h_final) {
@@ -847,8 +848,8 @@ hipError_t launch_split_t(const ScanArgs &a, int64_t seg_len, float *seg_a, floa
   dim3 grid(tiles, static_cast<unsigned>(nseg), static_cast<unsigned>(a.B));
   scan_split_kernel<T, SPL, W, TB, kSummary, false><<<grid, kWave * W, 0, s>>>(a, seg_len, seg_a, seg_h);
   const int64_t total = a.B * a.D * a.N;
-  scan_carry_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, s>>>(
-      a.B, a.D, a.N, nseg, a.h0, seg_a, seg_h, a.h_final);
+  const unsigned carry_grid = static_cast<unsigned>((total + kCarryThreads - 1) / kCarryThreads);
+  scan_carry_kernel<<<carry_grid, kCarryThreads, 0, s>>>(a.B, a.D, a.N, nseg, a.h0, seg_a, seg_h, a.h_final);
   if (a.z)
     scan_split_kernel<T, SPL, W, TB, kOutput, true><<<grid, kWave * W, 0, s>>>(a, seg_len, seg_a, seg_h);
   else
@@ -919,8 +920,8 @@ void launch_lanesplit_chunked_s(const ScanArgs &a, int64_t seg_len, float *seg_a
   scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP, 4, kSummary><<<grid, kWave * 4, 0, s>>>(a, seg_len, seg_a,
                                                                                                  seg_h);
   const int64_t total = a.B * a.D * a.N;
-  scan_carry_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, s>>>(a.B, a.D, a.N, nseg, a.h0, seg_a,
-                                                                              seg_h, a.h_final);
+  const unsigned carry_grid = static_cast<unsigned>((total + kCarryThreads - 1) / kCarryThreads);
+  scan_carry_kernel<<<carry_grid, kCarryThreads, 0, s>>>(a.B, a.D, a.N, nseg, a.h0, seg_a, seg_h, a.h_final);
   if (a.z)
     scan_lanesplit_kernel<T, LPC, SPL, true, false, STEP, 4, kOutput><<<grid, kWave * 4, 0, s>>>(a, seg_len, seg_a,
                                                                                                seg_h);
