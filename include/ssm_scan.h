@@ -82,11 +82,16 @@ typedef struct {
                           variant 3 where it applies, else 1, when L <= 256
                           or D >= 4096; variant 2 otherwise. */
     int32_t chunk_len; /* variant 2: tokens per segment (multiple of 8,
-                          >= 8); 0 = automatic */
+                          >= 8); 0 = automatic (a multiple of 32).  With a
+                          multiple of 32, states_per_lane 0 and the
+                          conditions of variant 3, the segment passes run
+                          on the lane-split kernel of variant 3, else on the
+                          workgroup kernel of variant 1; the two give
+                          bitwise the same result. */
     int32_t states_per_lane; /* 0 = automatic; else 2, 4, 8 or 16: each lane
                           keeps this many of a channel's N states and
                           ceil(N / states_per_lane) waves (1, 2, 4 or 8)
-                          share a channel tile */
+                          share a channel tile (the workgroup kernel) */
     int32_t reserved[5]; /* must be zero */
 } ssm_tuning;
 
