@@ -41,7 +41,7 @@ bool tuning_ok(const ssm_tuning *t) {
   if (!t) return true;
   for (int i = 0; i < 5; ++i)
     if (t->reserved[i] != 0) return false;
-  if (t->variant < 0 || t->variant > 3) return false;
+  if (t->variant < 0 || t->variant > 4) return false;
   if (t->chunk_len < 0 || (t->chunk_len != 0 && (t->chunk_len < 8 || t->chunk_len % 8 != 0)))
     return false;
   const int s = t->states_per_lane;
@@ -66,7 +66,8 @@ bool dsoft_of(const ssm_delta_opts *o) { return o && o->softplus == 1; }
 // segments sized so one sequence yields ~2048 waves, a multiple of 32 tokens
 // (whole load cycles of the lane-split kernel).
 struct Plan {
-  int variant;  // 1 sequential (waves split N), 2 chunked, 3 sequential (lanes split N)
+  int variant;  // 1 sequential (waves split N), 2 chunked, 3 sequential (lanes split N),
+                // 4 as 3 with every wave's tokens cut in two
   int64_t seg_len;
 };
 
@@ -87,6 +88,35 @@ Plan plan_scan(int64_t L, int64_t D, const ssm_tuning *t) {
 }
 
 ssm_status hip_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
+
+// SIMDs of the current device (4 per CU; cached per device; 0 if the query
+// fails, where the halved schedule is then not chosen automatically).
+int64_t device_simds() {
+  static int64_t cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 0;
+  if (dev < 64) cached[dev] = 4 * static_cast<int64_t>(cus);
+  return 4 * static_cast<int64_t>(cus);
+}
+
+// Whether this call takes the halved lane-split schedule (variant 4): asked
+// for, or chosen automatically where the channel-sequential schedule applies
+// and halving the waves evens the SIMDs' load.  Its results are bitwise
+// those of variant 3, so the choice, which depends on B and on the device,
+// changes no result.
+// Returns the workgroup tasks to cut in two (0: not this schedule).
+int64_t halves_planned(int64_t B, int64_t L, int64_t D, int64_t N, const ssm_tuning *t) {
+  const Plan p = plan_scan(L, D, t);
+  const bool n_ok = N == 4 || N == 8 || N == 16 || N == 32 || N == 64;
+  if (!n_ok || L < 64) return 0;
+  if (p.variant == 4) return ssm::scan_halves_split(B, D, N, 0, true);
+  const bool auto_seq = (t == nullptr || (t->variant == 0 && t->states_per_lane == 0)) && p.variant == 1;
+  return auto_seq ? ssm::scan_halves_split(B, D, N, device_simds(), false) : 0;
+}
 
 // shapes the matrix-core SSD kernels are built for
 bool ssd_mfma_applies(ssm_dtype dt, int64_t P, int64_t N, int64_t chunk) {
@@ -160,11 +190,14 @@ const char *ssm_status_string(ssm_status s) {
 
 int ssm_version(void) { return 100; }  // 0.1.0
 
-// Workspace: the segment summaries of the chunked schedule (none otherwise).
+// Workspace: the segment summaries of the chunked schedule, the state
+// handoff of the halved one (none otherwise).
 int64_t scan_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, const ssm_tuning *t) {
   if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
   const Plan p = plan_scan(L, D, t);
-  return p.variant == 2 ? ssm::scan_chunked_ws_floats(B, L, D, N, p.seg_len) : 0;
+  if (p.variant == 2) return ssm::scan_chunked_ws_floats(B, L, D, N, p.seg_len);
+  if (halves_planned(B, L, D, N, t) > 0) return ssm::scan_halves_ws_floats(B, D, N);
+  return 0;
 }
 
 size_t ssm_scan_fwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N,
@@ -245,6 +278,23 @@ ssm_status scan_fwd_impl(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype d
   }
   const bool auto_variant = tuning == nullptr || tuning->variant == 0;
   const bool lanesplit_ok = ssm::scan_lanesplit_supported(a);
+  const int64_t nsplit = halves_planned(B, L, D, N, tuning);
+  if (p.variant == 4 || (nsplit > 0 && lanesplit_ok)) {
+    if (!lanesplit_ok || nsplit == 0) return SSM_ERR_UNSUPPORTED;
+    const size_t need = static_cast<size_t>(ssm::scan_halves_ws_floats(B, D, N)) * sizeof(float);
+    if (own_scratch) {
+      if (need > ssm::kScratchBytes) return SSM_ERR_WORKSPACE;
+      const hipError_t e = ssm::scratch_device_ptr(&workspace);
+      if (e != hipSuccess) return SSM_ERR_HIP;
+    } else {
+      if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+      const Range wsr{workspace, static_cast<int64_t>(need)};
+      if (overlaps_any(wsr, ins) || overlap(wsr, Range{y, nBLD * es}) ||
+          overlap(wsr, Range{h_final, nBDN * 4}))
+        return SSM_ERR_INVALID_ARG;
+    }
+    return hip_status(ssm::launch_scan_lanesplit_halves(a, nsplit, static_cast<float *>(workspace), s));
+  }
   if (p.variant == 3) {
     if (!lanesplit_ok) return SSM_ERR_UNSUPPORTED;
     return hip_status(ssm::launch_scan_lanesplit(a, s));

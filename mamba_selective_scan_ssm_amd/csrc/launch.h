@@ -54,6 +54,16 @@ hipError_t launch_scan_sequential(const ScanArgs &a, int spl_req, hipStream_t s)
 bool scan_lanesplit_supported(const ScanArgs &a);
 hipError_t launch_scan_lanesplit(const ScanArgs &a, hipStream_t s);
 
+// The lane-split scan with the first nsplit workgroup tasks cut in two at
+// a 32-token cycle, their second halves continuing from the state the first
+// halves hand over through ws (no slots, no saved states, L >= 64): bitwise
+// the results of launch_scan_lanesplit.  scan_halves_split: nsplit for this
+// shape on `simds` SIMDs (0: the whole-task grid is as balanced; forced:
+// half the tasks, for tests).
+int64_t scan_halves_split(int64_t B, int64_t D, int64_t N, int64_t simds, bool forced);
+int64_t scan_halves_ws_floats(int64_t B, int64_t D, int64_t N);
+hipError_t launch_scan_lanesplit_halves(const ScanArgs &a, int64_t nsplit, float *ws, hipStream_t s);
+
 // Chunked scan: segment summaries, carry pass over segments, output pass.
 // ws must hold scan_chunked_ws_floats(...) floats.
 int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg_len);

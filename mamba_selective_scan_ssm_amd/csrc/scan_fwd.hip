@@ -55,7 +55,7 @@ namespace {
 
 constexpr int kWave = 64;
 
-enum Mode : int { kFull = 0, kSummary = 1, kOutput = 2 };
+enum Mode : int { kFull = 0, kSummary = 1, kOutput = 2, kHalves = 3 };
 
 template <int K>
 using f32v = float __attribute__((ext_vector_type(K)));
@@ -387,6 +387,21 @@ __device__ __forceinline__ float word_elem(const uint32_t *w, int e) {
 // kOutput runs its segment from seg_h (the state entering it) and writes y.
 // seg_len is a multiple of the 32-token load cycle (TB * CYC), so only the
 // last segment has a partial cycle and its rows past L lie past the plane.
+// kHalves (1-D grid of J + S workgroups, J = B x channel tiles): the first
+// S workgroup tasks are cut in two at seg_len, the rest run whole.  Ids
+// [0, S) run the first halves, [S, J) the whole tasks, [J, J + S) the
+// second halves.  With 2,560 waves on 1,024 SIMDs (2 each and 512 over)
+// and S = 128, round-robin placement gives every SIMD two whole waves and
+// one half, instead of 3 whole waves on half of them.  A first half stores
+// the state it reaches to seg_h (B, D, N) and then sets its wave's flag in
+// seg_a (a device-scope release); the second half waits for that flag
+// (bounded: kSpinLimit polls, after which the state is taken as NaN, making
+// the failure visible), then runs on from the state.  The state crosses the
+// cut exactly, so y and h_final are bitwise those of kFull.  The waiter's
+// publisher has a lower workgroup id, so it was dispatched first and never
+// waits, and the wait ends.
+constexpr int kSpinLimit = 1 << 20;
+
 template <typename T, int LPC, int SPL, bool HAS_Z, bool CK, bool STEP, int CYC = 4, int MODE = kFull>
 __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, int64_t seg_len, float *seg_a,
                                                                    float *seg_h) {
@@ -418,25 +433,53 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
   const int64_t D = a.D, L = a.L;
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t d0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * kCPW;  // first channel of the wave
-  const int64_t b = blockIdx.z;
+  constexpr bool kHalf = MODE == kHalves;
+  // kHalves: workgroup task j of J, split (first S) or whole
+  const int64_t h_ntile = (D + 4 * kCPW - 1) / (4 * kCPW);
+  const int64_t h_J = a.B * h_ntile;
+  const int64_t h_S = kHalf ? static_cast<int64_t>(gridDim.x) - h_J : 0;
+  const int64_t h_g = blockIdx.x;
+  const int64_t h_j = h_g < h_J ? h_g : h_g - h_J;
+  const int64_t d0 = kHalf ? ((h_j % h_ntile) * 4 + wave) * kCPW
+                           : (static_cast<int64_t>(blockIdx.x) * 4 + wave) * kCPW;  // first channel of the wave
+  const int64_t b = kHalf ? h_j / h_ntile : blockIdx.z;
   int64_t hrow;  // state row of sequence b
   if (!scan_state_row(a, b, hrow)) return;
-  const int64_t seg = blockIdx.y, nseg = gridDim.y;
-  const int64_t tok0 = seg * seg_len;                                // first token of the segment
-  const int64_t Ls = (L - tok0) < seg_len ? (L - tok0) : seg_len;    // its tokens
+  // kHalves: seg 0 first half, 1 second half, 2 whole
+  const int64_t seg = kHalf ? (h_g < h_S ? 0 : h_g < h_J ? 2 : 1) : blockIdx.y;
+  const int64_t nseg = kHalf ? 1 : gridDim.y;
+  const int64_t tok0 = kHalf ? (seg == 1 ? seg_len : 0) : seg * seg_len;  // first token of the segment
+  const int64_t Ls = kHalf ? (seg == 2 ? L : seg == 0 ? seg_len : L - seg_len)
+                           : ((L - tok0) < seg_len ? (L - tok0) : seg_len);  // its tokens
   const uint32_t tok0_u = static_cast<uint32_t>(tok0);
 
   // compute role: channel c, state slice q
   const int c = lane / LPC, q = lane % LPC;
   const int64_t dc = (d0 + c < D) ? d0 + c : D - 1;
   const int64_t ws_row = ((b * nseg + seg) * D + dc) * kN + q * SPL;  // segment summaries
+  // kHalves: this wave's handoff flag and this lane's handoff states
+  int *hflag = kHalf ? reinterpret_cast<int *>(seg_a) + h_j * 4 + wave : nullptr;
+  float *hslot = kHalf ? seg_h + (b * D + dc) * kN + q * SPL : nullptr;
+  if (kHalf && seg == 1) {
+    int seen = 0;
+    for (int it = 0; it < kSpinLimit; ++it) {
+      seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(hflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (seen != 0) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (seen == 0) {
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) hslot[s] = __builtin_nanf("");
+    }
+  }
   float A2[SPL], h[SPL];
   {
     const float *Ap = a.A + dc * kN + q * SPL;
     const float *hp = MODE == kOutput ? seg_h + ws_row
-                      : (MODE == kFull && a.h0) ? a.h0 + (hrow * D + dc) * kN + q * SPL
-                                                : nullptr;
+                      : (kHalf && seg == 1) ? hslot
+                      : ((MODE == kFull || kHalf) && a.h0) ? a.h0 + (hrow * D + dc) * kN + q * SPL
+                                                           : nullptr;
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
       A2[s] = Ap[s] * kLog2e;
@@ -683,6 +726,15 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
   }
   if (kY && ncyc > 0) store_cycle(cyc - 1);
 
+  if (kHalf && seg == 0) {  // publish the state reached at the cut
+    if (d0 + c < D) {
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) hslot[s] = h[s];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (lane == 0) __hip_atomic_store(hflag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   if (d0 + c >= D) return;
   if (MODE == kSummary) {
 #pragma unroll
@@ -691,7 +743,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
       seg_h[ws_row + s] = h[s];
     }
   }
-  if (MODE != kFull || a.h_final == nullptr) return;
+  if ((MODE != kFull && !kHalf) || a.h_final == nullptr) return;
   float *hf = a.h_final + (hrow * D + dc) * kN + q * SPL;
 #pragma unroll
   for (int s = 0; s < SPL; ++s) hf[s] = h[s];
@@ -736,6 +788,13 @@ __global__ __launch_bounds__(kCarryThreads) void scan_carry_kernel(int64_t B, in
     }
   }
   if (h_final) h_final[i] = carry;
+}
+
+// Zeroes the kHalves handoff flags (a fill kernel rather than a memset, so
+// the launch pair can be captured in a graph).
+__global__ __launch_bounds__(256) void halves_flags_clear(int *flag, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) flag[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -965,6 +1024,47 @@ hipError_t dispatch_lanesplit(const ScanArgs &a, hipStream_t s) {
   }
 }
 
+// Halved schedule: ws holds the handoff states (B, D, N) and then one flag
+// per wave of the first halves.
+template <typename T, int LPC, int SPL, bool STEP>
+void launch_lanesplit_halves_s(const ScanArgs &a, int64_t nsplit, float *ws, hipStream_t s) {
+  constexpr int kChPerWG = 4 * (kWave / LPC);
+  const int64_t tiles = (a.D + kChPerWG - 1) / kChPerWG;
+  const int64_t nflag = nsplit * 4;
+  float *hand = ws;
+  float *flags = ws + a.B * a.D * a.N;
+  halves_flags_clear<<<static_cast<unsigned>((nflag + 255) / 256), 256, 0, s>>>(reinterpret_cast<int *>(flags),
+                                                                             nflag);
+  const int64_t cut = ((a.L + 1) / 2 + 31) / 32 * 32;  // whole 32-token cycles
+  const dim3 grid(static_cast<unsigned>(a.B * tiles + nsplit), 1, 1);
+  if (a.z)
+    scan_lanesplit_kernel<T, LPC, SPL, true, false, STEP, 4, kHalves><<<grid, kWave * 4, 0, s>>>(a, cut, flags, hand);
+  else
+    scan_lanesplit_kernel<T, LPC, SPL, false, false, STEP, 4, kHalves><<<grid, kWave * 4, 0, s>>>(a, cut, flags,
+                                                                                               hand);
+}
+
+template <typename T, int LPC, int SPL>
+hipError_t launch_lanesplit_halves_t(const ScanArgs &a, int64_t nsplit, float *ws, hipStream_t s) {
+  if (a.delta_bias != nullptr || a.delta_softplus)
+    launch_lanesplit_halves_s<T, LPC, SPL, true>(a, nsplit, ws, s);
+  else
+    launch_lanesplit_halves_s<T, LPC, SPL, false>(a, nsplit, ws, s);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_lanesplit_halves(const ScanArgs &a, int64_t nsplit, float *ws, hipStream_t s) {
+  switch (a.N) {
+    case 4: return launch_lanesplit_halves_t<T, 1, 4>(a, nsplit, ws, s);
+    case 8: return launch_lanesplit_halves_t<T, 2, 4>(a, nsplit, ws, s);
+    case 16: return launch_lanesplit_halves_t<T, 4, 4>(a, nsplit, ws, s);
+    case 32: return launch_lanesplit_halves_t<T, 4, 8>(a, nsplit, ws, s);
+    case 64: return launch_lanesplit_halves_t<T, 4, 16>(a, nsplit, ws, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
 template <typename T, int NB, bool EXACT>
 hipError_t launch_lane_t(const ScanArgs &a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((a.D + kWave - 1) / kWave), 1, static_cast<unsigned>(a.B));
@@ -1004,6 +1104,30 @@ bool scan_lanesplit_supported(const ScanArgs &a) {
 hipError_t launch_scan_lanesplit(const ScanArgs &a, hipStream_t s) {
   if (a.dt == DType::BF16) return dispatch_lanesplit<bf16_t>(a, s);
   return dispatch_lanesplit<float>(a, s);
+}
+
+int64_t scan_halves_split(int64_t B, int64_t D, int64_t N, int64_t simds, bool forced) {
+  const int64_t lpc = N == 4 ? 1 : N == 8 ? 2 : 4;
+  const int64_t J = B * ((D + 4 * (kWave / lpc) - 1) / (4 * (kWave / lpc)));  // workgroup tasks
+  if (forced) return J / 2 > 0 ? J / 2 : 1;
+  // the waves over a whole number per SIMD, halved, give each SIMD at most
+  // one half more when they number at most half the SIMDs
+  const int64_t waves = 4 * J;
+  if (simds <= 0 || waves <= simds) return 0;
+  const int64_t r = waves % simds;
+  if (r == 0 || 2 * r > simds) return 0;
+  return r / 4;
+}
+
+int64_t scan_halves_ws_floats(int64_t B, int64_t D, int64_t N) {
+  const int64_t lpc = N == 4 ? 1 : N == 8 ? 2 : 4;
+  const int64_t tiles = (D + 4 * (kWave / lpc) - 1) / (4 * (kWave / lpc));
+  return B * D * N + B * tiles * 4;  // handoff states, then the flags (at most one per wave)
+}
+
+hipError_t launch_scan_lanesplit_halves(const ScanArgs &a, int64_t nsplit, float *ws, hipStream_t s) {
+  if (a.dt == DType::BF16) return dispatch_lanesplit_halves<bf16_t>(a, nsplit, ws, s);
+  return dispatch_lanesplit_halves<float>(a, nsplit, ws, s);
 }
 
 int64_t scan_chunked_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg_len) {

@@ -93,7 +93,7 @@ def test_scan_empty_batch_is_noop(lib):
 
 
 def test_scan_tuning_validation(lib):
-    t = ssm.Tuning(4, 0)
+    t = ssm.Tuning(5, 0)  # variants 0..4
     assert scan(lib, tun=t) == INVALID
     t = ssm.Tuning(2, 12)
     assert scan(lib, tun=t) == INVALID
@@ -355,4 +355,4 @@ def test_scan_noalloc_limit_and_validation(lib):
     assert na(y=None) == INVALID
     assert na(y=Q[0]) == INVALID                     # y on x
     assert na(N=65) == UNSUPPORTED
-    assert na(tun=ssm.Tuning(4, 0)) == INVALID
+    assert na(tun=ssm.Tuning(5, 0)) == INVALID

@@ -297,6 +297,75 @@ def test_chunked_lanesplit_matches_wavesplit_bitwise(B, L, D, N, dtype, chunk):
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
 
 
+# Halved schedule (variant 4): every wave's tokens cut in two at a 32-token
+# cycle, the second half continuing from the state the first hands over.
+HALVED_SHAPES = [
+    (2, 500, 256, 16, "bf16"),
+    (3, 777, 130, 8, "f32"),      # D not a multiple of the workgroup's channels
+    (1, 300, 512, 32, "bf16"),
+    (4, 96, 64, 16, "f32"),       # cut at token 64 of 96
+    (5, 1000, 192, 4, "f32"),
+    (1, 65, 128, 64, "bf16"),     # a one-token second half
+]
+
+
+@pytest.mark.parametrize("B,L,D,N,dtype", HALVED_SHAPES)
+@pytest.mark.parametrize("gate,h0", [(True, True), (False, False)])
+def test_halved_matches_lanesplit_bitwise(B, L, D, N, dtype, gate, h0):
+    """The halved schedule hands the fp32 state across its cut exactly, so y
+    and h_final are bitwise those of whole-sequence waves (variant 3)."""
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(B, L, D, N, dtype=dtype, seed=800 + L + N)
+    _say("halved vs lane-split", B, L, D, N, dtype, gate, h0)
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A, Ds = to_dev(inp.A), to_dev(inp.D_skip)
+    z = t["z"] if gate else None
+    hz = to_dev(inp.h0) if h0 else None
+    y3, h3 = ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, z, hz, variant=3)
+    y4, h4 = ssm.scan_fwd(t["x"], t["delta"], A, t["Bm"], t["Cm"], Ds, z, hz, variant=4)
+    assert torch.equal(y3, y4) and torch.equal(h3, h4)
+
+
+def test_halved_with_delta_transform(oracle_mod):
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_scan(2, 500, 256, 16, dtype="bf16", seed=820)
+    bias = np.random.default_rng(821).normal(0.0, 0.5, inp.D).astype(np.float32)
+    _say("halved, delta bias + softplus")
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    args = (t["x"], t["delta"], to_dev(inp.A), t["Bm"], t["Cm"], to_dev(inp.D_skip), t["z"], to_dev(inp.h0))
+    kw = dict(delta_bias=to_dev(bias), delta_softplus=True)
+    y3, h3 = ssm.scan_fwd(*args, variant=3, **kw)
+    y4, h4 = ssm.scan_fwd(*args, variant=4, **kw)
+    assert torch.equal(y3, y4) and torch.equal(h3, h4)
+    ry, rh = oracle_mod.scan(inp.x.f32, inp.delta.f32, inp.A, inp.Bm.f32, inp.Cm.f32, inp.D_skip, inp.z.f32,
+                             inp.h0, delta_bias=bias, delta_softplus=True)
+    assert_close(to_np(y4), ry, "bf16", "y")
+    assert_close(to_np(h4), rh, "bf16", "h_final")
+
+
+def test_halved_where_it_does_not_apply():
+    import mamba_selective_scan_ssm_amd as ssm
+    for (B, L, D, N) in ((1, 50, 64, 16), (2, 300, 100, 5)):
+        inp = gen.make_scan(B, L, D, N, dtype="f32", seed=830 + N)
+        _say("halved unsupported", B, L, D, N)
+        with pytest.raises(ssm.SSMError):
+            run_gpu(inp, variant=4)
+
+
+def test_mamba2p8b_prefill_auto_is_halved_bitwise():
+    """At the 2.8B shape (2,560 waves of 16 channels on 1,024 SIMDs) the
+    automatic choice is the halved schedule: bitwise whole-sequence waves."""
+    import mamba_selective_scan_ssm_amd as ssm
+    inp = gen.make_workload("mamba2p8b_prefill_bf16")
+    _say("2.8B shape: automatic (halved) vs whole-sequence waves")
+    assert ssm.scan_fwd_workspace_size(inp.B, inp.L, inp.D, inp.N) > 0
+    t = {k: to_dev(getattr(inp, k)) for k in ("x", "delta", "z", "Bm", "Cm")}
+    args = (t["x"], t["delta"], to_dev(inp.A), t["Bm"], t["Cm"], to_dev(inp.D_skip), t["z"], to_dev(inp.h0))
+    y0, h0 = ssm.scan_fwd(*args)
+    y3, h3 = ssm.scan_fwd(*args, variant=3)
+    assert torch.equal(y0, y3) and torch.equal(h0, h3)
+
+
 def test_unaligned_bc_falls_back_bitwise():
     """B/C views that are not 16-byte aligned take the wave-split kernel and
     give the same bits as aligned copies (which take the lane-split one)."""

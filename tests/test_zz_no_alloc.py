@@ -61,3 +61,19 @@ def test_noalloc_without_workspace_schedule():
     _say("noalloc lane-split", inp.B, inp.L, inp.D, inp.N)
     y, h, y_ref, h_ref = _pair(inp, gate=False)
     assert torch.equal(y, y_ref) and torch.equal(h, h_ref)
+
+
+def test_noalloc_halved_schedule():
+    """The halved schedule's state handoff in the device scratch: two calls in
+    a row, the second smaller, bitwise whole-sequence waves through _ex."""
+    import mamba_selective_scan_ssm_amd as ssm
+    for inp in (gen.make_scan(2, 500, 256, 16, dtype="bf16", seed=910),
+                gen.make_scan(2, 300, 256, 16, dtype="f32", seed=911)):
+        _say("noalloc halved", inp.B, inp.L, inp.D, inp.N)
+        args = [to_dev(getattr(inp, k)) for k in ("x", "delta", "A", "Bm", "Cm", "D_skip", "z", "h0")]
+        y_ref, h_ref = ssm.scan_fwd(*args, variant=3)
+        y = torch.full_like(y_ref, float("nan"))
+        h = torch.full_like(h_ref, float("nan"))
+        ssm.scan_fwd_noalloc(*args, y=y, h_final=h, variant=4)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(h, h_ref)
