@@ -66,11 +66,12 @@ typedef enum {
 } ssm_status;
 
 /* Kernel-variant selection for ssm_scan_fwd.  Pass NULL for the defaults.
- * The default schedule depends only on (L, D, N) -- never on B or on the
- * device -- so a sequence gives bitwise the same result whatever batch it
- * is part of.  (Within the channel-sequential schedule the automatic choice
- * also looks at the alignment of Bm and Cm; variants 1 and 3 give bitwise
- * identical results.)  */
+ * The default schedule's results depend only on (L, D, N) -- never on B or
+ * on the device -- so a sequence gives bitwise the same result whatever
+ * batch it is part of.  (Within the channel-sequential schedule the
+ * automatic choice also looks at the alignment of Bm and Cm, at B and at
+ * the device's CU count; variants 1, 3 and 4 give bitwise identical
+ * results.)  */
 typedef struct {
     int32_t variant;   /* 0 = automatic; 1 = channel-sequential, a workgroup
                           per 64-channel tile whose waves split the N states;
@@ -78,9 +79,18 @@ typedef struct {
                           output pass); 3 = channel-sequential, the N states
                           of a channel split over 1, 2 or 4 lanes of one wave
                           (N in {4, 8, 16, 32, 64} and Bm, Cm 16-byte
-                          aligned, else SSM_ERR_UNSUPPORTED).  Automatic:
-                          variant 3 where it applies, else 1, when L <= 256
-                          or D >= 4096; variant 2 otherwise. */
+                          aligned, else SSM_ERR_UNSUPPORTED); 4 = variant 3
+                          with some waves' tokens cut in two at a 32-token
+                          cycle, the second half continuing from the state
+                          the first hands over through the workspace (also
+                          L >= 64, else SSM_ERR_UNSUPPORTED; asked for
+                          explicitly it cuts half of the 64-channel tiles).
+                          Automatic: variant 3 where it applies, else 1,
+                          when L <= 256 or D >= 4096 -- variant 4 instead of
+                          3 when the waves exceed the device's SIMDs by at
+                          most half their count, cutting just the excess so
+                          every SIMD carries the same work; variant 2
+                          otherwise. */
     int32_t chunk_len; /* variant 2: tokens per segment (multiple of 8,
                           >= 8); 0 = automatic (a multiple of 32).  With a
                           multiple of 32, states_per_lane 0 and the
@@ -134,9 +144,12 @@ typedef struct {
  * y must not overlap any input.  Inputs are never modified.
  * workspace      : device scratch of at least ssm_scan_fwd_workspace_size()
  *                  bytes (may be NULL when that size is 0, which it is for
- *                  the channel-sequential schedule): the segment summaries
- *                  of the chunked schedule.  Contents on entry are ignored;
- *                  it must not overlap any argument.
+ *                  variants 1 and 3): the segment summaries of the chunked
+ *                  schedule, the handed-over states and flags of variant 4.
+ *                  Contents on entry are ignored (variant 4 clears its
+ *                  flags with a kernel of its own); it must not overlap any
+ *                  argument, and two calls that overlap in time must not
+ *                  share it.
  * Sizes: B, L, D, N >= 0; N <= SSM_SCAN_MAX_N; one sequence's x plane
  * (L + 64) * D * sizeof(dtype) and B/C plane (L + 64) * N * sizeof(dtype)
  * below 2^31 bytes (else SSM_ERR_UNSUPPORTED).  L == 0 writes h_final = h0
@@ -166,7 +179,8 @@ ssm_status ssm_scan_fwd_ex(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same arguments, results and schedule choice as
  * ssm_scan_fwd_ex, bitwise, without the workspace: where the chosen schedule
- * needs one (the chunked schedule's segment summaries), it uses a device
+ * needs one (the chunked schedule's segment summaries, variant 4's state
+ * handoff), it uses a device
  * scratch array that the library holds on every GPU it runs on, for the life
  * of the process.  The call allocates nothing (no hipMalloc, hipFree or
  * allocating library routine); the caller still passes inputs and outputs.
@@ -205,7 +219,9 @@ ssm_status ssm_scan_fwd_train(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dt
                               const void *z, const float *h0, void *y, float *h_final,
                               float *h_ckpt, const ssm_delta_opts *dopts, void *stream);
 
-/* Device workspace ssm_scan_fwd needs for these sizes and tuning (bytes). */
+/* Device workspace ssm_scan_fwd needs for these sizes and tuning (bytes);
+ * it may depend on the current device (variant 4 is chosen from its CU
+ * count). */
 size_t ssm_scan_fwd_workspace_size(int64_t B, int64_t L, int64_t D, int64_t N,
                                    const ssm_tuning *tuning);
 
