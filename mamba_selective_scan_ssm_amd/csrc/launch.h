@@ -54,6 +54,12 @@ hipError_t launch_scan_sequential(const ScanArgs &a, int spl_req, hipStream_t s)
 bool scan_lanesplit_supported(const ScanArgs &a);
 hipError_t launch_scan_lanesplit(const ScanArgs &a, hipStream_t s);
 
+// The lane-split scan writing only a.h_ckpt (the state entering every
+// 8-token segment, from h0): no y, h_final, z or C.  a.y and a.Cm must
+// still be valid pointers for scan_lanesplit_supported (neither is
+// accessed); no slots.
+hipError_t launch_scan_states(const ScanArgs &a, hipStream_t s);
+
 // The lane-split scan with the first nsplit workgroup tasks cut in two at
 // a 32-token cycle, their second halves continuing from the state the first
 // halves hand over through ws (no slots, no saved states, L >= 64): bitwise

@@ -579,6 +579,31 @@ int64_t scan_bwd_ws_floats(int64_t B, int64_t L, int64_t D, int64_t N, bool save
 }
 
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
+  // Without saved states, the lane-split forward recomputes them into the
+  // workspace (its first B * nseg * D * N floats) where its layout applies;
+  // the backward then runs as if the forward had saved them, with the rest
+  // of the workspace, which is where the partials already lie.  The
+  // kernel's own first pass remains for the shapes the lane-split scan
+  // does not take.
+  static_assert(kSeg == 8, "the lane-split scan saves the state entering every 8 tokens");
+  if (a.h_ckpt == nullptr && a.L > 0 && a.B > 0 && a.D > 0 && reinterpret_cast<uintptr_t>(a.ws) % 16 == 0) {
+    ScanArgs f{};
+    f.B = a.B; f.L = a.L; f.D = a.D; f.N = a.N; f.dt = a.dt;
+    f.x = a.x; f.delta = a.delta; f.A = a.A; f.Bm = a.Bm;
+    f.Cm = a.Bm;                    // not accessed in this mode
+    f.y = const_cast<void *>(a.x);  // not written in this mode
+    f.h0 = a.h0;
+    f.delta_bias = a.delta_bias; f.delta_softplus = a.delta_softplus;
+    f.h_ckpt = a.ws;
+    if (scan_lanesplit_supported(f)) {
+      hipError_t e = launch_scan_states(f, s);
+      if (e != hipSuccess) return e;
+      BwdArgs g = a;
+      g.h_ckpt = a.ws;
+      g.ws = a.ws + a.B * bwd_nseg(a.L) * a.D * a.N;
+      return a.dt == DType::BF16 ? launch_bwd_dt<bf16_t>(g, s) : launch_bwd_dt<float>(g, s);
+    }
+  }
   if (a.dt == DType::BF16) return launch_bwd_dt<bf16_t>(a, s);
   return launch_bwd_dt<float>(a, s);
 }

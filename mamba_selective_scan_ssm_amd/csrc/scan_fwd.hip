@@ -55,7 +55,7 @@ namespace {
 
 constexpr int kWave = 64;
 
-enum Mode : int { kFull = 0, kSummary = 1, kOutput = 2, kHalves = 3 };
+enum Mode : int { kFull = 0, kSummary = 1, kOutput = 2, kHalves = 3, kStates = 4 };
 
 template <int K>
 using f32v = float __attribute__((ext_vector_type(K)));
@@ -385,6 +385,8 @@ __device__ __forceinline__ float word_elem(const uint32_t *w, int e) {
 // kFull runs all of L from h0; kSummary runs its segment from 0 and writes
 // seg_a = exp(A sum delta) and seg_h = the state reached, without outputs;
 // kOutput runs its segment from seg_h (the state entering it) and writes y.
+// kStates (with CK) runs all of L from h0 and writes only the saved states
+// (no y or h_final, no loads of C or z): the backward's recomputation of them.
 // seg_len is a multiple of the 32-token load cycle (TB * CYC), so only the
 // last segment has a partial cycle and its rows past L lie past the plane.
 // kHalves (1-D grid of J + S workgroups, J = B x channel tiles): the first
@@ -402,6 +404,8 @@ __device__ __forceinline__ float word_elem(const uint32_t *w, int e) {
 // waits, and the wait ends.
 constexpr int kSpinLimit = 1 << 20;
 
+using f32x4 = float __attribute__((ext_vector_type(4)));
+
 template <typename T, int LPC, int SPL, bool HAS_Z, bool CK, bool STEP, int CYC = 4, int MODE = kFull>
 __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, int64_t seg_len, float *seg_a,
                                                                    float *seg_h) {
@@ -418,8 +422,9 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
   static_assert(LPC == 1 || LPC == 2 || LPC == 4, "LPC must be 1, 2 or 4");
   static_assert(SPL % kV == 0, "a loader lane's values must fall in one lane's slice");
   static_assert(kPairs * 64 * 2 == TB * kCPW, "pair slots must tile the block");
-  static_assert(!CK || MODE == kFull, "segment states are saved by full runs only");
-  constexpr bool kY = MODE != kSummary;
+  static_assert(!CK || MODE == kFull || MODE == kStates, "segment states are saved by full runs only");
+  static_assert(MODE != kStates || CK, "kStates writes the saved states only");
+  constexpr bool kY = MODE != kSummary && MODE != kStates;
 
   // per wave and block of the cycle: B/C [token][q][B|C][SPL] and
   // (delta, u) [token][channel]; per wave: partial sums [token][channel *
@@ -478,7 +483,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
     const float *Ap = a.A + dc * kN + q * SPL;
     const float *hp = MODE == kOutput ? seg_h + ws_row
                       : (kHalf && seg == 1) ? hslot
-                      : ((MODE == kFull || kHalf) && a.h0) ? a.h0 + (hrow * D + dc) * kN + q * SPL
+                      : ((MODE == kFull || MODE == kStates || kHalf) && a.h0) ? a.h0 + (hrow * D + dc) * kN + q * SPL
                                                            : nullptr;
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
@@ -547,9 +552,10 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
   auto store_ckpt = [&](int64_t seg, const float *v) {
     if constexpr (SPL % 4 == 0) {
 #pragma unroll
-      for (int s4 = 0; s4 < SPL / 4; ++s4)
-        reinterpret_cast<float4 *>(ckp + seg * D * kN)[s4] =
-            make_float4(v[4 * s4], v[4 * s4 + 1], v[4 * s4 + 2], v[4 * s4 + 3]);
+      for (int s4 = 0; s4 < SPL / 4; ++s4) {
+        const f32x4 sv = {v[4 * s4], v[4 * s4 + 1], v[4 * s4 + 2], v[4 * s4 + 3]};
+        __builtin_nontemporal_store(sv, reinterpret_cast<f32x4 *>(ckp + seg * D * kN) + s4);
+      }
     } else {
 #pragma unroll
       for (int s = 0; s < SPL; ++s) ckp[seg * D * kN + s] = v[s];
@@ -670,7 +676,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
       const uint32_t so =
           __builtin_amdgcn_readfirstlane((tok0_u + static_cast<uint32_t>(cyc * kCyc + u) * TB) * row_bytes);
 #pragma unroll
-      for (int m = 0; m < kPairs; ++m) {
+      for (int m = 0; m < (kY ? kPairs : 0); ++m) {
         const int vov = static_cast<int>(vo_st[m]), sov = static_cast<int>(so);
         if constexpr (sizeof(T) == 2) {
           __builtin_amdgcn_raw_buffer_store_b32(yv[u][m][0], ry, vov, sov, 0);
@@ -697,7 +703,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
   // y stores fall past the plane and the state is already final)
   auto cycle = [&](Raw &cur, Raw &nxt, int64_t cyc, int nb) {
     stage(cur, cyc);
-    if (kY && cyc > 0) store_cycle(cyc - 1);
+    if ((kY || CK) && cyc > 0) store_cycle(cyc - 1);
     issue(nxt, cyc + 1);
     wave_sync_lds();
 #pragma unroll
@@ -724,7 +730,7 @@ __global__ __launch_bounds__(kWave * 4) void scan_lanesplit_kernel(ScanArgs a, i
     cycle(r0, r1, cyc, static_cast<int>(nblk - cyc * kCyc));
     ++cyc;
   }
-  if (kY && ncyc > 0) store_cycle(cyc - 1);
+  if ((kY || CK) && ncyc > 0) store_cycle(cyc - 1);
 
   if (kHalf && seg == 0) {  // publish the state reached at the cut
     if (d0 + c < D) {
@@ -957,6 +963,31 @@ void launch_lanesplit_s(const ScanArgs &a, dim3 grid, hipStream_t s) {
 }
 
 template <typename T, int LPC, int SPL>
+hipError_t launch_states_t(const ScanArgs &a, hipStream_t s) {
+  constexpr int kChPerWG = 4 * (kWave / LPC);
+  dim3 grid(static_cast<unsigned>((a.D + kChPerWG - 1) / kChPerWG), 1, static_cast<unsigned>(a.B));
+  if (a.delta_bias != nullptr || a.delta_softplus)
+    scan_lanesplit_kernel<T, LPC, SPL, false, true, true, 4, kStates><<<grid, kWave * 4, 0, s>>>(a, a.L, nullptr,
+                                                                                                nullptr);
+  else
+    scan_lanesplit_kernel<T, LPC, SPL, false, true, false, 4, kStates><<<grid, kWave * 4, 0, s>>>(a, a.L, nullptr,
+                                                                                                 nullptr);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_states(const ScanArgs &a, hipStream_t s) {
+  switch (a.N) {
+    case 4: return launch_states_t<T, 1, 4>(a, s);
+    case 8: return launch_states_t<T, 2, 4>(a, s);
+    case 16: return launch_states_t<T, 4, 4>(a, s);
+    case 32: return launch_states_t<T, 4, 8>(a, s);
+    case 64: return launch_states_t<T, 4, 16>(a, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <typename T, int LPC, int SPL>
 hipError_t launch_lanesplit_t(const ScanArgs &a, hipStream_t s) {
   constexpr int kChPerWG = 4 * (kWave / LPC);
   dim3 grid(static_cast<unsigned>((a.D + kChPerWG - 1) / kChPerWG), 1, static_cast<unsigned>(a.B));
@@ -1104,6 +1135,11 @@ bool scan_lanesplit_supported(const ScanArgs &a) {
 hipError_t launch_scan_lanesplit(const ScanArgs &a, hipStream_t s) {
   if (a.dt == DType::BF16) return dispatch_lanesplit<bf16_t>(a, s);
   return dispatch_lanesplit<float>(a, s);
+}
+
+hipError_t launch_scan_states(const ScanArgs &a, hipStream_t s) {
+  if (a.dt == DType::BF16) return dispatch_states<bf16_t>(a, s);
+  return dispatch_states<float>(a, s);
 }
 
 int64_t scan_halves_split(int64_t B, int64_t D, int64_t N, int64_t simds, bool forced) {
