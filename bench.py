@@ -90,7 +90,7 @@ KERNEL_SOURCES = {
     "decode_steps_T1": ["state_update.hip"] + _COMMON,
     "decode_steps_T4": ["state_update.hip"] + _COMMON,
     "decode_steps_T16": ["scan_fwd.hip"] + _COMMON,
-    "scan_bwd": ["scan_bwd.hip", "bwd.h"] + _COMMON,
+    "scan_bwd": ["scan_bwd.hip", "bwd.h", "scan_fwd.hip"] + _COMMON,
     "scan_fwd_130m": ["scan_fwd.hip"] + _COMMON,
 }
 
@@ -604,7 +604,11 @@ PROFILE_ENTRIES = {
                                    "kernel)", k=["scan_lanesplit"]),
     "scan_bwd": dict(only="bwd", t="--steps 10", s="--steps 1", file="scan_bwd_mamba2p8b_prefill_bf16.md",
                      title="selective-scan backward, B=8 L=4096 D=5120 N=16, bf16, all gradients (ssm_scan_bwd)",
-                     k=["scan_bwd_kernel", "bwd_reduce"], elems=8 * 4096 * 5120 * 16, extra="v"),
+                     # the backward kernels, and the states-only launch of the lane-split scan that
+                     # recomputes the segment states when the forward saved none
+                     k=["scan_bwd_kernel", "bwd_reduce",
+                        "scan_lanesplit_kernel<ssm::bf16_t, 4, 4, false, true, false, 4, 4>"],
+                     elems=8 * 4096 * 5120 * 16, extra="v"),
 }
 
 
