@@ -615,6 +615,8 @@ PROFILE_ENTRIES = {
 # kernels of one call under the automatic schedule, where a profiled run
 # also times other schedules (short names, prefix match); default: all
 CALL_KERNELS = {
+    # the bf16 call's three kernels; the same run also times the fp32 token path
+    "ssd_fwd": ["ssd_chunk_state", "ssd_state_pass", "ssd_chunk_scan"],
     "scan_fwd_130m": ["scan_lanesplit_kernel<float, 4, 4, false, false, false, 4, 1>", "scan_carry_kernel",
                       "scan_lanesplit_kernel<float, 4, 4, true, false, false, 4, 2>"],
 }
@@ -772,8 +774,9 @@ def _entry_section(src, entry, p, rec):
         for name, c in last.items():
             gui = c.get("GRBM_GUI_ACTIVE", 0) / 8
             mb = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * gui) if gui else float("nan")
-            tot_busy += c["SQ_VALU_MFMA_BUSY_CYCLES"]
-            tot_gui += gui
+            if entry not in CALL_KERNELS or any(_short(name).startswith(k) for k in CALL_KERNELS[entry]):
+                tot_busy += c["SQ_VALU_MFMA_BUSY_CYCLES"]
+                tot_gui += gui
             lines.append(f"| `{_short(name, 70)}` | {c['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | {mb:.3f} | "
                          f"{c['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.4g} "
                          f"({c['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.1f} GFLOP) | "
