@@ -261,8 +261,9 @@ ssm_status ssm_state_update_ex(int64_t S, int64_t D, int64_t N, ssm_dtype dt,
  * below.  h_ckpt: the segment states ssm_scan_fwd_train wrote for the same
  * inputs (16-byte aligned), or NULL to recompute them here (into the
  * workspace, by the prefill scan's kernel where it takes the shape: even D,
- * x and delta aligned to two elements, Bm 16-byte aligned; the gradients
- * are then bitwise those computed from ssm_scan_fwd_train's states).
+ * x and delta aligned to two elements, Bm and the workspace 16-byte
+ * aligned; the gradients are then bitwise those computed from
+ * ssm_scan_fwd_train's states; otherwise by the backward kernel itself).
  *   dx, ddelta, dz : (B, L, D) dtype `dt` (ddelta is the gradient of the
  *                    delta INPUT, i.e. through bias and softplus when dopts
  *                    asks for them; dz only with z, else must be NULL)
