@@ -99,6 +99,19 @@ __device__ __forceinline__ void ld_spl(const float *p, float *v) {
     v[0] = r.x; v[1] = r.y;
   }
 }
+// The same, marked non-temporal: for the segment states, each read once
+template <int SPL>
+__device__ __forceinline__ void ld_spl_nt(const float *p, float *v) {
+  using f32x4 = float __attribute__((ext_vector_type(4)));
+  using f32x2 = float __attribute__((ext_vector_type(2)));
+  if constexpr (SPL == 4) {
+    const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    v[0] = r[0]; v[1] = r[1]; v[2] = r[2]; v[3] = r[3];
+  } else {
+    const f32x2 r = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(p));
+    v[0] = r[0]; v[1] = r[1];
+  }
+}
 template <int SPL>
 __device__ __forceinline__ void st_spl(float *p, const float *v) {
   if constexpr (SPL == 4)
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
   // entering states are unconditional, like the inputs')
   if (nseg > 0) {
     r.load(a, b, (nseg - 1) * kSeg, dst, tid);
-    ld_spl<SPL>(ckr + ((b * nseg + nseg - 1) * D + d) * N + SPL * q, hck);
+    ld_spl_nt<SPL>(ckr + ((b * nseg + nseg - 1) * D + d) * N + SPL * q, hck);
   }
   for (int64_t s = nseg - 1; s >= 0; --s) {
     const int64_t t0 = s * kSeg;
@@ -333,7 +346,7 @@ __global__ __launch_bounds__(kBwdThreads, LPC == 4 ? 3 : 1) void scan_bwd_kernel
     // again at the last one): with one value per step the loop carries it in
     // the registers it is loaded into, where a merge would need a copy and
     // the copy a wait for every load and store in flight
-    ld_spl<SPL>(ckr + ((b * nseg + (s > 0 ? s - 1 : 0)) * D + d) * N + SPL * q, hck);
+    ld_spl_nt<SPL>(ckr + ((b * nseg + (s > 0 ? s - 1 : 0)) * D + d) * N + SPL * q, hck);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kSeg; ++k) {
